@@ -1,0 +1,316 @@
+"""Seeded synthetic workloads for the bf16 grouped (ragged, per-expert) GEMM.
+
+This module holds shapes, group-size recipes and random draws only: none of
+the GEMM's arithmetic lives here, so the CPU oracle and the HIP path can both
+take their inputs from it without sharing any of the method.
+
+Shapes and group-size structure follow the workloads the pages describe:
+
+* ``tiny``: the minimal reproduction of the empty-expert backward hang in
+  PyTorch issue #152668 (section "Easy repro scenario"): 4 experts,
+  X [48, 8], W [4, 8, 16], end offsets (8, 8, 32, 40), so expert 1 is empty
+  and rows 40..47 are unused.
+* ``qwen3_gateup``: Qwen3-30B-A3B gate/up projection (sglang PR #32385,
+  section "Cause", model table: moe_intermediate 768, i.e. N = 2*768): 128
+  experts, K = 2048, N = 1536, 8192 tokens x top-8 = 65536 rows.
+* ``masked_down``: the masked down-projection of sglang PR #32385 (section
+  "Evidence", operand table: 64 experts x 256 rows, K = 768, N = 2048).
+* ``glm_up``: the GLM-up shape of TileOPs issue #1566 (section "Summary":
+  numel = 262144, N = 4096, K = 6144), 32 experts with 128-aligned sizes.
+* ``dsv3``: a DeepSeek-V3-class layer (sglang PR #32385, model table:
+  moe_intermediate 2048): 256 experts, K = 7168, N = 2048, 32768 rows with
+  Zipf-skewed sizes and about 10 % empty experts.
+
+The ``*_small`` variants keep each recipe's structure (empty groups, sizes 8
+and 16, unaligned tails, NaN in inactive rows) at sizes a plain CPU loop
+finishes in seconds while still spanning several 256 x 256 tiles.
+
+Tensors are drawn with ``torch.randn`` from a ``torch.Generator`` seeded per
+tensor, on the device the caller names, then rounded to bf16 by torch's
+round-to-nearest-even cast.  Group sizes are drawn on the host with numpy and
+are identical on every device.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import numpy as np
+
+# bf16 bit patterns used as markers in never-read / never-written regions.
+BF16_QNAN = 0x7FC0
+OUT_SENTINEL_BF16 = 0xDEAD          # a finite bf16 (about -6.2e18)
+OUT_SENTINEL_F32 = 0xDEADBEEF       # a finite fp32 (about -6.3e18)
+
+
+@dataclass
+class Workload:
+    """One grouped-GEMM problem: shapes, group structure and draw recipe."""
+
+    name: str
+    layout: str                      # "ragged" (end offsets) or "masked"
+    num_groups: int
+    m: int                           # ragged: rows of X; masked: max_m
+    k: int
+    n: int
+    seed: int
+    offs: Optional[np.ndarray] = None        # int32 [E], ragged only
+    masked_m: Optional[np.ndarray] = None    # int32 [E], masked only
+    x_std: float = 1.0
+    w_std: float = 0.02
+    dy_std: float = 1.0
+    notes: Dict[str, str] = field(default_factory=dict)
+
+    # --- derived sizes -------------------------------------------------
+    def group_sizes(self) -> np.ndarray:
+        if self.layout == "masked":
+            return np.minimum(np.maximum(self.masked_m.astype(np.int64), 0), self.m)
+        ends = self.offs.astype(np.int64)
+        starts = np.concatenate([[0], ends[:-1]])
+        return ends - starts
+
+    def active_rows(self) -> int:
+        return int(self.group_sizes().sum())
+
+    def flops(self) -> int:
+        """2 * (active rows) * K * N: the FLOP count of one pass."""
+        return 2 * self.active_rows() * self.k * self.n
+
+    def x_shape(self):
+        if self.layout == "masked":
+            return (self.num_groups, self.m, self.k)
+        return (self.m, self.k)
+
+    def w_shape(self):
+        return (self.num_groups, self.k, self.n)
+
+    def y_shape(self):
+        if self.layout == "masked":
+            return (self.num_groups, self.m, self.n)
+        return (self.m, self.n)
+
+
+# ---------------------------------------------------------------------------
+# group-size recipes (host, numpy)
+# ---------------------------------------------------------------------------
+
+def _rng(seed: int, stream: int) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([seed, stream]))
+
+
+def _ends(sizes) -> np.ndarray:
+    return np.cumsum(np.asarray(sizes, dtype=np.int64)).astype(np.int32)
+
+
+def _force_sizes(sizes: np.ndarray, forced: Dict[int, int]) -> np.ndarray:
+    """Set sizes[i] = v for each forced entry and move the difference onto
+    the largest unforced group, so the total is unchanged."""
+    sizes = sizes.astype(np.int64).copy()
+    total = int(sizes.sum())
+    for i, v in forced.items():
+        sizes[i] = v
+    free = [i for i in range(len(sizes)) if i not in forced]
+    big = max(free, key=lambda i: sizes[i])
+    sizes[big] += total - int(sizes.sum())
+    assert sizes[big] >= 0 and int(sizes.sum()) == total
+    return sizes
+
+
+def softmax_multinomial_sizes(num_groups: int, rows: int, seed: int,
+                              n_zero: int = 3, n_eight: int = 1,
+                              n_sixteen: int = 1) -> np.ndarray:
+    """Routing-like sizes: Multinomial(rows, softmax(N(0,1) logits)), then a
+    few experts forced to 0, 8 and 16 rows (the sizes that hung the
+    backward in PyTorch issue #152668, section "Describe the bug")."""
+    r = _rng(seed, 1)
+    logits = r.standard_normal(num_groups)
+    p = np.exp(logits - logits.max())
+    p /= p.sum()
+    sizes = r.multinomial(rows, p)
+    pick = r.permutation(num_groups)
+    forced = {}
+    j = 0
+    for count, val in ((n_zero, 0), (n_eight, 8), (n_sixteen, 16)):
+        for _ in range(count):
+            forced[int(pick[j])] = val
+            j += 1
+    return _force_sizes(sizes, forced)
+
+
+def dirichlet_aligned_sizes(num_groups: int, rows: int, align: int,
+                            seed: int) -> np.ndarray:
+    """Dirichlet(1) proportions, rounded to multiples of ``align`` by the
+    largest-remainder rule so the sizes sum exactly to ``rows``."""
+    assert rows % align == 0
+    units_total = rows // align
+    r = _rng(seed, 2)
+    p = r.dirichlet(np.ones(num_groups))
+    raw = p * units_total
+    units = np.floor(raw).astype(np.int64)
+    rem = units_total - int(units.sum())
+    order = np.argsort(-(raw - units), kind="stable")
+    units[order[:rem]] += 1
+    assert int(units.sum()) == units_total
+    return units * align
+
+
+def zipf_sizes(num_groups: int, rows: int, seed: int, s: float = 1.1,
+               empty_frac: float = 0.10) -> np.ndarray:
+    """Zipf(s)-skewed sizes over a random rank order, with ``empty_frac`` of
+    the experts forced empty (they get probability zero)."""
+    r = _rng(seed, 3)
+    n_empty = int(round(empty_frac * num_groups))
+    perm = r.permutation(num_groups)
+    empty = perm[:n_empty]
+    live = perm[n_empty:]
+    ranks = np.arange(1, len(live) + 1, dtype=np.float64)
+    w = ranks ** (-s)
+    p = np.zeros(num_groups)
+    p[live] = w / w.sum()
+    sizes = r.multinomial(rows, p)
+    sizes[empty] = 0
+    return sizes.astype(np.int64)
+
+
+def uniform_masked_m(num_groups: int, max_m: int, seed: int,
+                     n_zero: int = 2, n_eight: int = 2,
+                     n_full: int = 1) -> np.ndarray:
+    """masked_m ~ U{0..max_m}, with some experts forced to 0, 8 and max_m."""
+    r = _rng(seed, 4)
+    mm = r.integers(0, max_m + 1, size=num_groups)
+    pick = r.permutation(num_groups)
+    j = 0
+    for count, val in ((n_zero, 0), (n_eight, 8), (n_full, max_m)):
+        for _ in range(count):
+            if j < num_groups:
+                mm[pick[j]] = val
+                j += 1
+    return mm.astype(np.int32)
+
+
+# ---------------------------------------------------------------------------
+# the workloads
+# ---------------------------------------------------------------------------
+
+def tiny() -> Workload:
+    return Workload("tiny", "ragged", 4, 48, 8, 16, seed=1,
+                    offs=np.array([8, 8, 32, 40], dtype=np.int32),
+                    x_std=1.0, w_std=1.0, dy_std=1.0,
+                    notes={"source": "PyTorch issue #152668, Easy repro scenario"})
+
+
+def qwen3_gateup(scale: str = "full") -> Workload:
+    if scale == "full":
+        E, M, K, N, seed = 128, 65536, 2048, 1536, 2
+    else:
+        E, M, K, N, seed = 16, 4096, 512, 384, 12
+    sizes = softmax_multinomial_sizes(E, M, seed)
+    return Workload("qwen3_gateup" + ("" if scale == "full" else "_small"),
+                    "ragged", E, M, K, N, seed=seed, offs=_ends(sizes))
+
+
+def masked_down(scale: str = "full") -> Workload:
+    if scale == "full":
+        E, MAXM, K, N, seed = 64, 256, 768, 2048, 3
+    else:
+        E, MAXM, K, N, seed = 8, 256, 256, 320, 13
+    mm = uniform_masked_m(E, MAXM, seed)
+    return Workload("masked_down" + ("" if scale == "full" else "_small"),
+                    "masked", E, MAXM, K, N, seed=seed, masked_m=mm)
+
+
+def glm_up(scale: str = "full") -> Workload:
+    if scale == "full":
+        E, M, K, N, seed = 32, 262144, 6144, 4096, 4
+    else:
+        E, M, K, N, seed = 8, 4096, 384, 512, 14
+    sizes = dirichlet_aligned_sizes(E, M, 128, seed)
+    return Workload("glm_up" + ("" if scale == "full" else "_small"),
+                    "ragged", E, M, K, N, seed=seed, offs=_ends(sizes))
+
+
+def dsv3(scale: str = "full") -> Workload:
+    if scale == "full":
+        E, M, K, N, seed = 256, 32768, 7168, 2048, 5
+    else:
+        E, M, K, N, seed = 32, 2048, 456, 328, 15
+    sizes = zipf_sizes(E, M, seed)
+    return Workload("dsv3" + ("" if scale == "full" else "_small"),
+                    "ragged", E, M, K, N, seed=seed, offs=_ends(sizes))
+
+
+FULL = {"tiny": tiny, "qwen3_gateup": qwen3_gateup, "masked_down": masked_down,
+        "glm_up": glm_up, "dsv3": dsv3}
+
+
+def by_name(name: str) -> Workload:
+    if name.endswith("_small"):
+        return FULL[name[: -len("_small")]]("small")
+    return FULL[name]()
+
+
+def custom_ragged(name: str, sizes, k: int, n: int, seed: int, m: Optional[int] = None,
+                  x_std=1.0, w_std=0.02, dy_std=1.0) -> Workload:
+    """A ragged workload with explicit group sizes; ``m`` may exceed the sum
+    (unused trailing rows)."""
+    ends = _ends(sizes)
+    m = int(ends[-1]) if m is None else m
+    return Workload(name, "ragged", len(ends), m, k, n, seed=seed, offs=ends,
+                    x_std=x_std, w_std=w_std, dy_std=dy_std)
+
+
+def custom_masked(name: str, masked_m, max_m: int, k: int, n: int, seed: int,
+                  x_std=1.0, w_std=0.02) -> Workload:
+    mm = np.asarray(masked_m, dtype=np.int32)
+    return Workload(name, "masked", len(mm), max_m, k, n, seed=seed, masked_m=mm,
+                    x_std=x_std, w_std=w_std)
+
+
+# ---------------------------------------------------------------------------
+# tensor draws (torch; device chosen by the caller)
+# ---------------------------------------------------------------------------
+
+def _randn_bf16(shape, std: float, seed: int, stream: int, device):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000003 + stream)
+    t = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    return t.to(torch.bfloat16)
+
+
+def make_inputs(wl: Workload, device="cpu", need=("x", "w", "dy")):
+    """Draw the bf16 operands of ``wl`` on ``device``.
+
+    Returns a dict with any of ``x``, ``w``, ``dy`` (bf16 tensors) and
+    ``offs`` / ``masked_m`` (int32 tensors).  For the masked layout the
+    inactive rows of X hold bf16 quiet NaN, so a read of them would show.
+    """
+    import torch
+    out = {}
+    if "x" in need:
+        x = _randn_bf16(wl.x_shape(), wl.x_std, wl.seed, 1, device)
+        if wl.layout == "masked":
+            sizes = wl.group_sizes()
+            xi = x.view(torch.int16)
+            for e in range(wl.num_groups):
+                xi[e, int(sizes[e]):, :] = BF16_QNAN
+        out["x"] = x
+    if "w" in need:
+        out["w"] = _randn_bf16(wl.w_shape(), wl.w_std, wl.seed, 2, device)
+    if "dy" in need:
+        if wl.layout == "masked":
+            raise ValueError("the masked layout has a forward pass only")
+        out["dy"] = _randn_bf16((wl.m, wl.n), wl.dy_std, wl.seed, 3, device)
+    if wl.layout == "masked":
+        out["masked_m"] = torch.from_numpy(wl.masked_m.astype(np.int32)).to(device)
+    else:
+        out["offs"] = torch.from_numpy(wl.offs.astype(np.int32)).to(device)
+    return out
+
+
+def bf16_bits(t) -> np.ndarray:
+    """A bf16 torch tensor's bit patterns as a host uint16 array."""
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)

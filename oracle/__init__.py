@@ -1,0 +1,199 @@
+"""fp64 CPU oracle for the bf16 grouped GEMM -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library and its Python binding
+never touch it, and it shares no code with them: the arithmetic lives in
+``oracle.c`` (plain per-group loops in fp64 with its own bf16 codec) and this
+module only marshals numpy arrays into it.
+
+What each function computes is stated, with the passages it follows, at the
+top of ``oracle.c``.  Parity is pinned against exact rational brute force,
+closed forms, the three-pass adjoint identity and numpy's float64 matmul in
+``tests/test_oracle.py``; no function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (-O3, OpenMP, no fast-math) into
+    liboracle.so next to it."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        cmd = ["gcc", "-std=c11", "-O3", "-fopenmp", "-fPIC", "-shared",
+               "-fno-fast-math", "-ffp-contract=off", _SRC, "-o", tmp, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB):
+        build()
+    lib = ctypes.CDLL(_LIB)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I32 = ctypes.c_int32
+    sig = [P, P, P, I64, I64, I64, I32, P, I64, P, P, P]
+    for name in ("oracle_forward", "oracle_dgrad", "oracle_wgrad",
+                 "oracle_masked_forward"):
+        f = getattr(lib, name)
+        f.argtypes = sig
+        f.restype = ctypes.c_int
+    lib.oracle_round_bf16.argtypes = [ctypes.c_double]
+    lib.oracle_round_bf16.restype = ctypes.c_uint16
+    lib.oracle_round_bf16_array.argtypes = [P, I64, P]
+    lib.oracle_round_bf16_array.restype = None
+    lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
+    lib.oracle_decode_bf16.restype = ctypes.c_double
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 operands are passed as uint16 bit arrays")
+    return a
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def round_bf16(v) -> np.ndarray:
+    """fp64 -> bf16 bits, round to nearest, ties to even (oracle_round_bf16,
+    applied element-wise in C)."""
+    lib = _load()
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib.oracle_round_bf16_array(_ptr(v), ctypes.c_int64(v.size), _ptr(out))
+    return out
+
+
+def round_bf16_scalar(v: float) -> int:
+    return int(_load().oracle_round_bf16(float(v)))
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bits -> float64, exact (bits << 16 is the fp32 pattern)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+class Result:
+    """Oracle output: fp64 values, S = sum |a*b|, and which entries exist."""
+
+    def __init__(self, value, sabs, status, index):
+        self.value = value          # float64 [count, width]
+        self.sabs = sabs            # float64 [count, width]
+        self.status = status        # int32 [count]; 1 = computed
+        self.index = index          # the rows / pairs that were asked for
+
+
+def _run(fname, a, b, sel_arr, count, width, call_args):
+    lib = _load()
+    value = np.full((count, width), np.nan, dtype=np.float64)
+    sabs = np.full((count, width), np.nan, dtype=np.float64)
+    status = np.zeros(count, dtype=np.int32)
+    rc = getattr(lib, fname)(_ptr(a), _ptr(b), *call_args,
+                             _ptr(sel_arr), ctypes.c_int64(0 if sel_arr is None else len(sel_arr)),
+                             _ptr(value), _ptr(sabs), _ptr(status))
+    if rc != 0:
+        raise ValueError(f"{fname} rejected its arguments (code {rc})")
+    return value, sabs, status
+
+
+def forward(x, w, offs, rows=None) -> Result:
+    """Y rows of the ragged forward (oracle_forward).  x: uint16 [M,K];
+    w: uint16 [E,K,N]; offs: int32 [E] end offsets; rows: row indices or
+    None for all M rows."""
+    x, w = _u16(x), _u16(w)
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    m, k = x.shape
+    e, k2, n = w.shape
+    assert k2 == k and offs.shape == (e,)
+    sel = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    count = m if sel is None else len(sel)
+    v, s, st = _run("oracle_forward", x, w, sel, count, n,
+                    (_ptr(offs), ctypes.c_int64(m), ctypes.c_int64(k),
+                     ctypes.c_int64(n), ctypes.c_int32(e)))
+    return Result(v, s, st, sel if sel is not None else np.arange(m))
+
+
+def dgrad(dy, w, offs, rows=None) -> Result:
+    """dX rows of the ragged dgrad (oracle_dgrad).  dy: uint16 [M,N]."""
+    dy, w = _u16(dy), _u16(w)
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    m, n = dy.shape
+    e, k, n2 = w.shape
+    assert n2 == n and offs.shape == (e,)
+    sel = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    count = m if sel is None else len(sel)
+    v, s, st = _run("oracle_dgrad", dy, w, sel, count, k,
+                    (_ptr(offs), ctypes.c_int64(m), ctypes.c_int64(k),
+                     ctypes.c_int64(n), ctypes.c_int32(e)))
+    return Result(v, s, st, sel if sel is not None else np.arange(m))
+
+
+def wgrad(x, dy, offs, num_groups=None, pairs=None) -> Result:
+    """dW rows (expert g, k index kk) of the ragged wgrad (oracle_wgrad).
+    pairs: int [P,2] of (g, kk), or None for all E*K rows in order."""
+    x, dy = _u16(x), _u16(dy)
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    m, k = x.shape
+    m2, n = dy.shape
+    assert m2 == m
+    e = len(offs) if num_groups is None else num_groups
+    assert len(offs) == e
+    sel = None if pairs is None else np.ascontiguousarray(pairs, dtype=np.int64).reshape(-1, 2)
+    count = e * k if sel is None else len(sel)
+    lib = _load()
+    value = np.full((count, n), np.nan, dtype=np.float64)
+    sabs = np.full((count, n), np.nan, dtype=np.float64)
+    status = np.zeros(count, dtype=np.int32)
+    rc = lib.oracle_wgrad(_ptr(x), _ptr(dy), _ptr(offs), ctypes.c_int64(m),
+                          ctypes.c_int64(k), ctypes.c_int64(n), ctypes.c_int32(e),
+                          _ptr(sel), ctypes.c_int64(0 if sel is None else len(sel)),
+                          _ptr(value), _ptr(sabs), _ptr(status))
+    if rc != 0:
+        raise ValueError(f"oracle_wgrad rejected its arguments (code {rc})")
+    idx = sel if sel is not None else np.stack(
+        [np.repeat(np.arange(e), k), np.tile(np.arange(k), e)], axis=1)
+    return Result(value, sabs, status, idx)
+
+
+def masked_forward(x, w, masked_m, rows=None) -> Result:
+    """Rows of the masked forward (oracle_masked_forward).  x: uint16
+    [E, max_m, K]; rows: flat indices e*max_m + r, or None for all."""
+    x, w = _u16(x), _u16(w)
+    masked_m = np.ascontiguousarray(masked_m, dtype=np.int32)
+    e, max_m, k = x.shape
+    e2, k2, n = w.shape
+    assert e2 == e and k2 == k and masked_m.shape == (e,)
+    sel = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    count = e * max_m if sel is None else len(sel)
+    v, s, st = _run("oracle_masked_forward", x, w, sel, count, n,
+                    (_ptr(masked_m), ctypes.c_int64(max_m), ctypes.c_int64(k),
+                     ctypes.c_int64(n), ctypes.c_int32(e)))
+    return Result(v, s, st, sel if sel is not None else np.arange(e * max_m))
