@@ -1,0 +1,149 @@
+/*
+ * gg.h -- C ABI of the bf16 grouped (ragged, per-expert) GEMM for MI355X
+ * (gfx950).
+ *
+ * The operation (PyTorch issue #152668, "Easy repro scenario", and its
+ * backward): a 2-D activation X[M,K], a packed 3-D weight W[E,K,N] and int32
+ * cumulative END offsets offs[E].  Expert g owns rows [end(g-1), end(g)) of
+ * X, with end(-1) = 0, and
+ *
+ *   forward  Y[i, :]  = X[i, :] . W[g]            for each row i of expert g
+ *   dgrad    dX[i, :] = dY[i, :] . W[g]^T          (the input gradient)
+ *   wgrad    dW[g]    = X[rows of g]^T . dY[rows of g]   (the weight gradient)
+ *
+ * The masked variant (sglang PR #32385, "Evidence": A[E, max_m, K], a
+ * per-expert active count masked_m[E], output D[E, max_m, N]) computes
+ * D[e, r, :] = A[e, r, :] . W[e] for r < masked_m[e].
+ *
+ * Common contract of every entry point
+ * ------------------------------------
+ *  - Tensors are bf16 (uint16 storage), row-major and densely packed, in
+ *    device memory the CALLER owns.  The library allocates nothing, frees
+ *    nothing, needs no workspace, never copies device -> host and never
+ *    synchronises: it validates the arguments on the host, then enqueues
+ *    kernels on `stream` (a hipStream_t; NULL = the default stream) and
+ *    returns.  Group sizes stay on the device (TransformerEngine PR #3542,
+ *    "Changes": expert counts remain on the GPU), so calls are safe to
+ *    capture in a HIP graph.
+ *  - offs / masked_m are int32 device arrays of num_groups entries.  The
+ *    device clamps them: end(g) = min(max(offs[g], end(g-1)), M) and
+ *    active(e) = min(max(masked_m[e], 0), max_m).  Bad values therefore give
+ *    empty or shortened experts, never an out-of-range access or a hang.
+ *  - Outputs are overwritten (alpha = 1, beta = 0): an output element is
+ *    written without being read.  Elements the operation does not define
+ *    are left untouched (TransformerEngine PR #3542, "Changes": unused
+ *    capacity of caller-owned outputs is preserved; TileOPs issue #1566,
+ *    "Summary": no output memset).
+ *  - Host-checkable errors return a status before anything is enqueued;
+ *    outputs are then untouched.  A failed kernel launch returns
+ *    GG_ERR_HIP.  There is no fallback path of any kind.
+ *  - Requirements: k % 8 == 0 and n % 8 == 0 (16-byte rows), every pointer
+ *    16-byte aligned, 1 <= num_groups <= GG_MAX_GROUPS, m (or max_m) >= 0,
+ *    8 <= k, n <= GG_MAX_KN, and fewer than 2^31 rows (m, or num_groups *
+ *    max_m for the masked layout).
+ *  - Concurrent calls on different streams that write the same output race;
+ *    calls on one stream are ordered.
+ */
+#ifndef GG_H
+#define GG_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GG_MAX_GROUPS 2048
+#define GG_MAX_KN (1 << 20)   /* largest k and n */
+
+typedef enum {
+    GG_OK = 0,
+    GG_ERR_NULL_PTR = 1,   /* a required pointer is NULL */
+    GG_ERR_BAD_DIM = 2,    /* negative or zero size where not allowed, k or n not a multiple of 8, overflow */
+    GG_ERR_ALIGNMENT = 3,  /* a pointer is not 16-byte aligned */
+    GG_ERR_BAD_DTYPE = 4,  /* unknown output dtype */
+    GG_ERR_LIMIT = 5,      /* num_groups outside [1, GG_MAX_GROUPS] */
+    GG_ERR_HIP = 6         /* the HIP runtime reported an error (see gg_last_error) */
+} gg_status;
+
+typedef enum {
+    GG_BF16 = 0,           /* bf16 output, fp32 result rounded to nearest even */
+    GG_F32 = 1             /* fp32 output, the fp32 accumulator as is */
+} gg_dtype;
+
+/*
+ * gg_forward -- Y = X . W[g] on the rows of each expert.
+ *   x    [m, k]     bf16, rows grouped contiguously by expert
+ *   w    [E, k, n]  bf16, one packed buffer (E = num_groups)
+ *   offs [E]        int32 cumulative end offsets, device memory
+ *   y    [m, n]     y_dtype; rows [0, end(E-1)) are written, rows at or
+ *                   past end(E-1) are neither read nor written
+ * Cited passage: PyTorch issue #152668, "Easy repro scenario" (the forward
+ * of the grouped call on x[M,K], w[E,K,N], int32 offsets).
+ */
+gg_status gg_forward(const void* x, const void* w, const int32_t* offs,
+                     void* y, gg_dtype y_dtype, int64_t m, int64_t k,
+                     int64_t n, int32_t num_groups, void* stream);
+
+/*
+ * gg_dgrad -- dX = dY . W[g]^T on the rows of each expert.
+ *   dy   [m, n]     bf16
+ *   w    [E, k, n]  bf16
+ *   offs [E]        int32 cumulative end offsets, device memory
+ *   dx   [m, k]     dx_dtype; rows [0, end(E-1)) are written, the rest
+ *                   untouched
+ * Cited passage: PyTorch issue #152668, "Easy repro scenario" (the
+ * backward through the grouped call), and TransformerEngine PR #3542,
+ * "Changes" (the dgrad pass of the grouped GEMM).
+ */
+gg_status gg_dgrad(const void* dy, const void* w, const int32_t* offs,
+                   void* dx, gg_dtype dx_dtype, int64_t m, int64_t k,
+                   int64_t n, int32_t num_groups, void* stream);
+
+/*
+ * gg_wgrad -- dW[g] = X[rows of g]^T . dY[rows of g] for every expert.
+ *   x    [m, k]     bf16
+ *   dy   [m, n]     bf16
+ *   offs [E]        int32 cumulative end offsets, device memory
+ *   dw   [E, k, n]  dw_dtype; ALL of it is written (overwrite, not
+ *                   accumulate); an expert with no rows gets +0.0 everywhere
+ *   Rows of x and dy at or past end(E-1) are never read.
+ * Cited passages: PyTorch issue #152668, "Describe the bug" (an expert with
+ * zero tokens must not hang the backward) and TransformerEngine PR #3542,
+ * "Changes" / "Validation" (overwrite wgrad; empty experts).
+ */
+gg_status gg_wgrad(const void* x, const void* dy, const int32_t* offs,
+                   void* dw, gg_dtype dw_dtype, int64_t m, int64_t k,
+                   int64_t n, int32_t num_groups, void* stream);
+
+/*
+ * gg_masked_forward -- Y[e, r, :] = X[e, r, :] . W[e] for r < masked_m[e].
+ *   x        [E, max_m, k]  bf16; inactive rows are never read (they may
+ *                           hold anything, NaN included)
+ *   w        [E, k, n]      bf16
+ *   masked_m [E]            int32 active-row counts, device memory
+ *   y        [E, max_m, n]  y_dtype; only active rows are written
+ * Cited passage: sglang PR #32385, "Evidence" (the masked grouped GEMM over
+ * [E, max_m, K] with per-expert masked_m) and "Cause" (consumers must not
+ * depend on inactive rows).
+ */
+gg_status gg_masked_forward(const void* x, const void* w,
+                            const int32_t* masked_m, void* y,
+                            gg_dtype y_dtype, int64_t max_m, int64_t k,
+                            int64_t n, int32_t num_groups, void* stream);
+
+/* Static description of a status code. */
+const char* gg_status_str(gg_status s);
+
+/* Text of the last error seen by the calling thread (argument check or HIP
+ * runtime message); "" when the last call succeeded. */
+const char* gg_last_error(void);
+
+/* Library version string. */
+const char* gg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GG_H */

@@ -1,0 +1,223 @@
+"""ctypes binding of libgg.so (the C ABI in include/gg.h).
+
+Argument marshalling only: shapes, dtypes and devices are checked, outputs
+are allocated with ``torch.empty`` when the caller passes none (the library
+itself allocates nothing), and the pointers plus the current HIP stream go to
+the C entry point of the same name.  Every step of the computation runs in
+the HIP kernels; there is no fallback: if the library is missing or a call
+fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libgg.so")
+_HEADER = os.path.join(os.path.dirname(_PKG), "include", "gg.h")
+_lib = None
+
+GG_BF16 = 0
+GG_F32 = 1
+
+STATUS = {
+    0: "GG_OK",
+    1: "GG_ERR_NULL_PTR",
+    2: "GG_ERR_BAD_DIM",
+    3: "GG_ERR_ALIGNMENT",
+    4: "GG_ERR_BAD_DTYPE",
+    5: "GG_ERR_LIMIT",
+    6: "GG_ERR_HIP",
+}
+
+
+class GGError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        self.status = status
+        self.status_name = STATUS.get(status, str(status))
+        super().__init__(f"{fn} failed: {self.status_name}: {message}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def header_path() -> str:
+    return _HEADER
+
+
+def load():
+    """Load libgg.so (built in-tree by moe_grouped_gemm_ragged_amd.build)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m moe_grouped_gemm_ragged_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    I32 = ctypes.c_int32
+    sig = [P, P, P, P, ctypes.c_int, I64, I64, I64, I32, P]
+    for name in ("gg_forward", "gg_dgrad", "gg_wgrad", "gg_masked_forward"):
+        f = getattr(lib, name)
+        f.argtypes = sig
+        f.restype = ctypes.c_int
+    lib.gg_status_str.argtypes = [ctypes.c_int]
+    lib.gg_status_str.restype = ctypes.c_char_p
+    lib.gg_last_error.argtypes = []
+    lib.gg_last_error.restype = ctypes.c_char_p
+    lib.gg_version.argtypes = []
+    lib.gg_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def header_symbols():
+    """Names of the functions include/gg.h declares."""
+    with open(_HEADER) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gg_[a-z_]+)\s*\(", text)))
+
+
+def call_raw(name: str, *args) -> int:
+    """Call a C entry point with raw integer pointers/sizes; returns the
+    gg_status code."""
+    return int(getattr(load(), name)(*args))
+
+
+def last_error() -> str:
+    return load().gg_last_error().decode()
+
+
+# ---------------------------------------------------------------------------
+# torch-level helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.bfloat16:
+        return GG_BF16
+    if dt == torch.float32:
+        return GG_F32
+    raise TypeError(f"unsupported output dtype {dt}; use torch.bfloat16 or torch.float32")
+
+
+def _check(t, name, dtype, ndim, device):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _invoke(name, a, b, groups, out, out_code, m, k, n, e, device):
+    rc = call_raw(name, a.data_ptr(), b.data_ptr(), groups.data_ptr(), out.data_ptr(), out_code,
+                  int(m), int(k), int(n), int(e), _stream_handle(device))
+    if rc != 0:
+        raise GGError(name, rc, last_error())
+
+
+def forward(x, w, offs, out: Optional["torch.Tensor"] = None, out_dtype=None):
+    """Y[rows of g] = X[rows of g] . W[g] (gg_forward).  x: bf16 [m,k];
+    w: bf16 [E,k,n]; offs: int32 [E] cumulative end offsets on the device.
+    Rows of ``out`` at or past offs[-1] are left untouched."""
+    torch = _torch()
+    dev = x.device
+    _check(x, "x", torch.bfloat16, 2, dev)
+    _check(w, "w", torch.bfloat16, 3, dev)
+    _check(offs, "offs", torch.int32, 1, dev)
+    m, k = x.shape
+    e, k2, n = w.shape
+    if k2 != k or offs.shape[0] != e:
+        raise ValueError("shape mismatch between x, w and offs")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check(out, "out", out.dtype, 2, dev)
+    if tuple(out.shape) != (m, n):
+        raise ValueError(f"out must be [{m}, {n}]")
+    _invoke("gg_forward", x, w, offs, out, _dtype_code(out.dtype), m, k, n, e, dev)
+    return out
+
+
+def dgrad(dy, w, offs, out=None, out_dtype=None):
+    """dX[rows of g] = dY[rows of g] . W[g]^T (gg_dgrad).  dy: bf16 [m,n]."""
+    torch = _torch()
+    dev = dy.device
+    _check(dy, "dy", torch.bfloat16, 2, dev)
+    _check(w, "w", torch.bfloat16, 3, dev)
+    _check(offs, "offs", torch.int32, 1, dev)
+    m, n = dy.shape
+    e, k, n2 = w.shape
+    if n2 != n or offs.shape[0] != e:
+        raise ValueError("shape mismatch between dy, w and offs")
+    if out is None:
+        out = torch.empty((m, k), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check(out, "out", out.dtype, 2, dev)
+    if tuple(out.shape) != (m, k):
+        raise ValueError(f"out must be [{m}, {k}]")
+    _invoke("gg_dgrad", dy, w, offs, out, _dtype_code(out.dtype), m, k, n, e, dev)
+    return out
+
+
+def wgrad(x, dy, offs, out=None, out_dtype=None):
+    """dW[g] = X[rows of g]^T . dY[rows of g] for every expert (gg_wgrad);
+    all of ``out`` [E,k,n] is written, empty experts get +0.0."""
+    torch = _torch()
+    dev = x.device
+    _check(x, "x", torch.bfloat16, 2, dev)
+    _check(dy, "dy", torch.bfloat16, 2, dev)
+    _check(offs, "offs", torch.int32, 1, dev)
+    m, k = x.shape
+    m2, n = dy.shape
+    e = offs.shape[0]
+    if m2 != m:
+        raise ValueError("x and dy must have the same number of rows")
+    if out is None:
+        out = torch.empty((e, k, n), dtype=out_dtype or torch.float32, device=dev)
+    _check(out, "out", out.dtype, 3, dev)
+    if tuple(out.shape) != (e, k, n):
+        raise ValueError(f"out must be [{e}, {k}, {n}]")
+    _invoke("gg_wgrad", x, dy, offs, out, _dtype_code(out.dtype), m, k, n, e, dev)
+    return out
+
+
+def masked_forward(x, w, masked_m, out=None, out_dtype=None):
+    """Y[e, r] = X[e, r] . W[e] for r < masked_m[e] (gg_masked_forward).
+    x: bf16 [E, max_m, k]; inactive rows are neither read nor written."""
+    torch = _torch()
+    dev = x.device
+    _check(x, "x", torch.bfloat16, 3, dev)
+    _check(w, "w", torch.bfloat16, 3, dev)
+    _check(masked_m, "masked_m", torch.int32, 1, dev)
+    e, max_m, k = x.shape
+    e2, k2, n = w.shape
+    if e2 != e or k2 != k or masked_m.shape[0] != e:
+        raise ValueError("shape mismatch between x, w and masked_m")
+    if out is None:
+        out = torch.empty((e, max_m, n), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check(out, "out", out.dtype, 3, dev)
+    if tuple(out.shape) != (e, max_m, n):
+        raise ValueError(f"out must be [{e}, {max_m}, {n}]")
+    _invoke("gg_masked_forward", x, w, masked_m, out, _dtype_code(out.dtype), max_m, k, n, e, dev)
+    return out

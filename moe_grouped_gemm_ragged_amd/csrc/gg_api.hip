@@ -1,0 +1,142 @@
+// gg_api.hip -- the C ABI of include/gg.h: argument checks on the host, then
+// one kernel launch on the caller's stream.  Nothing here allocates device
+// memory, copies device -> host or synchronises.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+#include <cstdio>
+#include <string>
+
+#include "gg.h"
+#include "gg_internal.h"
+
+static_assert(GG_MAX_GROUPS == GG_MAX_GROUPS_DEV, "group limit mismatch");
+
+namespace {
+
+thread_local std::string g_last_error;
+
+gg_status fail(gg_status s, const char* what) {
+  g_last_error = what;
+  return s;
+}
+
+// Compute-unit count per device, read once (a device attribute query; no
+// allocation, no synchronisation).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
+gg_status device_cus(int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_error = std::string("hipGetDevice: ") + hipGetErrorString(e);
+    return GG_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(GG_ERR_HIP, "device ordinal out of range");
+  int cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || cus <= 0) {
+      g_last_error = std::string("hipDeviceGetAttribute: ") + hipGetErrorString(e);
+      return GG_ERR_HIP;
+    }
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  *out = cus;
+  return GG_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared checks.  rows = m (ragged) or max_m (masked).
+gg_status check(const void* p0, const void* p1, const void* groups, const void* out, gg_dtype dt,
+                int64_t rows, int64_t k, int64_t n, int32_t E) {
+  if (!p0 || !p1 || !groups || !out) return fail(GG_ERR_NULL_PTR, "a required pointer is NULL");
+  if (dt != GG_BF16 && dt != GG_F32) return fail(GG_ERR_BAD_DTYPE, "output dtype must be GG_BF16 or GG_F32");
+  if (E < 1 || E > GG_MAX_GROUPS) return fail(GG_ERR_LIMIT, "num_groups must be in [1, GG_MAX_GROUPS]");
+  if (rows < 0 || k < 8 || n < 8) return fail(GG_ERR_BAD_DIM, "need m >= 0, k >= 8, n >= 8");
+  if (k % 8 != 0 || n % 8 != 0) return fail(GG_ERR_BAD_DIM, "k and n must be multiples of 8");
+  // Row indices and reduction lengths are int32 on the device; element
+  // offsets are int64.  Keep every count comfortably inside both.
+  const int64_t lim31 = (int64_t(1) << 31) - 1;
+  if (rows > lim31) return fail(GG_ERR_BAD_DIM, "row count exceeds 2^31 - 1");
+  // Per-tile byte offsets are 32-bit: 256 rows of k or n fp32 values must
+  // stay below 2^31 bytes.
+  if (k > GG_MAX_KN || n > GG_MAX_KN) return fail(GG_ERR_BAD_DIM, "k and n must not exceed GG_MAX_KN");
+  if ((double)(rows + E) * (double)(k > n ? k : n) * 4.0 > 4.0e18)
+    return fail(GG_ERR_BAD_DIM, "problem too large");
+  if (!aligned16(p0) || !aligned16(p1) || !aligned16(out) || !aligned16(groups))
+    return fail(GG_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+  return GG_OK;
+}
+
+gg_status run(int mode, const void* a, const void* b, const int32_t* groups, void* c, gg_dtype dt,
+              int64_t m, int64_t k, int64_t n, int32_t E, void* stream) {
+  int cus = 0;
+  gg_status s = device_cus(&cus);
+  if (s != GG_OK) return s;
+  hipError_t e = gg::launch(mode, a, b, groups, c, dt == GG_F32, m, k, n, E, cus,
+                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_error = std::string("kernel launch: ") + hipGetErrorString(e);
+    return GG_ERR_HIP;
+  }
+  g_last_error.clear();
+  return GG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gg_status gg_forward(const void* x, const void* w, const int32_t* offs, void* y, gg_dtype y_dtype,
+                     int64_t m, int64_t k, int64_t n, int32_t num_groups, void* stream) {
+  gg_status s = check(x, w, offs, y, y_dtype, m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  return run(0, x, w, offs, y, y_dtype, m, k, n, num_groups, stream);
+}
+
+gg_status gg_dgrad(const void* dy, const void* w, const int32_t* offs, void* dx, gg_dtype dx_dtype,
+                   int64_t m, int64_t k, int64_t n, int32_t num_groups, void* stream) {
+  gg_status s = check(dy, w, offs, dx, dx_dtype, m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  return run(1, dy, w, offs, dx, dx_dtype, m, k, n, num_groups, stream);
+}
+
+gg_status gg_wgrad(const void* x, const void* dy, const int32_t* offs, void* dw, gg_dtype dw_dtype,
+                   int64_t m, int64_t k, int64_t n, int32_t num_groups, void* stream) {
+  gg_status s = check(x, dy, offs, dw, dw_dtype, m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  return run(2, x, dy, offs, dw, dw_dtype, m, k, n, num_groups, stream);
+}
+
+gg_status gg_masked_forward(const void* x, const void* w, const int32_t* masked_m, void* y,
+                            gg_dtype y_dtype, int64_t max_m, int64_t k, int64_t n,
+                            int32_t num_groups, void* stream) {
+  gg_status s = check(x, w, masked_m, y, y_dtype, max_m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  if ((double)num_groups * (double)max_m > 2147483647.0)
+    return fail(GG_ERR_BAD_DIM, "num_groups * max_m exceeds 2^31 - 1");
+  return run(3, x, w, masked_m, y, y_dtype, max_m, k, n, num_groups, stream);
+}
+
+const char* gg_status_str(gg_status s) {
+  switch (s) {
+    case GG_OK: return "GG_OK";
+    case GG_ERR_NULL_PTR: return "GG_ERR_NULL_PTR: a required pointer is NULL";
+    case GG_ERR_BAD_DIM: return "GG_ERR_BAD_DIM: invalid dimension";
+    case GG_ERR_ALIGNMENT: return "GG_ERR_ALIGNMENT: pointer not 16-byte aligned";
+    case GG_ERR_BAD_DTYPE: return "GG_ERR_BAD_DTYPE: unknown output dtype";
+    case GG_ERR_LIMIT: return "GG_ERR_LIMIT: num_groups out of range";
+    case GG_ERR_HIP: return "GG_ERR_HIP: HIP runtime error";
+  }
+  return "unknown gg_status";
+}
+
+const char* gg_last_error(void) { return g_last_error.c_str(); }
+
+const char* gg_version(void) { return "gg 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,17 @@
+// gg_internal.h -- declarations shared by the host API and the kernel file.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+// Experts per call the device-side decode holds in LDS.  Must equal
+// GG_MAX_GROUPS in include/gg.h.
+#define GG_MAX_GROUPS_DEV 2048
+
+namespace gg {
+// mode: 0 forward, 1 dgrad, 2 wgrad, 3 masked forward.  Arguments were
+// validated by the caller.  Launches one persistent grid of at most
+// num_cus workgroups on `stream`.
+hipError_t launch(int mode, const void* a, const void* b, const int32_t* groups, void* c,
+                  bool out_f32, int64_t m, int64_t k, int64_t n, int32_t num_groups,
+                  int num_cus, hipStream_t stream);
+}  // namespace gg

@@ -1,0 +1,82 @@
+"""The C ABI on the host (no GPU needed): the library loads, exports every
+function include/gg.h declares, and rejects bad arguments with the
+documented status before touching the HIP runtime."""
+import ctypes
+import re
+
+import pytest
+
+from moe_grouped_gemm_ragged_amd import binding as gg
+
+ENTRY = ["gg_forward", "gg_dgrad", "gg_wgrad", "gg_masked_forward"]
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gg.load()
+
+
+def test_header_declares_the_four_passes():
+    syms = gg.header_symbols()
+    for name in ENTRY + ["gg_status_str", "gg_last_error", "gg_version"]:
+        assert name in syms
+
+
+def test_library_exports_every_header_symbol(lib):
+    for name in gg.header_symbols():
+        assert hasattr(lib, name), f"libgg.so does not export {name}"
+
+
+def test_no_torch_types_in_header():
+    with open(gg.header_path()) as f:
+        text = f.read()
+    assert "torch" not in re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+
+
+def test_status_strings(lib):
+    for code, name in gg.STATUS.items():
+        assert lib.gg_status_str(code).decode().startswith(name)
+    assert lib.gg_version().decode().startswith("gg ")
+
+
+# Fake but 16-byte aligned device addresses: every case below must be
+# rejected by the host checks, so nothing is ever dereferenced or launched.
+A = 0x10000
+OK = dict(a=A, b=A + 0x100, g=A + 0x200, c=A + 0x300, dt=0, m=64, k=64, n=64, e=4, s=0)
+
+
+def call(name, **kw):
+    v = dict(OK, **kw)
+    return gg.call_raw(name, v["a"], v["b"], v["g"], v["c"], v["dt"], v["m"], v["k"], v["n"],
+                       v["e"], v["s"])
+
+
+@pytest.mark.parametrize("name", ENTRY)
+@pytest.mark.parametrize("case,status", [
+    (dict(a=0), 1), (dict(b=0), 1), (dict(g=0), 1), (dict(c=0), 1),
+    (dict(m=-1), 2), (dict(k=0), 2), (dict(n=0), 2), (dict(k=12), 2), (dict(n=20), 2),
+    (dict(k=(1 << 20) + 8), 2), (dict(m=1 << 31), 2),
+    (dict(a=A + 8), 3), (dict(b=A + 2), 3), (dict(c=A + 4), 3), (dict(g=A + 4), 3),
+    (dict(dt=2), 4), (dict(dt=-1), 4),
+    (dict(e=0), 5), (dict(e=-3), 5), (dict(e=2049), 5),
+])
+def test_bad_arguments_rejected_before_launch(lib, name, case, status):
+    rc = call(name, **case)
+    assert rc == status, (name, case, rc, gg.last_error())
+    assert gg.last_error() != ""
+
+
+def test_masked_row_limit(lib):
+    rc = call("gg_masked_forward", m=1 << 24, e=256)
+    assert rc == 2 and "max_m" in gg.last_error()
+
+
+def test_binding_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(8, 8, dtype=torch.float32)
+    w = torch.zeros(1, 8, 8, dtype=torch.bfloat16)
+    offs = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(TypeError):
+        gg.forward(x, w, offs)
+    with pytest.raises(ValueError):
+        gg.forward(torch.zeros(8, 16, dtype=torch.bfloat16), w, offs)

@@ -1,0 +1,267 @@
+"""GPU parity: the HIP kernels (through the C ABI) against the fp64 oracle.
+
+* every pass of the scaled-down workloads, compared element by element with
+  all rows, both output dtypes, sentinel-filled outputs (rows that belong to
+  no expert must come back bit-identical);
+* the five full-size workloads, in the same launch configuration the
+  benchmark times, on sampled rows (fwd, dgrad, masked) and sampled
+  (expert, k) rows of dW (wgrad), chosen to hit every expert's first and
+  last rows, tile boundaries and random rows.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+from moe_grouped_gemm_ragged_amd import binding as gg
+from moe_grouped_gemm_ragged_amd import synth
+from gpu_util import device, host, raw_bits, say, sentinel_bits, sentinel_tensor
+from parity import Report, check
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny", "qwen3_gateup_small", "dsv3_small", "glm_up_small"]
+
+
+def _dt(name):
+    import torch
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
+
+
+def _group_len_per_row(wl, m):
+    sizes = wl.group_sizes()
+    L = np.zeros(m, dtype=np.float64)
+    start = 0
+    for s in sizes:
+        L[start:start + s] = max(int(s), 1)
+        start += s
+    return L
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("name", SMALL)
+def test_forward_small(name, out):
+    dev = device()
+    import torch
+    wl = synth.by_name(name)
+    t = synth.make_inputs(wl, dev)
+    y = sentinel_tensor((wl.m, wl.n), _dt(out), dev)
+    say("forward", name, out)
+    gg.forward(t["x"], t["w"], t["offs"], out=y)
+    torch.cuda.synchronize()
+    ref = oracle.forward(synth.bf16_bits(t["x"]), synth.bf16_bits(t["w"]), wl.offs)
+    yh = host(y)
+    used = ref.status == 1
+    rep = Report()
+    check(yh[used], ref.value[used], ref.sabs[used], wl.k, f"forward {name}", rep)
+    assert np.all(raw_bits(yh[~used]) == sentinel_bits(_dt(out))), "unused rows were written"
+    print(name, out, rep)
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+@pytest.mark.parametrize("name", SMALL)
+def test_dgrad_small(name, out):
+    dev = device()
+    import torch
+    wl = synth.by_name(name)
+    t = synth.make_inputs(wl, dev)
+    dx = sentinel_tensor((wl.m, wl.k), _dt(out), dev)
+    say("dgrad", name, out)
+    gg.dgrad(t["dy"], t["w"], t["offs"], out=dx)
+    torch.cuda.synchronize()
+    ref = oracle.dgrad(synth.bf16_bits(t["dy"]), synth.bf16_bits(t["w"]), wl.offs)
+    dh = host(dx)
+    used = ref.status == 1
+    rep = Report()
+    check(dh[used], ref.value[used], ref.sabs[used], wl.n, f"dgrad {name}", rep)
+    assert np.all(raw_bits(dh[~used]) == sentinel_bits(_dt(out))), "unused rows were written"
+    print(name, out, rep)
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+@pytest.mark.parametrize("name", SMALL)
+def test_wgrad_small(name, out):
+    dev = device()
+    import torch
+    wl = synth.by_name(name)
+    t = synth.make_inputs(wl, dev)
+    dw = sentinel_tensor((wl.num_groups, wl.k, wl.n), _dt(out), dev)
+    say("wgrad", name, out)
+    gg.wgrad(t["x"], t["dy"], t["offs"], out=dw)
+    torch.cuda.synchronize()
+    ref = oracle.wgrad(synth.bf16_bits(t["x"]), synth.bf16_bits(t["dy"]), wl.offs)
+    dh = host(dw).reshape(wl.num_groups * wl.k, wl.n)
+    sizes = wl.group_sizes()
+    L = np.repeat(np.maximum(sizes, 1), wl.k)[:, None]
+    rep = Report()
+    check(dh, ref.value, ref.sabs, L, f"wgrad {name}", rep)
+    empty = np.repeat(sizes == 0, wl.k)
+    assert np.all(raw_bits(dh[empty]) == 0), "an empty expert's dW is not +0.0"
+    print(name, out, rep, "empty experts:", int((sizes == 0).sum()))
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_masked_small(out):
+    dev = device()
+    import torch
+    wl = synth.by_name("masked_down_small")
+    t = synth.make_inputs(wl, dev, need=("x", "w"))
+    y = sentinel_tensor((wl.num_groups, wl.m, wl.n), _dt(out), dev)
+    say("masked", wl.name, out)
+    gg.masked_forward(t["x"], t["w"], t["masked_m"], out=y)
+    torch.cuda.synchronize()
+    ref = oracle.masked_forward(synth.bf16_bits(t["x"]), synth.bf16_bits(t["w"]), wl.masked_m)
+    yh = host(y).reshape(wl.num_groups * wl.m, wl.n)
+    act = ref.status == 1
+    rep = Report()
+    check(yh[act], ref.value[act], ref.sabs[act], wl.k, "masked", rep)
+    assert np.all(raw_bits(yh[~act]) == sentinel_bits(_dt(out))), "inactive rows were written"
+    assert np.all(np.isfinite(ref.value[act]))
+    print(out, rep)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, sampled
+# ---------------------------------------------------------------------------
+
+def sample_rows(wl, rng, n_random=384):
+    sizes = wl.group_sizes()
+    ends = np.cumsum(sizes)
+    starts = ends - sizes
+    rows = set()
+    for s, e in zip(starts, ends):
+        if e <= s:
+            continue
+        for r in (s, s + 1, e - 2, e - 1):
+            if s <= r < e:
+                rows.add(int(r))
+        # rows at the start and end of 256-row tiles inside the expert
+        for t0 in range(s, e, 256):
+            rows.add(int(t0))
+            rows.add(int(min(t0 + 255, e - 1)))
+    total = int(ends[-1])
+    if total > 0:
+        rows.update(int(r) for r in rng.integers(0, total, n_random))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+def sample_pairs(wl, rng, per_group=3):
+    sizes = wl.group_sizes()
+    pairs = []
+    for g in range(wl.num_groups):
+        ks = {0, wl.k - 1, int(rng.integers(0, wl.k))}
+        if sizes[g] == 0:
+            ks = set(range(0, wl.k, max(1, wl.k // 16)))   # cheap: empty sums
+        for kk in sorted(ks)[: max(per_group, len(ks))]:
+            pairs.append((g, kk))
+    return np.array(pairs, dtype=np.int64)
+
+
+_cache = {}
+
+
+def _full_inputs(name, need):
+    dev = device()
+    key = (name, need)
+    if key not in _cache:
+        _cache.clear()
+        import torch
+        torch.cuda.empty_cache()
+        wl = synth.by_name(name)
+        say("generate", name, need)
+        t = synth.make_inputs(wl, dev, need=need)
+        hb = {k: synth.bf16_bits(v) for k, v in t.items() if k in ("x", "w", "dy")}
+        _cache[key] = (wl, t, hb)
+    return _cache[key]
+
+
+@pytest.mark.parametrize("pass_", ["fwd", "dgrad", "wgrad"])
+@pytest.mark.parametrize("name", ["qwen3_gateup", "dsv3", "glm_up"])
+def test_full_size_sampled(name, pass_):
+    import torch
+    wl, t, hb = _full_inputs(name, ("x", "w", "dy"))
+    dev = t["x"].device
+    rng = np.random.default_rng(zlib.crc32(f"{name}/{pass_}".encode()))
+    rep = Report()
+    if pass_ == "fwd":
+        y = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device=dev)
+        say("full forward", name)
+        gg.forward(t["x"], t["w"], t["offs"], out=y)
+        torch.cuda.synchronize()
+        rows = sample_rows(wl, rng)
+        ref = oracle.forward(hb["x"], hb["w"], wl.offs, rows=rows)
+        got = host(y[torch.from_numpy(rows).to(dev)])
+        assert np.all(ref.status == 1)
+        check(got, ref.value, ref.sabs, wl.k, f"forward {name}", rep)
+    elif pass_ == "dgrad":
+        dx = torch.empty((wl.m, wl.k), dtype=torch.bfloat16, device=dev)
+        say("full dgrad", name)
+        gg.dgrad(t["dy"], t["w"], t["offs"], out=dx)
+        torch.cuda.synchronize()
+        rows = sample_rows(wl, rng)
+        ref = oracle.dgrad(hb["dy"], hb["w"], wl.offs, rows=rows)
+        got = host(dx[torch.from_numpy(rows).to(dev)])
+        check(got, ref.value, ref.sabs, wl.n, f"dgrad {name}", rep)
+    else:
+        dw = torch.empty((wl.num_groups, wl.k, wl.n), dtype=torch.float32, device=dev)
+        say("full wgrad", name)
+        gg.wgrad(t["x"], t["dy"], t["offs"], out=dw)
+        torch.cuda.synchronize()
+        pairs = sample_pairs(wl, rng)
+        ref = oracle.wgrad(hb["x"], hb["dy"], wl.offs, pairs=pairs)
+        flat = dw.view(wl.num_groups * wl.k, wl.n)
+        idx = torch.from_numpy(pairs[:, 0] * wl.k + pairs[:, 1]).to(dev)
+        got = host(flat[idx])
+        sizes = wl.group_sizes()
+        L = np.maximum(sizes[pairs[:, 0]], 1)[:, None]
+        check(got, ref.value, ref.sabs, L, f"wgrad {name}", rep)
+        # every empty expert's whole dW[g] is +0.0, bit for bit
+        empty = np.nonzero(sizes == 0)[0]
+        if len(empty):
+            z = host(dw[torch.from_numpy(empty).to(dev)])
+            assert np.all(z.view(np.uint32) == 0), "an empty expert's dW is not +0.0"
+    print(name, pass_, rep)
+
+
+def test_full_size_masked():
+    import torch
+    wl, t, hb = _full_inputs("masked_down", ("x", "w"))
+    dev = t["x"].device
+    y = sentinel_tensor((wl.num_groups, wl.m, wl.n), torch.bfloat16, dev)
+    say("full masked", wl.name)
+    gg.masked_forward(t["x"], t["w"], t["masked_m"], out=y)
+    torch.cuda.synchronize()
+    ref = oracle.masked_forward(hb["x"], hb["w"], wl.masked_m)
+    yh = host(y).reshape(wl.num_groups * wl.m, wl.n)
+    act = ref.status == 1
+    rep = Report()
+    check(yh[act], ref.value[act], ref.sabs[act], wl.k, "masked_down", rep)
+    assert np.all(yh[~act] == synth.OUT_SENTINEL_BF16), "inactive rows were written"
+    print(rep)
+
+
+def test_full_size_tiny_all_passes():
+    """The tiny reproduction is itself a full-size workload."""
+    import torch
+    dev = device()
+    wl = synth.tiny()
+    t = synth.make_inputs(wl, dev)
+    hb = {k: synth.bf16_bits(t[k]) for k in ("x", "w", "dy")}
+    y = sentinel_tensor((wl.m, wl.n), torch.bfloat16, dev)
+    dx = sentinel_tensor((wl.m, wl.k), torch.bfloat16, dev)
+    dw = sentinel_tensor((wl.num_groups, wl.k, wl.n), torch.float32, dev)
+    say("tiny all passes")
+    gg.forward(t["x"], t["w"], t["offs"], out=y)
+    gg.dgrad(t["dy"], t["w"], t["offs"], out=dx)
+    gg.wgrad(t["x"], t["dy"], t["offs"], out=dw)
+    torch.cuda.synchronize()
+    rf = oracle.forward(hb["x"], hb["w"], wl.offs)
+    rd = oracle.dgrad(hb["dy"], hb["w"], wl.offs)
+    rw = oracle.wgrad(hb["x"], hb["dy"], wl.offs)
+    used = rf.status == 1
+    check(host(y)[used], rf.value[used], rf.sabs[used], wl.k, "tiny fwd")
+    check(host(dx)[used], rd.value[used], rd.sabs[used], wl.n, "tiny dgrad")
+    check(host(dw).reshape(-1, wl.n), rw.value, rw.sabs, 24, "tiny wgrad")
+    assert np.all(host(y)[40:] == synth.OUT_SENTINEL_BF16)
+    assert np.all(host(dw)[1].view(np.uint32) == 0)
