@@ -1,0 +1,262 @@
+#!/usr/bin/env python3
+"""Benchmark of the bf16 grouped GEMM on one MI355X.
+
+One step = the three passes of the grouped GEMM (forward, dgrad, wgrad) over
+the GLM-up workload: 32 experts, 262144 rows, K = 6144, N = 4096, group sizes
+Dirichlet(1) proportions rounded to multiples of 128 (TileOPs issue #1566,
+"Summary", gives the shape).  Inputs are seeded synthetic bf16 data already
+resident in HBM; outputs are preallocated caller buffers (bf16 Y and dX,
+fp32 dW).  The line printed is whole-job TFLOP/s over the timed steps
+(3 x 2 x rows x K x N FLOP per step).
+
+Also reported: per-pass times from HIP events on the launch stream, the
+roofline object for the dominant kernel, the masked down-projection workload
+and the other shapes as context, and the fp64 CPU oracle timed on a bounded
+sample of the same workload (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense)
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def time_passes(fns, steps, warmup, torch):
+    """Run the list of (name, fn) ``warmup`` times, then ``steps`` times with
+    HIP events around every launch.  Returns (total seconds, {name: [ms]})."""
+    for _ in range(warmup):
+        for _, f in fns:
+            f()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = {name: [] for name, _ in fns}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        for name, f in fns:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            f()
+            b.record(stream)
+            evs[name].append((a, b))
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = {name: [a.elapsed_time(b) for a, b in v] for name, v in evs.items()}
+    return t1 - t0, ms
+
+
+def algorithmic_bytes(wl, pass_):
+    """Bytes the pass must move at minimum: active rows of its inputs and
+    outputs and the weights of experts with rows (wgrad: all of fp32 dW)."""
+    import numpy as np
+    sizes = wl.group_sizes()
+    rows = int(sizes.sum())
+    live = int((sizes > 0).sum())
+    k, n = wl.k, wl.n
+    if pass_ == "fwd":
+        return 2 * rows * k + 2 * live * k * n + 2 * rows * n
+    if pass_ == "dgrad":
+        return 2 * rows * n + 2 * live * k * n + 2 * rows * k
+    if pass_ == "wgrad":
+        return 2 * rows * k + 2 * rows * n + 4 * wl.num_groups * k * n
+    raise ValueError(pass_)
+
+
+def cpu_baseline(wl, t, synth, budget_s=15.0):
+    """The fp64 oracle on a bounded sample of the same workload: rows of the
+    forward and dgrad, (expert, k) rows of the wgrad, each sized from a short
+    calibration run to take about budget_s / 3 seconds."""
+    import numpy as np
+    import oracle
+    hb = {k: synth.bf16_bits(t[k]) for k in ("x", "w", "dy")}
+    rng = np.random.default_rng(2024)
+    total = wl.active_rows()
+    sizes = wl.group_sizes()
+    flops = 0.0
+    secs = 0.0
+    parts = []
+
+    def timed(fn, *args, **kw):
+        t0 = time.perf_counter()
+        fn(*args, **kw)
+        return time.perf_counter() - t0
+
+    # forward / dgrad: calibrate on 64 rows, then size the sample
+    for name, fn, a, per_row in (("forward", oracle.forward, (hb["x"], hb["w"], wl.offs), 2.0 * wl.k * wl.n),
+                                 ("dgrad", oracle.dgrad, (hb["dy"], hb["w"], wl.offs), 2.0 * wl.k * wl.n)):
+        cal = rng.integers(0, total, 64)
+        dt = timed(fn, *a, rows=cal)
+        rate = 64 * per_row / max(dt, 1e-6)
+        nrows = int(min(max(64, rate * budget_s / 3 / per_row), total))
+        rows = rng.integers(0, total, nrows)
+        dt = timed(fn, *a, rows=rows)
+        flops += nrows * per_row
+        secs += dt
+        parts.append(f"{name}: {nrows} random rows")
+    # wgrad: (expert, k) rows of dW, expert chosen with probability ~ rows
+    live = np.nonzero(sizes > 0)[0]
+    p = sizes[live] / sizes[live].sum()
+    mean_cost = 2.0 * float((sizes[live] * p).sum()) * wl.n
+    cal_pairs = np.stack([rng.choice(live, 8, p=p), rng.integers(0, wl.k, 8)], axis=1)
+    dt = timed(oracle.wgrad, hb["x"], hb["dy"], wl.offs, pairs=cal_pairs)
+    cost = 2.0 * float(sizes[cal_pairs[:, 0]].sum()) * wl.n
+    rate = cost / max(dt, 1e-6)
+    npairs = int(max(8, rate * budget_s / 3 / mean_cost))
+    pairs = np.stack([rng.choice(live, npairs, p=p), rng.integers(0, wl.k, npairs)], axis=1)
+    dt = timed(oracle.wgrad, hb["x"], hb["dy"], wl.offs, pairs=pairs)
+    flops += 2.0 * float(sizes[pairs[:, 0]].sum()) * wl.n
+    secs += dt
+    parts.append(f"wgrad: {npairs} (expert, k) rows of dW")
+    return {
+        "value": flops / secs / 1e12,
+        "unit": "TFLOP/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{wl.name}, {'; '.join(parts)}; {flops / 1e9:.1f} GFLOP in {secs:.1f} s",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the other workloads reported as context")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from moe_grouped_gemm_ragged_amd import binding as gg
+    from moe_grouped_gemm_ragged_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    gg.load()
+
+    wl = synth.glm_up()
+    log("generating", wl.name)
+    t = synth.make_inputs(wl, dev)
+    y = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device=dev)
+    dx = torch.empty((wl.m, wl.k), dtype=torch.bfloat16, device=dev)
+    dw = torch.empty((wl.num_groups, wl.k, wl.n), dtype=torch.float32, device=dev)
+    fns = [
+        ("fwd", lambda: gg.forward(t["x"], t["w"], t["offs"], out=y)),
+        ("dgrad", lambda: gg.dgrad(t["dy"], t["w"], t["offs"], out=dx)),
+        ("wgrad", lambda: gg.wgrad(t["x"], t["dy"], t["offs"], out=dw)),
+    ]
+    log("timing", args.steps, "steps after", args.warmup, "warmup steps")
+    secs, ms = time_passes(fns, args.steps, args.warmup, torch)
+    flop_pass = wl.flops()
+    flop_step = 3 * flop_pass
+    value = flop_step * args.steps / secs / 1e12
+
+    per_pass = {}
+    for name in ("fwd", "dgrad", "wgrad"):
+        avg = sum(ms[name]) / len(ms[name])
+        tf = flop_pass / (avg * 1e-3) / 1e12
+        per_pass[name] = {"ms": round(avg, 4), "TFLOP/s": round(tf, 2),
+                          "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                          "algorithmic_GB/s": round(algorithmic_bytes(wl, name) / (avg * 1e-3) / 1e9, 1)}
+    dom = max(per_pass, key=lambda k: per_pass[k]["ms"])
+    kernel_names = {"fwd": "grouped_gemm_kernel<0,false>", "dgrad": "grouped_gemm_kernel<1,false>",
+                    "wgrad": "grouped_gemm_kernel<2,true>"}
+    roofline = {
+        "bound": "mfma",
+        "kernel": f"{kernel_names[dom]} ({dom})",
+        "achieved": per_pass[dom]["TFLOP/s"],
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(per_pass[dom]["TFLOP/s"] / PEAK_BF16_TFLOPS, 4),
+        "traffic": None,
+    }
+
+    context = {}
+    if not args.no_context:
+        for name in ("qwen3_gateup", "dsv3"):
+            w2 = synth.by_name(name)
+            t2 = synth.make_inputs(w2, dev)
+            y2 = torch.empty((w2.m, w2.n), dtype=torch.bfloat16, device=dev)
+            dx2 = torch.empty((w2.m, w2.k), dtype=torch.bfloat16, device=dev)
+            dw2 = torch.empty((w2.num_groups, w2.k, w2.n), dtype=torch.float32, device=dev)
+            f2 = [("fwd", lambda: gg.forward(t2["x"], t2["w"], t2["offs"], out=y2)),
+                  ("dgrad", lambda: gg.dgrad(t2["dy"], t2["w"], t2["offs"], out=dx2)),
+                  ("wgrad", lambda: gg.wgrad(t2["x"], t2["dy"], t2["offs"], out=dw2))]
+            _, ms2 = time_passes(f2, 10, 3, torch)
+            entry = {}
+            for p, v in ms2.items():
+                avg = sorted(v)[len(v) // 2]
+                entry[p] = {"ms": round(avg, 4),
+                            "TFLOP/s": round(w2.flops() / (avg * 1e-3) / 1e12, 2),
+                            "algorithmic_GB/s": round(algorithmic_bytes(w2, p) / (avg * 1e-3) / 1e9, 1)}
+            context[name] = entry
+            del t2, y2, dx2, dw2
+        wm = synth.masked_down()
+        tm = synth.make_inputs(wm, dev, need=("x", "w"))
+        ym = torch.empty((wm.num_groups, wm.m, wm.n), dtype=torch.bfloat16, device=dev)
+        _, msm = time_passes([("masked", lambda: gg.masked_forward(tm["x"], tm["w"], tm["masked_m"], out=ym))],
+                             50, 5, torch)
+        avg = sorted(msm["masked"])[len(msm["masked"]) // 2]
+        live = int((wm.group_sizes() > 0).sum())
+        mbytes = 2 * wm.active_rows() * (wm.k + wm.n) + 2 * live * wm.k * wm.n
+        context["masked_down"] = {"ms": round(avg, 4),
+                                  "TFLOP/s": round(wm.flops() / (avg * 1e-3) / 1e12, 2),
+                                  "algorithmic_GB/s": round(mbytes / (avg * 1e-3) / 1e9, 1)}
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(wl, t, synth)
+
+    out = {
+        "metric": "grouped GEMM TFLOP/s (fwd/dgrad/wgrad) and % of bf16 MFMA peak, 1 MI355X",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(secs / args.steps * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "glm_up: 32 experts, 262144 rows (Dirichlet(1) sizes rounded to 128), "
+                        "K=6144, N=4096; step = forward + dgrad + wgrad",
+            "experts": wl.num_groups, "rows": wl.m, "k": wl.k, "n": wl.n,
+            "outputs": "Y bf16, dX bf16, dW fp32",
+            "flop_per_step": flop_step,
+        },
+        "frac_of_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "per_pass": per_pass,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "context": context,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -103,7 +103,9 @@ __device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t 
 // range explicitly (it would otherwise read the next row).
 __device__ __forceinline__ void load_contig(const Operand& op, int q0, int tid, u32x4 (&r)[8]) {
   const int c = tid & 7;
-  const uint32_t nrec = (uint32_t)op.rows * op.ld_bytes - 2u * (uint32_t)q0;
+  // Past the reduction end the record count is 0 (every load reads zero and
+  // touches no memory).
+  const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - 2u * (uint32_t)q0 : 0u;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(op.origin + 2 * (int64_t)q0, nrec);
   uint32_t voff = (uint32_t)(tid >> 3) * op.ld_bytes + 16u * (uint32_t)c;
   if (q0 + 8 * c >= op.red) voff = kOutOfRange;
@@ -121,8 +123,8 @@ __device__ __forceinline__ void load_contig(const Operand& op, int q0, int tid, 
 __device__ __forceinline__ void load_strided(const Operand& op, int q0, int tid, u32x4 (&r)[8]) {
   const int rb = tid & 7;
   const int cb = tid >> 3;
-  const int left = op.red - q0;                 // >= 1
-  const uint32_t nrec = (uint32_t)(left - 1) * op.ld_bytes + op.row_tail;
+  const int left = op.red - q0;
+  const uint32_t nrec = left > 0 ? (uint32_t)(left - 1) * op.ld_bytes + op.row_tail : 0u;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(op.origin + (int64_t)q0 * op.ld_bytes, nrec);
   const uint32_t voff = (uint32_t)(8 * rb) * op.ld_bytes + 16u * (uint32_t)cb;
 #pragma unroll
@@ -132,8 +134,14 @@ __device__ __forceinline__ void load_strided(const Operand& op, int q0, int tid,
 
 // ---- registers -> LDS --------------------------------------------------------
 
+// LDS tile layout: row r at r * 128 bytes, its 16-byte chunk c at chunk
+// position c ^ ((r / 2) mod 8).  The LDS serves 16 lanes (256 bytes) of a
+// 16-byte access per cycle; 16 consecutive rows at one logical chunk then
+// land on 16 distinct 16-byte bank groups (row parity picks the 128-byte
+// half, (r / 2) mod 8 the chunk), so fragment reads are conflict-free, and
+// so are row-pair writes of 8 chunks each.
 __device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
-  return (uint32_t)(row * (BK * 2) + ((chunk ^ (row & 7)) << 4));
+  return (uint32_t)(row * (BK * 2) + ((chunk ^ ((row >> 1) & 7)) << 4));
 }
 
 __device__ __forceinline__ void store_contig(uint8_t* lds, int tid, const u32x4 (&r)[8]) {
@@ -148,13 +156,21 @@ __device__ __forceinline__ void store_contig(uint8_t* lds, int tid, const u32x4 
 
 // Transpose the 8 x 8 block (r[j] holds reduction index j for 8 consecutive
 // rows) so that each of the 8 rows gets its 8 reduction values in one chunk.
+// Lanes with an odd row block visit the rows in the order 1, 0, 3, 2, ...:
+// each write instruction then covers a row pair of opposite parity across
+// 16 lanes, which the LDS serves without bank conflicts.
 __device__ __forceinline__ void store_strided(uint8_t* lds, int tid, const u32x4 (&r)[8]) {
   const int rb = tid & 7;
+  const int flip = (tid >> 3) & 1;
   const int row0 = 8 * (tid >> 3);
+  // byte selectors: low halves (even row) or high halves (odd row)
+  const uint32_t sel_even = flip ? 0x07060302u : 0x05040100u;
+  const uint32_t sel_odd = flip ? 0x05040100u : 0x07060302u;
 #pragma unroll
-  for (int qr = 0; qr < 8; ++qr) {
-    const int w = qr >> 1;                                  // dword holding row qr
-    const uint32_t sel = (qr & 1) ? 0x07060302u : 0x05040100u;
+  for (int s = 0; s < 8; ++s) {
+    const int w = s >> 1;                                   // dword holding rows 2w, 2w + 1
+    const uint32_t sel = (s & 1) ? sel_odd : sel_even;
+    const int qr = s ^ flip;
     u32x4 o;
     o[0] = perm_b32(r[1][w], r[0][w], sel);
     o[1] = perm_b32(r[3][w], r[2][w], sel);
@@ -174,6 +190,66 @@ __device__ __forceinline__ void store_op(uint8_t* lds, int tid, const u32x4 (&r)
   if constexpr (STRIDED) store_strided(lds, tid, r); else store_contig(lds, tid, r);
 }
 
+// ---- per-chunk forms of the above (for the interleaved main loop) --------------
+
+// Buffer resource and lane offset of one operand for one stage; chunk j is
+// at voff + j * step.
+struct LoadCtx {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t voff;
+  uint32_t step;
+};
+
+template <bool STRIDED>
+__device__ __forceinline__ LoadCtx load_ctx(const Operand& op, int q0, int tid) {
+  LoadCtx c;
+  if constexpr (STRIDED) {
+    const int rb = tid & 7;
+    const int cb = tid >> 3;
+    const int left = op.red - q0;
+    const uint32_t nrec = left > 0 ? (uint32_t)(left - 1) * op.ld_bytes + op.row_tail : 0u;
+    c.rs = make_rsrc(op.origin + (int64_t)q0 * op.ld_bytes, nrec);
+    c.voff = (uint32_t)(8 * rb) * op.ld_bytes + 16u * (uint32_t)cb;
+    c.step = op.ld_bytes;
+  } else {
+    const int ch = tid & 7;
+    const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - 2u * (uint32_t)q0 : 0u;
+    c.rs = make_rsrc(op.origin + 2 * (int64_t)q0, nrec);
+    c.voff = (uint32_t)(tid >> 3) * op.ld_bytes + 16u * (uint32_t)ch;
+    if (q0 + 8 * ch >= op.red) c.voff = kOutOfRange;
+    c.step = 32u * op.ld_bytes;
+  }
+  return c;
+}
+
+__device__ __forceinline__ u32x4 load_chunk(const LoadCtx& c, int j) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c.rs, c.voff + j * c.step, 0, 0));
+}
+
+// Write chunk j of the staged registers (red-contig: row tid/8 + 32 j;
+// red-strided: the j-th of the thread's 8 rows, transposed).
+template <bool STRIDED>
+__device__ __forceinline__ void store_chunk(uint8_t* lds, int tid, const u32x4 (&r)[8], int j) {
+  if constexpr (STRIDED) {
+    const int rb = tid & 7;
+    const int flip = (tid >> 3) & 1;
+    const int row0 = 8 * (tid >> 3);
+    const uint32_t sel_even = flip ? 0x07060302u : 0x05040100u;
+    const uint32_t sel_odd = flip ? 0x05040100u : 0x07060302u;
+    const int w = j >> 1;
+    const uint32_t sel = (j & 1) ? sel_odd : sel_even;
+    u32x4 o;
+    o[0] = perm_b32(r[1][w], r[0][w], sel);
+    o[1] = perm_b32(r[3][w], r[2][w], sel);
+    o[2] = perm_b32(r[5][w], r[4][w], sel);
+    o[3] = perm_b32(r[7][w], r[6][w], sel);
+    *reinterpret_cast<u32x4*>(lds + lds_off(row0 + (j ^ flip), rb)) = o;
+  } else {
+    const int row = (tid >> 3) + 32 * j;
+    *reinterpret_cast<u32x4*>(lds + lds_off(row, tid & 7)) = r[j];
+  }
+}
+
 // ---- MFMA over one staged reduction step ---------------------------------------
 
 __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* lds, int row, int chunk) {
@@ -181,26 +257,48 @@ __device__ __forceinline__ bf16x8 lds_frag(const uint8_t* lds, int row, int chun
   return __builtin_bit_cast(bf16x8, v);
 }
 
-__device__ __forceinline__ void mma_step(const uint8_t* As, const uint8_t* Bs, int wm, int wn,
-                                         int lane, floatx16 (&acc)[4][4]) {
+// The 4 A and 4 B fragments of one 16-deep MFMA sub-step (ks = 0..3 of a
+// 64-deep stage): lane l reads tile row 32 i + l % 32 (plus the wave's
+// offset), reduction chunk 2 ks + l / 32.
+struct Frags {
+  bf16x8 a[4];
+  bf16x8 b[4];
+};
+
+__device__ __forceinline__ void read_frags(const uint8_t* As, const uint8_t* Bs, int wm, int wn,
+                                           int lane, int ks, Frags& f) {
   const int lrow = lane & 31;
-  const int lhalf = lane >> 5;
+  const int chunk = 2 * ks + (lane >> 5);
 #pragma unroll
-  for (int ks = 0; ks < BK / 16; ++ks) {
-    bf16x8 a[4], b[4];
+  for (int i = 0; i < 4; ++i) f.a[i] = lds_frag(As, 128 * wm + 32 * i + lrow, chunk);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = lds_frag(As, 128 * wm + 32 * i + lrow, 2 * ks + lhalf);
+  for (int j = 0; j < 4; ++j) f.b[j] = lds_frag(Bs, 128 * wn + 32 * j + lrow, chunk);
+}
+
+// Fragment q of a sub-step: q < 4 is A fragment q, else B fragment q - 4.
+__device__ __forceinline__ void read_frag(const uint8_t* As, const uint8_t* Bs, int wm, int wn,
+                                          int lane, int ks, int q, Frags& f) {
+  const int lrow = lane & 31;
+  const int chunk = 2 * ks + (lane >> 5);
+  if (q < 4) f.a[q] = lds_frag(As, 128 * wm + 32 * q + lrow, chunk);
+  else f.b[q - 4] = lds_frag(Bs, 128 * wn + 32 * (q - 4) + lrow, chunk);
+}
+
+// LDS-only barrier: this wave's LDS operations are complete, then all waves
+// meet.  (Outstanding global loads stay in flight.)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 16 MFMAs of one sub-step.  The B fragment is the MFMA's first operand, so
+// each 32 x 32 result block is C^T and a lane ends up holding 4 consecutive
+// output columns of one output row (see store_tile).
+__device__ __forceinline__ void mfma_block(const Frags& f, floatx16 (&acc)[4][4]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = lds_frag(Bs, 128 * wn + 32 * j + lrow, 2 * ks + lhalf);
-    // B fragment as the MFMA's first operand: the 32 x 32 result block is
-    // C^T, so each lane ends up holding 4 consecutive output columns of one
-    // output row (see store_tile).
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
-  }
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
 // ---- epilogue --------------------------------------------------------------------
@@ -465,26 +563,82 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     const int red = A.red;
     const int nk = (red + BK - 1) / BK;
     if (nk > 0) {
+      // Software pipeline, one LDS barrier per 64-deep stage kt (LDS buffer
+      // cur = kt & 1).  On entry to stage kt: LDS[cur] holds stage kt,
+      // registers ra/rb hold stage kt+1 (loaded during stage kt-1) and
+      // fragment set f[0] holds sub-step 0 of stage kt.  The 64 MFMAs of the
+      // stage are issued in order; beside MFMA m the wave issues:
+      //   m  0..7  : read sub-step 1 fragment m -> f[1]; write A chunk m of stage kt+1
+      //   m  8..15 : write B chunk m-8 of stage kt+1; load A chunk m-8 of stage kt+2
+      //   m 16..23 : read sub-step 2 fragment -> f[0]; load B chunk of stage kt+2
+      //   m 32..39 : read sub-step 3 fragment -> f[1]
+      //   m 47     : LDS barrier (stage kt+1 is written, stage kt no longer read)
+      //   m 48..55 : read sub-step 0 of stage kt+1 (LDS[cur^1]) -> f[0]
+      // Scheduling barriers keep the compiler from regrouping these.  Loads
+      // past the reduction end read zeros without touching memory; what they
+      // put in LDS is never read for this tile.
       u32x4 ra[8], rb[8];
-      load_op<A_STRIDED>(A, 0, tid, ra);
-      load_op<B_STRIDED>(B, 0, tid, rb);
-      store_op<A_STRIDED>(As(0), tid, ra);
-      store_op<B_STRIDED>(Bs(0), tid, rb);
-      __syncthreads();
+      {
+        const LoadCtx ca = load_ctx<A_STRIDED>(A, 0, tid);
+        const LoadCtx cb = load_ctx<B_STRIDED>(B, 0, tid);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ra[j] = load_chunk(ca, j);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rb[j] = load_chunk(cb, j);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) store_chunk<A_STRIDED>(As(0), tid, ra, j);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) store_chunk<B_STRIDED>(Bs(0), tid, rb, j);
+        const LoadCtx ca1 = load_ctx<A_STRIDED>(A, BK, tid);
+        const LoadCtx cb1 = load_ctx<B_STRIDED>(B, BK, tid);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) ra[j] = load_chunk(ca1, j);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rb[j] = load_chunk(cb1, j);
+      }
+      lds_barrier();
+      Frags f[2];
+      read_frags(As(0), Bs(0), wm, wn, lane, 0, f[0]);
       for (int kt = 0; kt < nk; ++kt) {
         const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-          load_op<A_STRIDED>(A, (kt + 1) * BK, tid, ra);
-          load_op<B_STRIDED>(B, (kt + 1) * BK, tid, rb);
+        const uint8_t* Ac = As(cur);
+        const uint8_t* Bc = Bs(cur);
+        uint8_t* An = As(cur ^ 1);
+        uint8_t* Bn = Bs(cur ^ 1);
+        const LoadCtx ca = load_ctx<A_STRIDED>(A, (kt + 2) * BK, tid);
+        const LoadCtx cb = load_ctx<B_STRIDED>(B, (kt + 2) * BK, tid);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < 64; ++m) {
+          const int ks = m >> 4;
+          const int q = m & 15;
+          Frags& fc = f[ks & 1];
+          const int i = q >> 2, j = q & 3;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.b[j], fc.a[i], acc[i][j], 0, 0, 0);
+          if (ks == 0) {
+            if (q < 8) {
+              read_frag(Ac, Bc, wm, wn, lane, 1, q, f[1]);
+              store_chunk<A_STRIDED>(An, tid, ra, q);
+            } else {
+              store_chunk<B_STRIDED>(Bn, tid, rb, q - 8);
+              ra[q - 8] = load_chunk(ca, q - 8);
+            }
+          } else if (ks == 1) {
+            if (q < 8) {
+              read_frag(Ac, Bc, wm, wn, lane, 2, q, f[0]);
+              rb[q] = load_chunk(cb, q);
+            }
+          } else if (ks == 2) {
+            if (q < 8) read_frag(Ac, Bc, wm, wn, lane, 3, q, f[1]);
+            if (q == 15) lds_barrier();
+          } else {
+            if (q < 8) read_frag(An, Bn, wm, wn, lane, 0, q, f[0]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        mma_step(As(cur), Bs(cur), wm, wn, lane, acc);
-        if (more) {
-          store_op<A_STRIDED>(As(cur ^ 1), tid, ra);
-          store_op<B_STRIDED>(Bs(cur ^ 1), tid, rb);
-        }
-        __syncthreads();
       }
+      // The last stage's reads are done; the next tile's prologue rewrites LDS.
+      lds_barrier();
     }
     store_tile<OUT_F32>(cbase, ldc_bytes, out_rows, out_cols_valid, wm, wn, lane, acc);
   }
