@@ -1,7 +1,7 @@
 // gg_kernels.hip -- persistent bf16 grouped-GEMM kernels for gfx950 (CDNA4).
 //
 // One kernel template serves the four passes of the grouped GEMM (forward,
-// dgrad, wgrad and the masked forward; see include/gg.h for the operations
+// dgrad, wgrad and the masked forward; include/gg.h states the operations
 // and the passages that define them).  Each pass is the same tile engine fed
 // by a different operand description:
 //
@@ -12,24 +12,40 @@
 //   masked   active rows  x n          k           X[e] (red-contig)   W[e] (red-strided)
 //
 // "red-contig" means the reduction index is the contiguous one in memory;
-// "red-strided" means the tile's row index is.  Both land in LDS in one
-// layout -- tile row r holds its 64 reduction values contiguously (128 B),
-// the 16-byte chunk c stored at chunk position c ^ (r & 7) so that the eight
-// lanes served together by an LDS access touch eight different chunks.
-// Red-strided operands are transposed 8 x 8 in registers on their way into
-// LDS (32 byte permutes per thread per stage).
+// "red-strided" means the tile's row index is.
 //
-// Work decomposition (no host sync, no workspace): the launch has one
-// workgroup per compute unit.  Each workgroup decodes the device-side end
-// offsets (or masked_m) into LDS -- clamped ends by a prefix max, then a
-// prefix sum of per-expert tile counts -- and walks tiles t = blockIdx.x,
-// blockIdx.x + gridDim.x, ...  Ragged row tails are handled in the tile
-// itself: rows past an expert's end are clamped (forward, dgrad: their
-// results are never stored) or read as zero (wgrad, where they would enter
-// the sum); stores are predicated per row and column.  So there is no pad
-// copy and no output memset (TileOPs issue #1566, "Summary" and "Proposed
-// change"), and an expert with no rows costs nothing in forward/dgrad and
-// still writes its all-zero dW[g] in wgrad.
+// Data path (no register staging): every operand tile goes from global
+// memory straight into LDS with buffer loads in LDS mode (16 bytes per lane,
+// 1 KB per wave instruction), one 32-deep reduction stage at a time, through
+// a ring of 4 LDS stages: the loads for stage s + 3 are issued while the
+// MFMAs consume stage s, so three stages of loads are always in flight.
+// Each operand keeps its memory layout in LDS:
+//   red-contig  : 256 tile rows x 64 bytes (32 reduction values), the
+//                 16-byte chunk c of row r at position c ^ ((r / 4) mod 4);
+//                 MFMA fragments come from ds_read_b128.
+//   red-strided : 4 blocks of 64 tile rows; in a block, reduction row q holds
+//                 the block's 64 values (128 bytes), chunk c of reduction row
+//                 q at position c ^ (4 ((q / 2) mod 2)); fragments come from
+//                 the transposing LDS read (ds_read_b64_tr_b16), two per
+//                 fragment.  Within a group of 16 lanes it hands lane j
+//                 element j mod 4 of source lane 4 e + j / 4 as its element e,
+//                 so source lanes pointing at 4 values of 4 consecutive
+//                 reduction rows deliver 4 consecutive reduction values of one
+//                 tile row to each lane -- the MFMA operand layout.
+// Both layouts make the fragment reads conflict-free on the 64-bank LDS.
+// Ragged edges cost nothing extra: each load's buffer resource ends exactly
+// at the last byte the tile may read, and out-of-range loads write zeros into
+// LDS, so rows past an expert's end and reduction rows past its length are
+// zero (no pad copy; TileOPs issue #1566, "Summary" and "Proposed change").
+//
+// Work decomposition (no host sync, no workspace): one workgroup per compute
+// unit.  Each workgroup decodes the device-side end offsets (or masked_m)
+// into LDS -- clamped ends by a prefix max, then a prefix sum of per-expert
+// tile counts -- and walks tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...
+// Stores are predicated by the buffer range check and per column group, so
+// rows that belong to no expert are never written and there is no output
+// memset; an expert with no rows costs nothing in forward/dgrad and still
+// writes its all-zero dW[g] in wgrad.
 //
 // MFMA: v_mfma_f32_32x32x16_bf16, fp32 accumulation.  A workgroup is 4 waves
 // (2 x 2) over a 256 x 256 output tile; each wave owns 128 x 128, i.e. 4 x 4
@@ -37,19 +53,26 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "gg_internal.h"
 
 namespace gg {
 
 constexpr int BM = 256;          // tile rows
 constexpr int BN = 256;          // tile cols
-constexpr int BK = 64;           // reduction step
+constexpr int BK = 32;           // reduction stage
 constexpr int NT = 256;          // threads per workgroup (4 waves)
-constexpr int STAGE_BYTES = 256 * BK * 2;   // one operand tile: 32 KB
+constexpr int NSTAGE = 4;        // LDS stages (loads run NSTAGE - 1 stages ahead)
+constexpr int OP_BYTES = 256 * BK * 2;      // one operand's stage tile: 16 KB
+constexpr int STAGE_BYTES = 2 * OP_BYTES;   // A then B: 32 KB
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 enum Mode { FWD = 0, DGRAD = 1, WGRAD = 2, MASKED = 3 };
 
@@ -64,14 +87,9 @@ struct Params {
   int32_t num_groups;
 };
 
-// One operand tile: element (row r, reduction index q) of the tile lives at
-// byte origin + 2 (r * ld + q) (red-contig) or origin + 2 (q * ld + r)
-// (red-strided).  Loads go through a buffer resource rebuilt per reduction
-// step whose record count ends exactly at the last byte the tile may read,
-// so rows past an expert's end (and reduction rows past its length) read as
-// zero from the hardware range check, and nothing past the operand is ever
-// touched.  All offsets are in the 32-bit VGPR offset (the scalar offset is
-// kept 0: the range check covers the VGPR and instruction offsets).
+// One operand tile: element (tile row r, reduction index q) of the tile
+// lives at byte origin + 2 (r * ld + q) (red-contig) or origin + 2 (q * ld +
+// r) (red-strided).
 struct Operand {
   const uint8_t* origin;
   uint32_t ld_bytes;  // 2 * ld
@@ -91,203 +109,160 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // scalar registers, so buffer resources built from them stay scalar.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
-__device__ __forceinline__ uint32_t perm_b32(uint32_t hi, uint32_t lo, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi, lo, sel);
+// Opaque copies: the compiler must recompute whatever depends on them where
+// they are used, instead of hoisting per-lane constants out of the tile loop
+// (which would keep dozens of them live across the main loop).
+__device__ __forceinline__ uint32_t opaque_v(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ uint32_t opaque_s(uint32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
 }
 
-// ---- global -> registers ---------------------------------------------------
-
-// Red-contig: thread owns chunk c = tid & 7 (reduction values 8c..8c+7) of
-// tile rows tid/8 + 32 j, j = 0..7.  Rows past the valid ones fall outside
-// the record range (zero); a chunk past the reduction end is sent out of
-// range explicitly (it would otherwise read the next row).
-__device__ __forceinline__ void load_contig(const Operand& op, int q0, int tid, u32x4 (&r)[8]) {
-  const int c = tid & 7;
-  // Past the reduction end the record count is 0 (every load reads zero and
-  // touches no memory).
-  const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - 2u * (uint32_t)q0 : 0u;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(op.origin + 2 * (int64_t)q0, nrec);
-  uint32_t voff = (uint32_t)(tid >> 3) * op.ld_bytes + 16u * (uint32_t)c;
-  if (q0 + 8 * c >= op.red) voff = kOutOfRange;
-  const uint32_t step = 32u * op.ld_bytes;
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + j * step, 0, 0));
+// Stage barrier: this wave's global->LDS loads and LDS operations are
+// complete, then all waves meet.  The wait is the builtin (so the compiler
+// knows nothing is outstanding afterwards); the barrier is an asm statement
+// with a memory clobber so no LDS access moves across it.
+constexpr int kWaitVmLgkm0 = 0x0070;   // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(0)
+__device__ __forceinline__ void stage_barrier() {
+  __builtin_amdgcn_s_waitcnt(kWaitVmLgkm0);
+  asm volatile("s_barrier" ::: "memory");
 }
 
-// Red-strided: thread owns the 8 (reduction) x 8 (row) block with reduction
-// block rb = tid & 7 and row block cb = tid >> 3.  Reduction rows past the
-// valid length fall outside the record range (zero).  Tile rows past the
-// memory row end read neighbouring data or zero; they only feed output rows
-// or columns that are never stored.
-__device__ __forceinline__ void load_strided(const Operand& op, int q0, int tid, u32x4 (&r)[8]) {
-  const int rb = tid & 7;
-  const int cb = tid >> 3;
-  const int left = op.red - q0;
-  const uint32_t nrec = left > 0 ? (uint32_t)(left - 1) * op.ld_bytes + op.row_tail : 0u;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(op.origin + (int64_t)q0 * op.ld_bytes, nrec);
-  const uint32_t voff = (uint32_t)(8 * rb) * op.ld_bytes + 16u * (uint32_t)cb;
-#pragma unroll
-  for (int j = 0; j < 8; ++j)
-    r[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + j * op.ld_bytes, 0, 0));
-}
+// ---- global -> LDS, one stage of one operand ------------------------------------
 
-// ---- registers -> LDS --------------------------------------------------------
-
-// LDS tile layout: row r at r * 128 bytes, its 16-byte chunk c at chunk
-// position c ^ ((r / 2) mod 8).  The LDS serves 16 lanes (256 bytes) of a
-// 16-byte access per cycle; 16 consecutive rows at one logical chunk then
-// land on 16 distinct 16-byte bank groups (row parity picks the 128-byte
-// half, (r / 2) mod 8 the chunk), so fragment reads are conflict-free, and
-// so are row-pair writes of 8 chunks each.
-__device__ __forceinline__ uint32_t lds_off(int row, int chunk) {
-  return (uint32_t)(row * (BK * 2) + ((chunk ^ ((row >> 1) & 7)) << 4));
-}
-
-__device__ __forceinline__ void store_contig(uint8_t* lds, int tid, const u32x4 (&r)[8]) {
-  const int c = tid & 7;
-  const int row0 = tid >> 3;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = row0 + 32 * j;
-    *reinterpret_cast<u32x4*>(lds + lds_off(row, c)) = r[j];
-  }
-}
-
-// Transpose the 8 x 8 block (r[j] holds reduction index j for 8 consecutive
-// rows) so that each of the 8 rows gets its 8 reduction values in one chunk.
-// Lanes with an odd row block visit the rows in the order 1, 0, 3, 2, ...:
-// each write instruction then covers a row pair of opposite parity across
-// 16 lanes, which the LDS serves without bank conflicts.
-__device__ __forceinline__ void store_strided(uint8_t* lds, int tid, const u32x4 (&r)[8]) {
-  const int rb = tid & 7;
-  const int flip = (tid >> 3) & 1;
-  const int row0 = 8 * (tid >> 3);
-  // byte selectors: low halves (even row) or high halves (odd row)
-  const uint32_t sel_even = flip ? 0x07060302u : 0x05040100u;
-  const uint32_t sel_odd = flip ? 0x05040100u : 0x07060302u;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    const int w = s >> 1;                                   // dword holding rows 2w, 2w + 1
-    const uint32_t sel = (s & 1) ? sel_odd : sel_even;
-    const int qr = s ^ flip;
-    u32x4 o;
-    o[0] = perm_b32(r[1][w], r[0][w], sel);
-    o[1] = perm_b32(r[3][w], r[2][w], sel);
-    o[2] = perm_b32(r[5][w], r[4][w], sel);
-    o[3] = perm_b32(r[7][w], r[6][w], sel);
-    *reinterpret_cast<u32x4*>(lds + lds_off(row0 + qr, rb)) = o;
-  }
-}
-
-template <bool STRIDED>
-__device__ __forceinline__ void load_op(const Operand& op, int q0, int tid, u32x4 (&r)[8]) {
-  if constexpr (STRIDED) load_strided(op, q0, tid, r); else load_contig(op, q0, tid, r);
-}
-
-template <bool STRIDED>
-__device__ __forceinline__ void store_op(uint8_t* lds, int tid, const u32x4 (&r)[8]) {
-  if constexpr (STRIDED) store_strided(lds, tid, r); else store_contig(lds, tid, r);
-}
-
-// ---- per-chunk forms of the above (for the interleaved main loop) --------------
-
-// Buffer resource and lane offset of one operand for one stage; chunk j is
-// at voff + j * step.
-struct LoadCtx {
+// The 4 loads a thread issues for one operand stage.  Load j of wave w
+// fills LDS bytes [1024 (4 w + j), +1024) of the operand's stage tile; lane
+// i writes 16 bytes at 16 i.  Offsets beyond the record count read as zero.
+struct DmaCtx {
   __amdgpu_buffer_rsrc_t rs;
-  uint32_t voff;
-  uint32_t step;
+  uint32_t voff;      // lane offset of load 0
+  uint32_t step;      // extra byte offset per load (scalar offset)
 };
 
 template <bool STRIDED>
-__device__ __forceinline__ LoadCtx load_ctx(const Operand& op, int q0, int tid) {
-  LoadCtx c;
+__device__ __forceinline__ DmaCtx dma_ctx(const Operand& op, int q0, int tid) {
+  DmaCtx c;
+  // lane terms recomputed per stage (a few VALU ops) rather than hoisted and
+  // kept live across the unrolled main loop
+  const int lane = (int)opaque_v((uint32_t)(tid & 63));
+  const int w = tid >> 6;
   if constexpr (STRIDED) {
-    const int rb = tid & 7;
-    const int cb = tid >> 3;
+    // wave w fills block w (tile rows 64 w ..): load j covers reduction rows
+    // 8 j .. 8 j + 7; lane i: row 8 j + i / 8, chunk position i mod 8,
+    // logical chunk (i mod 8) ^ 4 ((row / 2) mod 2) = (i mod 8) ^ 4 ((i / 16) mod 2).
     const int left = op.red - q0;
     const uint32_t nrec = left > 0 ? (uint32_t)(left - 1) * op.ld_bytes + op.row_tail : 0u;
     c.rs = make_rsrc(op.origin + (int64_t)q0 * op.ld_bytes, nrec);
-    c.voff = (uint32_t)(8 * rb) * op.ld_bytes + 16u * (uint32_t)cb;
-    c.step = op.ld_bytes;
+    const int chunk = (lane & 7) ^ (4 * ((lane >> 4) & 1));
+    c.voff = (uint32_t)(lane >> 3) * op.ld_bytes + (uint32_t)(128 * w + 16 * chunk);
+    c.step = 8u * op.ld_bytes;
   } else {
-    const int ch = tid & 7;
+    // load j of wave w covers tile rows 64 w + 16 j .. + 15; lane i: row
+    // 64 w + 16 j + i / 4, chunk position i mod 4, logical chunk
+    // (i mod 4) ^ ((row / 4) mod 4) = (i mod 4) ^ ((i / 16) mod 4).
     const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - 2u * (uint32_t)q0 : 0u;
     c.rs = make_rsrc(op.origin + 2 * (int64_t)q0, nrec);
-    c.voff = (uint32_t)(tid >> 3) * op.ld_bytes + 16u * (uint32_t)ch;
-    if (q0 + 8 * ch >= op.red) c.voff = kOutOfRange;
-    c.step = 32u * op.ld_bytes;
+    const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+    uint32_t v = (uint32_t)(64 * w + (lane >> 2)) * op.ld_bytes + 16u * (uint32_t)chunk;
+    if (q0 + 8 * chunk >= op.red) v = kOutOfRange;   // past the reduction end: zero
+    c.voff = v;
+    c.step = 16u * op.ld_bytes;
   }
   return c;
 }
 
-__device__ __forceinline__ u32x4 load_chunk(const LoadCtx& c, int j) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(c.rs, c.voff + j * c.step, 0, 0));
+__device__ __forceinline__ void dma_load(const DmaCtx& c, uint8_t* lds_op, int wave, int j) {
+  // the wave's first 1 KB block of this tile, recomputed per use
+  const uint32_t wbase = opaque_s((uint32_t)(4 * wave) * 1024u);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, LDS_PTR(lds_op + wbase + 1024 * j), 16, c.voff, j * c.step, 0, 0);
 }
 
-// Write chunk j of the staged registers (red-contig: row tid/8 + 32 j;
-// red-strided: the j-th of the thread's 8 rows, transposed).
-template <bool STRIDED>
-__device__ __forceinline__ void store_chunk(uint8_t* lds, int tid, const u32x4 (&r)[8], int j) {
-  if constexpr (STRIDED) {
-    const int rb = tid & 7;
-    const int flip = (tid >> 3) & 1;
-    const int row0 = 8 * (tid >> 3);
-    const uint32_t sel_even = flip ? 0x07060302u : 0x05040100u;
-    const uint32_t sel_odd = flip ? 0x05040100u : 0x07060302u;
-    const int w = j >> 1;
-    const uint32_t sel = (j & 1) ? sel_odd : sel_even;
-    u32x4 o;
-    o[0] = perm_b32(r[1][w], r[0][w], sel);
-    o[1] = perm_b32(r[3][w], r[2][w], sel);
-    o[2] = perm_b32(r[5][w], r[4][w], sel);
-    o[3] = perm_b32(r[7][w], r[6][w], sel);
-    *reinterpret_cast<u32x4*>(lds + lds_off(row0 + (j ^ flip), rb)) = o;
-  } else {
-    const int row = (tid >> 3) + 32 * j;
-    *reinterpret_cast<u32x4*>(lds + lds_off(row, tid & 7)) = r[j];
-  }
-}
+// ---- LDS -> MFMA fragments ------------------------------------------------------
 
-// ---- MFMA over one staged reduction step ---------------------------------------
-
-__device__ __forceinline__ bf16x8 lds_frag(const uint8_t* lds, int row, int chunk) {
-  u32x4 v = *reinterpret_cast<const u32x4*>(lds + lds_off(row, chunk));
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-// The 4 A and 4 B fragments of one 16-deep MFMA sub-step (ks = 0..3 of a
-// 64-deep stage): lane l reads tile row 32 i + l % 32 (plus the wave's
-// offset), reduction chunk 2 ks + l / 32.
+// A fragment: 8 consecutive reduction values (sub-step ks, half l / 32) of
+// tile row 32 i + l % 32 of the wave's 128-row slice.
 struct Frags {
   bf16x8 a[4];
   bf16x8 b[4];
 };
 
-__device__ __forceinline__ void read_frags(const uint8_t* As, const uint8_t* Bs, int wm, int wn,
-                                           int lane, int ks, Frags& f) {
-  const int lrow = lane & 31;
-  const int chunk = 2 * ks + (lane >> 5);
+// Lane-dependent part of the fragment addresses of one operand (its wave
+// slice index wp = wm or wn).  Red-contig: the byte offset of chunk 2 ks +
+// l / 32 of row 128 wp + l % 32, for ks = 0, 1 (the XOR swizzle mixes ks
+// with the lane bits).  Red-strided: the offset of the 4-value group a
+// source lane points at, for fragment parity i mod 2 (sub-step, fragment
+// pair and read half are added as immediates).
+struct FragAddr {
+  uint32_t o[2];
+};
+
+template <bool STRIDED>
+__device__ __forceinline__ FragAddr frag_addr(int wp, int lane) {
+  FragAddr f;
+  if constexpr (STRIDED) {
+    const int g = lane >> 4, s = lane & 15;
+    const int qrow = 8 * (g >> 1) + (s >> 2);                     // reduction row within the sub-step
+    const int sw = 4 * ((s >> 3) & 1);                            // (qrow / 2) mod 2 == (s / 8) mod 2
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = lds_frag(As, 128 * wm + 32 * i + lrow, chunk);
+    for (int par = 0; par < 2; ++par) {
+      const int chunk = (4 * par + 2 * (g & 1) + ((s & 3) >> 1)) ^ sw;
+      f.o[par] = (uint32_t)(2 * wp * 4096 + qrow * 128 + 16 * chunk + 8 * (s & 1));
+    }
+  } else {
+    const int row = 128 * wp + (lane & 31);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = lds_frag(Bs, 128 * wn + 32 * j + lrow, chunk);
+    for (int ks = 0; ks < 2; ++ks) {
+      const int chunk = (2 * ks + (lane >> 5)) ^ ((row >> 2) & 3);
+      f.o[ks] = (uint32_t)(row * 64 + 16 * chunk);
+    }
+  }
+  return f;
 }
 
-// Fragment q of a sub-step: q < 4 is A fragment q, else B fragment q - 4.
-__device__ __forceinline__ void read_frag(const uint8_t* As, const uint8_t* Bs, int wm, int wn,
-                                          int lane, int ks, int q, Frags& f) {
-  const int lrow = lane & 31;
-  const int chunk = 2 * ks + (lane >> 5);
-  if (q < 4) f.a[q] = lds_frag(As, 128 * wm + 32 * q + lrow, chunk);
-  else f.b[q - 4] = lds_frag(Bs, 128 * wn + 32 * (q - 4) + lrow, chunk);
+__device__ __forceinline__ bf16x8 read_tr_pair(const uint8_t* lds, uint32_t off) {
+  typedef __attribute__((address_space(3))) shortx4 lds_s4;
+  const __attribute__((address_space(3))) uint8_t* base = (const __attribute__((address_space(3))) uint8_t*)lds;
+  shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(base + off));
+  shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)(base + off + 4 * 128));
+  typedef short shortx8 __attribute__((ext_vector_type(8)));
+  shortx8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
 }
 
-// LDS-only barrier: this wave's LDS operations are complete, then all waves
-// meet.  (Outstanding global loads stay in flight.)
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+// Fragment i of sub-step ks of one operand.
+template <bool STRIDED>
+__device__ __forceinline__ bf16x8 read_frag(const uint8_t* lds, const FragAddr& fa, int ks, int i) {
+  if constexpr (STRIDED) {
+    // block 2 wp + i / 2, reduction rows 16 ks + ..., fragment parity i mod 2
+    return read_tr_pair(lds, fa.o[i & 1] + (uint32_t)((i >> 1) * 4096 + ks * 16 * 128));
+  } else {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lds + fa.o[ks] + (uint32_t)(i * 32 * 64)));
+  }
+}
+
+template <bool A_STRIDED, bool B_STRIDED>
+__device__ __forceinline__ void read_stage_frags(const uint8_t* As, const uint8_t* Bs, const FragAddr& faa,
+                                                 const FragAddr& fab, int ks, Frags& f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f.a[i] = read_frag<A_STRIDED>(As, faa, ks, i);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f.b[j] = read_frag<B_STRIDED>(Bs, fab, ks, j);
+}
+
+// Phase fence for the MFMA stream: an empty statement that claims to read and
+// rewrite every accumulator.  MFMAs have no side effects, so without it the
+// compiler is free to move them across the stage barrier and the fragment
+// reads (it did, and then copied fragment registers around the loop).  With
+// it, MFMAs issued before the fence stay before it and MFMAs after it stay
+// after; it emits no instruction.
+__device__ __forceinline__ void mfma_fence(floatx16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]) :: "memory");
 }
 
 // 16 MFMAs of one sub-step.  The B fragment is the MFMA's first operand, so
@@ -299,6 +274,102 @@ __device__ __forceinline__ void mfma_block(const Frags& f, floatx16 (&acc)[4][4]
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
+}
+
+// ---- the main loop ---------------------------------------------------------------
+
+// Issue the 8 global->LDS loads (4 per operand) of stage `st` into stage
+// buffer `buf` (A tile at +0, B tile at +OP_BYTES).
+template <bool A_STRIDED, bool B_STRIDED>
+__device__ __forceinline__ void load_stage(const Operand& A, const Operand& B, int st, uint8_t* buf,
+                                           int tid, int wave) {
+  const DmaCtx ca = dma_ctx<A_STRIDED>(A, st * BK, tid);
+  const DmaCtx cb = dma_ctx<B_STRIDED>(B, st * BK, tid);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma_load(ca, buf, wave, j);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) dma_load(cb, buf + OP_BYTES, wave, j);
+}
+
+// Wait until at most n global->LDS loads of this wave are in flight, then
+// barrier.  (The LDS operations of this wave are complete too.)
+template <int N>
+__device__ __forceinline__ void stage_barrier_vm() {
+  // s_waitcnt vmcnt(N) expcnt(7) lgkmcnt(0); vmcnt is 6 bits (low 4 at
+  // [3:0], high 2 at [15:14])
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// The reduction loop of one output tile.  Stage kt (BK = 32 reduction
+// values of both operands) lives in LDS buffer kt mod 4; the loads of stage
+// kt + 4 are issued as soon as stage kt is consumed, so three stages (96 KB)
+// are in flight while one is read.  Per stage, in this order:
+//   MFMA sub-step 0 (fragments f0, read earlier)
+//   wait for stage kt+1, barrier
+//   load stage kt+4 into the buffer of stage kt
+//   read sub-step 0 of stage kt+1 -> f0, interleaved with MFMA sub-step 1 (f1)
+//   read sub-step 1 of stage kt+1 -> f1
+// The four buffers are distinct restrict-qualified pointers and the loop is
+// unrolled by four so that every LDS access names its buffer: the compiler
+// then knows a fragment read never overlaps a load in flight to another
+// buffer and does not make the read wait for it.  Loads past the reduction
+// end write zeros (never read for this tile); the caller waits for them
+// before the LDS is reused.
+template <bool A_STRIDED, bool B_STRIDED>
+__device__ __attribute__((always_inline)) inline void mainloop(
+    uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
+    uint8_t* __restrict__ s3, const uint8_t* __restrict__ a_origin,
+    const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid, int wave,
+    const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[4][4]) {
+  // The global operands are only read here; deriving every load from these
+  // restrict-qualified pointers (and every LDS access from s0..s3) lets each
+  // global->LDS load carry the identity of the one stage buffer it writes.
+  A.origin = a_origin;
+  B.origin = b_origin;
+  const int nk = (A.red + BK - 1) / BK;
+  if (nk <= 0) return;
+  Frags f0, f1;
+  load_stage<A_STRIDED, B_STRIDED>(A, B, 0, s0, tid, wave);
+  load_stage<A_STRIDED, B_STRIDED>(A, B, 1, s1, tid, wave);
+  load_stage<A_STRIDED, B_STRIDED>(A, B, 2, s2, tid, wave);
+  load_stage<A_STRIDED, B_STRIDED>(A, B, 3, s3, tid, wave);
+  stage_barrier_vm<24>();                       // stage 0 landed
+  read_stage_frags<A_STRIDED, B_STRIDED>(s0, s0 + OP_BYTES, faa, fab, 0, f0);
+  read_stage_frags<A_STRIDED, B_STRIDED>(s0, s0 + OP_BYTES, faa, fab, 1, f1);
+
+// One stage (buffers named directly, so every access is based on one of the
+// restrict-qualified parameters).
+#define GG_STAGE(BC, BN, KT)                                                              \
+  {                                                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    mfma_block(f0, acc);                                                                  \
+    mfma_fence(acc);                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    stage_barrier_vm<16>(); /* stage KT+1 landed; stage KT consumed */                    \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    load_stage<A_STRIDED, B_STRIDED>(A, B, (KT) + 4, BC, tid, wave);                      \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                      \
+      const int i = q >> 2, j = q & 3;                                                    \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0); \
+      if (q < 4) f0.a[q] = read_frag<A_STRIDED>(BN, faa, 0, q);                           \
+      else if (q < 8) f0.b[q - 4] = read_frag<B_STRIDED>((BN) + OP_BYTES, fab, 0, q - 4); \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+    }                                                                                     \
+    mfma_fence(acc);                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    read_stage_frags<A_STRIDED, B_STRIDED>(BN, (BN) + OP_BYTES, faa, fab, 1, f1);         \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+  }
+
+  for (int kt = 0; kt < nk; kt += 4) {
+    GG_STAGE(s0, s1, kt)
+    if (kt + 1 < nk) GG_STAGE(s1, s2, kt + 1)
+    if (kt + 2 < nk) GG_STAGE(s2, s3, kt + 2)
+    if (kt + 3 < nk) GG_STAGE(s3, s0, kt + 3)
+  }
+#undef GG_STAGE
 }
 
 // ---- epilogue --------------------------------------------------------------------
@@ -328,19 +399,19 @@ __device__ __forceinline__ void store_tile(uint8_t* cbase, uint32_t ldc_bytes, i
   constexpr uint32_t esz = OUT_F32 ? 4 : 2;
   const uint32_t nrec = (uint32_t)(rows - 1) * ldc_bytes + (uint32_t)cols * esz;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(cbase, nrec);
-  const uint32_t lane_off = (uint32_t)(128 * wm + (lane & 31)) * ldc_bytes +
-                            (uint32_t)(128 * wn + 4 * (lane >> 5)) * esz;
+  const uint32_t lane_off = opaque_v((uint32_t)(128 * wm + (lane & 31)) * ldc_bytes +
+                                     (uint32_t)(128 * wn + 4 * (lane >> 5)) * esz);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t voff = lane_off + (uint32_t)(32 * i) * ldc_bytes;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const floatx16& a = acc[i][j];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int col8 = 128 * wn + 32 * j + 8 * rr;      // first of 8 columns, wave-uniform
         if (col8 >= cols) continue;
         const uint32_t imm = (uint32_t)(32 * j + 8 * rr) * esz;
-        const floatx16& a = acc[i][j];
         if constexpr (OUT_F32) {
           // Built as a float vector and bit-cast whole: a u32x4 built from
           // per-element bit casts of accumulator values was miscompiled by
@@ -353,6 +424,54 @@ __device__ __forceinline__ void store_tile(uint8_t* cbase, uint32_t ldc_bytes, i
         }
       }
     }
+  }
+}
+
+// bf16 output through LDS.  Packing to bf16 needs the values in ordinary
+// registers; moving all 256 accumulators there at once overflows them, so
+// each wave instead writes one 32 x 128 fp32 slab (block row i) from its
+// accumulator registers into its own LDS region (rows padded by 16 bytes so
+// the 16 rows a write touches fall on distinct banks), reads back 8
+// consecutive values per lane, packs them and stores 16 bytes per lane --
+// 16 lanes cover 256 contiguous bytes of an output row.  Row and column
+// predication as in store_tile.  `slab` is this wave's LDS region (>= 32 *
+// 528 bytes), free for the epilogue.
+constexpr int kSlabPitch = 128 * 4 + 16;
+
+__device__ __forceinline__ void store_tile_bf16_lds(uint8_t* cbase, uint32_t ldc_bytes, int rows,
+                                                    int cols, int wm, int wn, int lane,
+                                                    const floatx16 (&acc)[4][4], uint8_t* slab) {
+  const uint32_t nrec = (uint32_t)(rows - 1) * ldc_bytes + (uint32_t)cols * 2u;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(cbase, nrec);
+  const int wrow = lane & 31;                 // slab row this lane writes
+  const int wcol = 4 * (lane >> 5);           // first of its 4 columns in each 8-column group
+  const int rcol8 = 8 * (lane & 15);          // read: 8 consecutive columns ...
+  const int rrow = lane >> 4;                 // ... of slab rows rrow + 4 q
+  const int gcol = 128 * wn + rcol8;
+  const bool col_ok = gcol < cols;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        floatx4 v = {acc[i][j][4 * rr + 0], acc[i][j][4 * rr + 1], acc[i][j][4 * rr + 2], acc[i][j][4 * rr + 3]};
+        *reinterpret_cast<floatx4*>(slab + wrow * kSlabPitch + 4 * (32 * j + 8 * rr + wcol)) = v;
+      }
+    // LDS operations of one wave complete in order: the reads see the writes.
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int r = rrow + 4 * q;
+      const floatx4 lo = *reinterpret_cast<const floatx4*>(slab + r * kSlabPitch + 4 * rcol8);
+      const floatx4 hi = *reinterpret_cast<const floatx4*>(slab + r * kSlabPitch + 4 * rcol8 + 16);
+      u32x4 o = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                 pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
+      uint32_t voff = (uint32_t)(128 * wm + 32 * i + r) * ldc_bytes + (uint32_t)gcol * 2u;
+      if (!col_ok) voff = kOutOfRange;
+      __builtin_amdgcn_raw_buffer_store_b128(o, rs, voff, 0, 0);
+    }
+    // the next block row rewrites the slab: wait for this row's reads
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
   }
 }
 
@@ -438,6 +557,43 @@ __device__ __forceinline__ int find_group(const int32_t* s_pref, int E, int t) {
   return lo;
 }
 
+// ---- tile order -------------------------------------------------------------------
+
+// Workgroups are dealt to the 8 XCDs (each with its own L2) round-robin:
+// workgroup b runs on XCD b mod 8.  Within each round of gridDim.x tiles,
+// workgroup b takes position (b mod 8) (G / 8) + b / 8, so each XCD works on
+// a contiguous run of the order below.  The last, partial round keeps the
+// plain order (any bijection works there).
+__device__ __forceinline__ int64_t xcd_tile(int64_t t, int64_t total) {
+  const int G = gridDim.x;
+  const int b = blockIdx.x;
+  const int64_t round0 = t - b;
+  if ((G & 7) != 0 || round0 + G > total) return t;
+  return round0 + (int64_t)(b & 7) * (G >> 3) + (b >> 3);
+}
+
+// Order of an rows x cols grid of tiles: column strips of (up to) 8 tiles,
+// each strip walked row by row, so a run of 32 consecutive tiles is a block
+// of 4 tile rows x 8 tile columns (4 A panels and 8 B panels shared within
+// one XCD).  Returns (row, col) of linear index u.
+constexpr int kStrip = 8;
+__device__ __forceinline__ void strip_order(int64_t u, int64_t rows, int cols, int64_t& r, int& c) {
+  const int bw = cols < kStrip ? cols : kStrip;
+  const int full = cols / bw;                    // strips of width bw
+  const int64_t per = rows * bw;
+  if (u < (int64_t)full * per) {
+    const int s = (int)(u / per);
+    const int64_t w = u - (int64_t)s * per;
+    r = w / bw;
+    c = s * bw + (int)(w - r * bw);
+  } else {
+    const int rem = cols - full * bw;            // last, narrower strip
+    const int64_t w = u - (int64_t)full * per;
+    r = w / rem;
+    c = full * bw + (int)(w - r * rem);
+  }
+}
+
 // ---- the kernel ------------------------------------------------------------------
 
 template <int MODE, bool OUT_F32>
@@ -445,7 +601,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   constexpr bool A_STRIDED = (MODE == WGRAD);
   constexpr bool B_STRIDED = (MODE != DGRAD);
 
-  __shared__ __attribute__((aligned(16))) uint8_t smem[4 * STAGE_BYTES];
+  // LDS: NSTAGE stage buffers of 32 KB (A tile, then B tile).
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE_BYTES];
   __shared__ int32_t s_start[GG_MAX_GROUPS_DEV];
   __shared__ int32_t s_end[GG_MAX_GROUPS_DEV];
   __shared__ int32_t s_pref[GG_MAX_GROUPS_DEV + 1];
@@ -472,14 +629,13 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     total = (int64_t)uniform(s_pref[E]) * col_tiles;
   }
 
-  // LDS: [A stage 0][A stage 1][B stage 0][B stage 1].
-  auto As = [&](int st) { return smem + st * STAGE_BYTES; };
-  auto Bs = [&](int st) { return smem + (2 + st) * STAGE_BYTES; };
 
   constexpr uint32_t esz = OUT_F32 ? 4 : 2;
   const uint8_t* pa = reinterpret_cast<const uint8_t*>(p.a);
   const uint8_t* pb = reinterpret_cast<const uint8_t*>(p.b);
   uint8_t* pc = reinterpret_cast<uint8_t*>(p.c);
+  const FragAddr faa = frag_addr<A_STRIDED>(wm, lane);
+  const FragAddr fab = frag_addr<B_STRIDED>(wn, lane);
 
   for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
     Operand A, B;
@@ -487,8 +643,19 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     uint32_t ldc_bytes;
     int out_rows, out_cols_valid;
     {
-      const int ct = (int)(t % col_tiles);
-      const int64_t rt_all = t / col_tiles;
+      const int64_t u = xcd_tile(t, total);
+      int ct;
+      int64_t rt_all;
+      if constexpr (MODE == WGRAD) {
+        // per expert: a row_tiles_w x col_tiles grid in strip order
+        const int64_t per_g = (int64_t)row_tiles_w * col_tiles;
+        const int64_t gq = u / per_g;
+        int64_t rr;
+        strip_order(u - gq * per_g, row_tiles_w, col_tiles, rr, ct);
+        rt_all = gq * row_tiles_w + rr;
+      } else {
+        strip_order(u, total / col_tiles, col_tiles, rt_all, ct);
+      }
       const int col0 = ct * BN;
       if constexpr (MODE == WGRAD) {
         const int g = (int)(rt_all / row_tiles_w);
@@ -551,7 +718,6 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
         out_cols_valid = B.rows;
       }
     }
-
     floatx16 acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -560,87 +726,22 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-    const int red = A.red;
-    const int nk = (red + BK - 1) / BK;
-    if (nk > 0) {
-      // Software pipeline, one LDS barrier per 64-deep stage kt (LDS buffer
-      // cur = kt & 1).  On entry to stage kt: LDS[cur] holds stage kt,
-      // registers ra/rb hold stage kt+1 (loaded during stage kt-1) and
-      // fragment set f[0] holds sub-step 0 of stage kt.  The 64 MFMAs of the
-      // stage are issued in order; beside MFMA m the wave issues:
-      //   m  0..7  : read sub-step 1 fragment m -> f[1]; write A chunk m of stage kt+1
-      //   m  8..15 : write B chunk m-8 of stage kt+1; load A chunk m-8 of stage kt+2
-      //   m 16..23 : read sub-step 2 fragment -> f[0]; load B chunk of stage kt+2
-      //   m 32..39 : read sub-step 3 fragment -> f[1]
-      //   m 47     : LDS barrier (stage kt+1 is written, stage kt no longer read)
-      //   m 48..55 : read sub-step 0 of stage kt+1 (LDS[cur^1]) -> f[0]
-      // Scheduling barriers keep the compiler from regrouping these.  Loads
-      // past the reduction end read zeros without touching memory; what they
-      // put in LDS is never read for this tile.
-      u32x4 ra[8], rb[8];
-      {
-        const LoadCtx ca = load_ctx<A_STRIDED>(A, 0, tid);
-        const LoadCtx cb = load_ctx<B_STRIDED>(B, 0, tid);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ra[j] = load_chunk(ca, j);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) rb[j] = load_chunk(cb, j);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) store_chunk<A_STRIDED>(As(0), tid, ra, j);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) store_chunk<B_STRIDED>(Bs(0), tid, rb, j);
-        const LoadCtx ca1 = load_ctx<A_STRIDED>(A, BK, tid);
-        const LoadCtx cb1 = load_ctx<B_STRIDED>(B, BK, tid);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) ra[j] = load_chunk(ca1, j);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) rb[j] = load_chunk(cb1, j);
-      }
-      lds_barrier();
-      Frags f[2];
-      read_frags(As(0), Bs(0), wm, wn, lane, 0, f[0]);
-      for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const uint8_t* Ac = As(cur);
-        const uint8_t* Bc = Bs(cur);
-        uint8_t* An = As(cur ^ 1);
-        uint8_t* Bn = Bs(cur ^ 1);
-        const LoadCtx ca = load_ctx<A_STRIDED>(A, (kt + 2) * BK, tid);
-        const LoadCtx cb = load_ctx<B_STRIDED>(B, (kt + 2) * BK, tid);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int m = 0; m < 64; ++m) {
-          const int ks = m >> 4;
-          const int q = m & 15;
-          Frags& fc = f[ks & 1];
-          const int i = q >> 2, j = q & 3;
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fc.b[j], fc.a[i], acc[i][j], 0, 0, 0);
-          if (ks == 0) {
-            if (q < 8) {
-              read_frag(Ac, Bc, wm, wn, lane, 1, q, f[1]);
-              store_chunk<A_STRIDED>(An, tid, ra, q);
-            } else {
-              store_chunk<B_STRIDED>(Bn, tid, rb, q - 8);
-              ra[q - 8] = load_chunk(ca, q - 8);
-            }
-          } else if (ks == 1) {
-            if (q < 8) {
-              read_frag(Ac, Bc, wm, wn, lane, 2, q, f[0]);
-              rb[q] = load_chunk(cb, q);
-            }
-          } else if (ks == 2) {
-            if (q < 8) read_frag(Ac, Bc, wm, wn, lane, 3, q, f[1]);
-            if (q == 15) lds_barrier();
-          } else {
-            if (q < 8) read_frag(An, Bn, wm, wn, lane, 0, q, f[0]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      // The last stage's reads are done; the next tile's prologue rewrites LDS.
-      lds_barrier();
+    mainloop<A_STRIDED, B_STRIDED>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
+                                   smem + 3 * STAGE_BYTES, A.origin, B.origin, A, B, tid, wave,
+                                   faa, fab, acc);
+    // loads of stages past the end may still be landing (zeros), and other
+    // waves may still read the last stage: settle before the LDS is reused
+    stage_barrier();
+    if constexpr (OUT_F32) {
+      store_tile<true>(cbase, ldc_bytes, out_rows, out_cols_valid, wm, wn, lane, acc);
+    } else {
+      // each wave stages through its own 32 KB stage buffer (all idle here)
+      uint8_t* slab = smem + wave * STAGE_BYTES;
+      store_tile_bf16_lds(cbase, ldc_bytes, out_rows, out_cols_valid, wm, wn, lane, acc, slab);
+      // the next tile's first loads overwrite these arrays
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __syncthreads();
     }
-    store_tile<OUT_F32>(cbase, ldc_bytes, out_rows, out_cols_valid, wm, wn, lane, acc);
   }
 }
 
