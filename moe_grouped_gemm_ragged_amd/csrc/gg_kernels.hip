@@ -47,9 +47,12 @@
 // memset; an expert with no rows costs nothing in forward/dgrad and still
 // writes its all-zero dW[g] in wgrad.
 //
-// MFMA: v_mfma_f32_32x32x16_bf16, fp32 accumulation.  A workgroup is 4 waves
-// (2 x 2) over a 256 x 256 output tile; each wave owns 128 x 128, i.e. 4 x 4
-// MFMA blocks of 32 x 32 (256 accumulator registers per lane).
+// MFMA: v_mfma_f32_32x32x16_bf16, fp32 accumulation.  A workgroup is 8 waves
+// (2 x 4) over a 256 x 256 output tile; each wave owns 128 x 64, i.e. 4 x 2
+// MFMA blocks of 32 x 32 (128 accumulator registers per lane), so two waves
+// share each SIMD: while one waits at the stage barrier or on its loads, the
+// other keeps the matrix core busy, and the global->LDS loads (whose rate is
+// bounded per wave) are spread over twice as many waves.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -62,7 +65,10 @@ namespace gg {
 constexpr int BM = 256;          // tile rows
 constexpr int BN = 256;          // tile cols
 constexpr int BK = 32;           // reduction stage
-constexpr int NT = 256;          // threads per workgroup (4 waves)
+constexpr int NWAVE = 8;         // waves per workgroup, 2 x 4 over the tile
+constexpr int NT = 64 * NWAVE;   // threads per workgroup
+constexpr int TM = 4;            // 32-row MFMA blocks per wave (wave tile 128 rows)
+constexpr int TN = 2;            // 32-col MFMA blocks per wave (wave tile 64 cols)
 constexpr int NSTAGE = 4;        // LDS stages (loads run NSTAGE - 1 stages ahead)
 constexpr int OP_BYTES = 256 * BK * 2;      // one operand's stage tile: 16 KB
 constexpr int STAGE_BYTES = 2 * OP_BYTES;   // A then B: 32 KB
@@ -133,8 +139,8 @@ __device__ __forceinline__ void stage_barrier() {
 
 // ---- global -> LDS, one stage of one operand ------------------------------------
 
-// The 4 loads a thread issues for one operand stage.  Load j of wave w
-// fills LDS bytes [1024 (4 w + j), +1024) of the operand's stage tile; lane
+// The 2 loads a thread issues for one operand stage.  Load j of wave w
+// fills LDS bytes [1024 (2 w + j), +1024) of the operand's stage tile; lane
 // i writes 16 bytes at 16 i.  Offsets beyond the record count read as zero.
 struct DmaCtx {
   __amdgpu_buffer_rsrc_t rs;
@@ -150,23 +156,24 @@ __device__ __forceinline__ DmaCtx dma_ctx(const Operand& op, int q0, int tid) {
   const int lane = (int)opaque_v((uint32_t)(tid & 63));
   const int w = tid >> 6;
   if constexpr (STRIDED) {
-    // wave w fills block w (tile rows 64 w ..): load j covers reduction rows
-    // 8 j .. 8 j + 7; lane i: row 8 j + i / 8, chunk position i mod 8,
-    // logical chunk (i mod 8) ^ 4 ((row / 2) mod 2) = (i mod 8) ^ 4 ((i / 16) mod 2).
+    // wave w fills half w mod 2 of block w / 2 (tile rows 64 (w / 2) ..):
+    // load j covers reduction rows 16 (w mod 2) + 8 j .. + 7; lane i: row
+    // 16 (w mod 2) + 8 j + i / 8, chunk position i mod 8, logical chunk
+    // (i mod 8) ^ 4 ((row / 2) mod 2) = (i mod 8) ^ 4 ((i / 16) mod 2).
     const int left = op.red - q0;
     const uint32_t nrec = left > 0 ? (uint32_t)(left - 1) * op.ld_bytes + op.row_tail : 0u;
     c.rs = make_rsrc(op.origin + (int64_t)q0 * op.ld_bytes, nrec);
     const int chunk = (lane & 7) ^ (4 * ((lane >> 4) & 1));
-    c.voff = (uint32_t)(lane >> 3) * op.ld_bytes + (uint32_t)(128 * w + 16 * chunk);
+    c.voff = (uint32_t)((lane >> 3) + 16 * (w & 1)) * op.ld_bytes + (uint32_t)(128 * (w >> 1) + 16 * chunk);
     c.step = 8u * op.ld_bytes;
   } else {
-    // load j of wave w covers tile rows 64 w + 16 j .. + 15; lane i: row
-    // 64 w + 16 j + i / 4, chunk position i mod 4, logical chunk
+    // load j of wave w covers tile rows 32 w + 16 j .. + 15; lane i: row
+    // 32 w + 16 j + i / 4, chunk position i mod 4, logical chunk
     // (i mod 4) ^ ((row / 4) mod 4) = (i mod 4) ^ ((i / 16) mod 4).
     const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - 2u * (uint32_t)q0 : 0u;
     c.rs = make_rsrc(op.origin + 2 * (int64_t)q0, nrec);
     const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
-    uint32_t v = (uint32_t)(64 * w + (lane >> 2)) * op.ld_bytes + 16u * (uint32_t)chunk;
+    uint32_t v = (uint32_t)(32 * w + (lane >> 2)) * op.ld_bytes + 16u * (uint32_t)chunk;
     if (q0 + 8 * chunk >= op.red) v = kOutOfRange;   // past the reduction end: zero
     c.voff = v;
     c.step = 16u * op.ld_bytes;
@@ -176,31 +183,32 @@ __device__ __forceinline__ DmaCtx dma_ctx(const Operand& op, int q0, int tid) {
 
 __device__ __forceinline__ void dma_load(const DmaCtx& c, uint8_t* lds_op, int wave, int j) {
   // the wave's first 1 KB block of this tile, recomputed per use
-  const uint32_t wbase = opaque_s((uint32_t)(4 * wave) * 1024u);
+  const uint32_t wbase = opaque_s((uint32_t)(2 * wave) * 1024u);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, LDS_PTR(lds_op + wbase + 1024 * j), 16, c.voff, j * c.step, 0, 0);
 }
 
 // ---- LDS -> MFMA fragments ------------------------------------------------------
 
 // A fragment: 8 consecutive reduction values (sub-step ks, half l / 32) of
-// tile row 32 i + l % 32 of the wave's 128-row slice.
+// row 32 i + l % 32 of the wave's slice of an operand tile (128 rows of A,
+// 64 rows of B).
 struct Frags {
-  bf16x8 a[4];
-  bf16x8 b[4];
+  bf16x8 a[TM];
+  bf16x8 b[TN];
 };
 
-// Lane-dependent part of the fragment addresses of one operand (its wave
-// slice index wp = wm or wn).  Red-contig: the byte offset of chunk 2 ks +
-// l / 32 of row 128 wp + l % 32, for ks = 0, 1 (the XOR swizzle mixes ks
-// with the lane bits).  Red-strided: the offset of the 4-value group a
-// source lane points at, for fragment parity i mod 2 (sub-step, fragment
-// pair and read half are added as immediates).
+// Lane-dependent part of the fragment addresses of one operand whose wave
+// slice starts at tile row r0 (a multiple of 64).  Red-contig: the byte
+// offset of chunk 2 ks + l / 32 of row r0 + l % 32, for ks = 0, 1 (the XOR
+// swizzle mixes ks with the lane bits).  Red-strided: the offset of the
+// 4-value group a source lane points at, for fragment parity i mod 2
+// (sub-step, fragment pair and read half are added as immediates).
 struct FragAddr {
   uint32_t o[2];
 };
 
 template <bool STRIDED>
-__device__ __forceinline__ FragAddr frag_addr(int wp, int lane) {
+__device__ __forceinline__ FragAddr frag_addr(int r0, int lane) {
   FragAddr f;
   if constexpr (STRIDED) {
     const int g = lane >> 4, s = lane & 15;
@@ -209,10 +217,10 @@ __device__ __forceinline__ FragAddr frag_addr(int wp, int lane) {
 #pragma unroll
     for (int par = 0; par < 2; ++par) {
       const int chunk = (4 * par + 2 * (g & 1) + ((s & 3) >> 1)) ^ sw;
-      f.o[par] = (uint32_t)(2 * wp * 4096 + qrow * 128 + 16 * chunk + 8 * (s & 1));
+      f.o[par] = (uint32_t)((r0 / 64) * 4096 + qrow * 128 + 16 * chunk + 8 * (s & 1));
     }
   } else {
-    const int row = 128 * wp + (lane & 31);
+    const int row = r0 + (lane & 31);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int chunk = (2 * ks + (lane >> 5)) ^ ((row >> 2) & 3);
@@ -236,7 +244,7 @@ __device__ __forceinline__ bf16x8 read_tr_pair(const uint8_t* lds, uint32_t off)
 template <bool STRIDED>
 __device__ __forceinline__ bf16x8 read_frag(const uint8_t* lds, const FragAddr& fa, int ks, int i) {
   if constexpr (STRIDED) {
-    // block 2 wp + i / 2, reduction rows 16 ks + ..., fragment parity i mod 2
+    // block r0 / 64 + i / 2, reduction rows 16 ks + ..., fragment parity i mod 2
     return read_tr_pair(lds, fa.o[i & 1] + (uint32_t)((i >> 1) * 4096 + ks * 16 * 128));
   } else {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(lds + fa.o[ks] + (uint32_t)(i * 32 * 64)));
@@ -247,9 +255,9 @@ template <bool A_STRIDED, bool B_STRIDED>
 __device__ __forceinline__ void read_stage_frags(const uint8_t* As, const uint8_t* Bs, const FragAddr& faa,
                                                  const FragAddr& fab, int ks, Frags& f) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) f.a[i] = read_frag<A_STRIDED>(As, faa, ks, i);
+  for (int i = 0; i < TM; ++i) f.a[i] = read_frag<A_STRIDED>(As, faa, ks, i);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) f.b[j] = read_frag<B_STRIDED>(Bs, fab, ks, j);
+  for (int j = 0; j < TN; ++j) f.b[j] = read_frag<B_STRIDED>(Bs, fab, ks, j);
 }
 
 // Phase fence for the MFMA stream: an empty statement that claims to read and
@@ -258,27 +266,27 @@ __device__ __forceinline__ void read_stage_frags(const uint8_t* As, const uint8_
 // reads (it did, and then copied fragment registers around the loop).  With
 // it, MFMAs issued before the fence stay before it and MFMAs after it stay
 // after; it emits no instruction.
-__device__ __forceinline__ void mfma_fence(floatx16 (&acc)[4][4]) {
+__device__ __forceinline__ void mfma_fence(floatx16 (&acc)[TM][TN]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) asm volatile("" : "+a"(acc[i][j]) :: "memory");
+    for (int j = 0; j < TN; ++j) asm volatile("" : "+a"(acc[i][j]) :: "memory");
 }
 
-// 16 MFMAs of one sub-step.  The B fragment is the MFMA's first operand, so
-// each 32 x 32 result block is C^T and a lane ends up holding 4 consecutive
-// output columns of one output row (see store_tile).
-__device__ __forceinline__ void mfma_block(const Frags& f, floatx16 (&acc)[4][4]) {
+// The TM x TN MFMAs of one sub-step.  The B fragment is the MFMA's first
+// operand, so each 32 x 32 result block is C^T and a lane ends up holding 4
+// consecutive output columns of one output row (see store_tile).
+__device__ __forceinline__ void mfma_block(const Frags& f, floatx16 (&acc)[TM][TN]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
 // ---- the main loop ---------------------------------------------------------------
 
-// Issue the 8 global->LDS loads (4 per operand) of stage `st` into stage
+// Issue the 4 global->LDS loads (2 per operand) of stage `st` into stage
 // buffer `buf` (A tile at +0, B tile at +OP_BYTES).
 template <bool A_STRIDED, bool B_STRIDED>
 __device__ __forceinline__ void load_stage(const Operand& A, const Operand& B, int st, uint8_t* buf,
@@ -286,9 +294,9 @@ __device__ __forceinline__ void load_stage(const Operand& A, const Operand& B, i
   const DmaCtx ca = dma_ctx<A_STRIDED>(A, st * BK, tid);
   const DmaCtx cb = dma_ctx<B_STRIDED>(B, st * BK, tid);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dma_load(ca, buf, wave, j);
+  for (int j = 0; j < 2; ++j) dma_load(ca, buf, wave, j);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) dma_load(cb, buf + OP_BYTES, wave, j);
+  for (int j = 0; j < 2; ++j) dma_load(cb, buf + OP_BYTES, wave, j);
 }
 
 // Wait until at most n global->LDS loads of this wave are in flight, then
@@ -304,11 +312,11 @@ __device__ __forceinline__ void stage_barrier_vm() {
 // The reduction loop of one output tile.  Stage kt (BK = 32 reduction
 // values of both operands) lives in LDS buffer kt mod 4; the loads of stage
 // kt + 4 are issued as soon as stage kt is consumed, so three stages (96 KB)
-// are in flight while one is read.  Per stage, in this order:
+// are in flight while one is read.  Per stage and wave, in this order:
 //   MFMA sub-step 0 (fragments f0, read earlier)
 //   wait for stage kt+1, barrier
-//   load stage kt+4 into the buffer of stage kt
-//   read sub-step 0 of stage kt+1 -> f0, interleaved with MFMA sub-step 1 (f1)
+//   MFMA sub-step 1 (f1), interleaved with the loads of stage kt+4 into the
+//   buffer of stage kt and the reads of sub-step 0 of stage kt+1 -> f0
 //   read sub-step 1 of stage kt+1 -> f1
 // The four buffers are distinct restrict-qualified pointers and the loop is
 // unrolled by four so that every LDS access names its buffer: the compiler
@@ -316,12 +324,30 @@ __device__ __forceinline__ void stage_barrier_vm() {
 // buffer and does not make the read wait for it.  Loads past the reduction
 // end write zeros (never read for this tile); the caller waits for them
 // before the LDS is reused.
+#ifndef GG_LOAD_EVERY
+#define GG_LOAD_EVERY 2
+#endif
+#ifndef GG_SPLIT_LOADS
+#define GG_SPLIT_LOADS 1
+#endif
+#ifndef GG_SPLIT_GAP
+#define GG_SPLIT_GAP 4
+#endif
+#ifndef GG_SPLIT_AT
+#define GG_SPLIT_AT 1
+#endif
+constexpr int kLoadEvery = GG_LOAD_EVERY;
+constexpr int kSplitGap = GG_SPLIT_GAP;
+constexpr int kSplitAt = GG_SPLIT_AT;
+static_assert(kSplitAt < kSplitGap && kSplitGap + kSplitAt < TM * TN, "two loads per sub-step");
+static_assert(kLoadEvery >= 1 && 4 * kLoadEvery <= TM * TN + kLoadEvery - 1, "loads must fit in the sub-step");
+
 template <bool A_STRIDED, bool B_STRIDED>
 __device__ __attribute__((always_inline)) inline void mainloop(
     uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
     uint8_t* __restrict__ s3, const uint8_t* __restrict__ a_origin,
     const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid, int wave,
-    const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[4][4]) {
+    const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[TM][TN]) {
   // The global operands are only read here; deriving every load from these
   // restrict-qualified pointers (and every LDS access from s0..s3) lets each
   // global->LDS load carry the identity of the one stage buffer it writes.
@@ -330,31 +356,101 @@ __device__ __attribute__((always_inline)) inline void mainloop(
   const int nk = (A.red + BK - 1) / BK;
   if (nk <= 0) return;
   Frags f0, f1;
+#if GG_SPLIT_LOADS
+  // stages 0..2 and the A half of stage 3; stage 0's first sub-step issues
+  // the B half of stage 3
+  load_stage<A_STRIDED, B_STRIDED>(A, B, 0, s0, tid, wave);
+  load_stage<A_STRIDED, B_STRIDED>(A, B, 1, s1, tid, wave);
+  load_stage<A_STRIDED, B_STRIDED>(A, B, 2, s2, tid, wave);
+  {
+    const DmaCtx ca = dma_ctx<A_STRIDED>(A, 3 * BK, tid);
+    dma_load(ca, s3, wave, 0);
+    dma_load(ca, s3, wave, 1);
+  }
+  stage_barrier_vm<10>();                       // stage 0 landed
+#else
   load_stage<A_STRIDED, B_STRIDED>(A, B, 0, s0, tid, wave);
   load_stage<A_STRIDED, B_STRIDED>(A, B, 1, s1, tid, wave);
   load_stage<A_STRIDED, B_STRIDED>(A, B, 2, s2, tid, wave);
   load_stage<A_STRIDED, B_STRIDED>(A, B, 3, s3, tid, wave);
-  stage_barrier_vm<24>();                       // stage 0 landed
+  stage_barrier_vm<12>();                       // stage 0 landed
+#endif
   read_stage_frags<A_STRIDED, B_STRIDED>(s0, s0 + OP_BYTES, faa, fab, 0, f0);
   read_stage_frags<A_STRIDED, B_STRIDED>(s0, s0 + OP_BYTES, faa, fab, 1, f1);
 
+#if GG_SPLIT_LOADS
 // One stage (buffers named directly, so every access is based on one of the
-// restrict-qualified parameters).
+// restrict-qualified parameters).  BC, BN, BP: the buffers of stages KT,
+// KT + 1 and KT - 1 (= KT + 3 mod 4).  A wave's global->LDS loads are
+// accepted at a bounded rate, and a load that cannot issue yet stalls the
+// (in-order) wave -- and with it the MFMAs behind it.  So each sub-step
+// issues only two loads, kSplitGap MFMAs apart: the first sub-step the B
+// half of stage KT + 3 (into BP, whose reads all finished before the
+// previous stage's barrier), the second the A half of stage KT + 4 (into BC,
+// free once this stage's barrier is passed).
+#define GG_STAGE(BC, BN, BP, KT)                                                          \
+  {                                                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    const DmaCtx cb = dma_ctx<B_STRIDED>(B, ((KT) + 3) * BK, tid);                        \
+    _Pragma("unroll") for (int q = 0; q < TM * TN; ++q) {                                 \
+      const int i = q / TN, j = q % TN;                                                   \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.b[j], f0.a[i], acc[i][j], 0, 0, 0); \
+      if (q % kSplitGap == kSplitAt && q / kSplitGap < 2)                                 \
+        dma_load(cb, (BP) + OP_BYTES, wave, q / kSplitGap);                               \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+    }                                                                                     \
+    mfma_fence(acc);                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    stage_barrier_vm<8>(); /* stage KT+1 landed; stage KT consumed */                     \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    const DmaCtx ca = dma_ctx<A_STRIDED>(A, ((KT) + 4) * BK, tid);                        \
+    _Pragma("unroll") for (int q = 0; q < TM * TN; ++q) {                                 \
+      const int i = q / TN, j = q % TN;                                                   \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0); \
+      if (q % kSplitGap == kSplitAt && q / kSplitGap < 2)                                 \
+        dma_load(ca, BC, wave, q / kSplitGap);                                            \
+      if (q < TM) f0.a[q] = read_frag<A_STRIDED>(BN, faa, 0, q);                          \
+      else if (q < TM + TN) f0.b[q - TM] = read_frag<B_STRIDED>((BN) + OP_BYTES, fab, 0, q - TM); \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+    }                                                                                     \
+    mfma_fence(acc);                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    read_stage_frags<A_STRIDED, B_STRIDED>(BN, (BN) + OP_BYTES, faa, fab, 1, f1);         \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+  }
+
+  for (int kt = 0; kt < nk; kt += 4) {
+    GG_STAGE(s0, s1, s3, kt)
+    if (kt + 1 < nk) GG_STAGE(s1, s2, s0, kt + 1)
+    if (kt + 2 < nk) GG_STAGE(s2, s3, s1, kt + 2)
+    if (kt + 3 < nk) GG_STAGE(s3, s0, s2, kt + 3)
+  }
+#else
+// One stage (buffers named directly, so every access is based on one of the
+// restrict-qualified parameters).  The four loads of stage KT + 4 are spread
+// over the second sub-step's MFMAs, one after every kLoadEvery-th: a wave's
+// global->LDS loads are accepted at a bounded rate, and a load that cannot
+// issue yet stalls the (in-order) wave, so a burst of them right after the
+// barrier would idle the matrix core while both waves of a SIMD wait.
 #define GG_STAGE(BC, BN, KT)                                                              \
   {                                                                                       \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     mfma_block(f0, acc);                                                                  \
     mfma_fence(acc);                                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                    \
-    stage_barrier_vm<16>(); /* stage KT+1 landed; stage KT consumed */                    \
+    stage_barrier_vm<8>(); /* stage KT+1 landed; stage KT consumed */                     \
     __builtin_amdgcn_sched_barrier(0);                                                    \
-    load_stage<A_STRIDED, B_STRIDED>(A, B, (KT) + 4, BC, tid, wave);                      \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                      \
-      const int i = q >> 2, j = q & 3;                                                    \
+    const DmaCtx ca = dma_ctx<A_STRIDED>(A, ((KT) + 4) * BK, tid);                        \
+    const DmaCtx cb = dma_ctx<B_STRIDED>(B, ((KT) + 4) * BK, tid);                        \
+    _Pragma("unroll") for (int q = 0; q < TM * TN; ++q) {                                 \
+      const int i = q / TN, j = q % TN;                                                   \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0); \
-      if (q < 4) f0.a[q] = read_frag<A_STRIDED>(BN, faa, 0, q);                           \
-      else if (q < 8) f0.b[q - 4] = read_frag<B_STRIDED>((BN) + OP_BYTES, fab, 0, q - 4); \
+      if (q % kLoadEvery == 0 && q / kLoadEvery < 4) {                                    \
+        const int l = q / kLoadEvery;                                                     \
+        if (l < 2) dma_load(ca, BC, wave, l); else dma_load(cb, (BC) + OP_BYTES, wave, l - 2); \
+      }                                                                                   \
+      if (q < TM) f0.a[q] = read_frag<A_STRIDED>(BN, faa, 0, q);                          \
+      else if (q < TM + TN) f0.b[q - TM] = read_frag<B_STRIDED>((BN) + OP_BYTES, fab, 0, q - TM); \
       __builtin_amdgcn_sched_barrier(0);                                                  \
     }                                                                                     \
     mfma_fence(acc);                                                                      \
@@ -369,6 +465,7 @@ __device__ __attribute__((always_inline)) inline void mainloop(
     if (kt + 2 < nk) GG_STAGE(s2, s3, kt + 2)
     if (kt + 3 < nk) GG_STAGE(s3, s0, kt + 3)
   }
+#endif
 #undef GG_STAGE
 }
 
@@ -387,7 +484,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Accumulator block (i, j) holds C^T: element v of lane l is output row
-// 128 wm + 32 i + l % 32 and output column 128 wn + 32 j + 8 (v / 4) +
+// 128 wm + 32 i + l % 32 and output column 64 wn + 32 j + 8 (v / 4) +
 // 4 (l / 32) + v % 4.  So each lane stores 4 consecutive columns at a time
 // (8 bytes of bf16 or 16 bytes of fp32).  Stores go through a buffer
 // resource ending at the tile's last valid element: rows past the valid ones
@@ -395,21 +492,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // (cols is a multiple of 8) is skipped for the whole wave.
 template <bool OUT_F32>
 __device__ __forceinline__ void store_tile(uint8_t* cbase, uint32_t ldc_bytes, int rows, int cols,
-                                           int wm, int wn, int lane, const floatx16 (&acc)[4][4]) {
+                                           int wm, int wn, int lane, const floatx16 (&acc)[TM][TN]) {
   constexpr uint32_t esz = OUT_F32 ? 4 : 2;
   const uint32_t nrec = (uint32_t)(rows - 1) * ldc_bytes + (uint32_t)cols * esz;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(cbase, nrec);
   const uint32_t lane_off = opaque_v((uint32_t)(128 * wm + (lane & 31)) * ldc_bytes +
-                                     (uint32_t)(128 * wn + 4 * (lane >> 5)) * esz);
+                                     (uint32_t)(64 * wn + 4 * (lane >> 5)) * esz);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TM; ++i) {
     const uint32_t voff = lane_off + (uint32_t)(32 * i) * ldc_bytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < TN; ++j) {
       const floatx16& a = acc[i][j];
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        const int col8 = 128 * wn + 32 * j + 8 * rr;      // first of 8 columns, wave-uniform
+        const int col8 = 64 * wn + 32 * j + 8 * rr;       // first of 8 columns, wave-uniform
         if (col8 >= cols) continue;
         const uint32_t imm = (uint32_t)(32 * j + 8 * rr) * esz;
         if constexpr (OUT_F32) {
@@ -428,31 +525,31 @@ __device__ __forceinline__ void store_tile(uint8_t* cbase, uint32_t ldc_bytes, i
 }
 
 // bf16 output through LDS.  Packing to bf16 needs the values in ordinary
-// registers; moving all 256 accumulators there at once overflows them, so
-// each wave instead writes one 32 x 128 fp32 slab (block row i) from its
+// registers; moving all 128 accumulators there at once overflows them, so
+// each wave instead writes one 32 x 64 fp32 slab (block row i) from its
 // accumulator registers into its own LDS region (rows padded by 16 bytes so
 // the 16 rows a write touches fall on distinct banks), reads back 8
 // consecutive values per lane, packs them and stores 16 bytes per lane --
-// 16 lanes cover 256 contiguous bytes of an output row.  Row and column
-// predication as in store_tile.  `slab` is this wave's LDS region (>= 32 *
-// 528 bytes), free for the epilogue.
-constexpr int kSlabPitch = 128 * 4 + 16;
+// 8 lanes cover the 128 contiguous bytes of a slab row in the output.  Row
+// and column predication as in store_tile.  `slab` is this wave's LDS region
+// (>= 32 * 272 bytes), free for the epilogue.
+constexpr int kSlabPitch = 64 * 4 + 16;
 
 __device__ __forceinline__ void store_tile_bf16_lds(uint8_t* cbase, uint32_t ldc_bytes, int rows,
                                                     int cols, int wm, int wn, int lane,
-                                                    const floatx16 (&acc)[4][4], uint8_t* slab) {
+                                                    const floatx16 (&acc)[TM][TN], uint8_t* slab) {
   const uint32_t nrec = (uint32_t)(rows - 1) * ldc_bytes + (uint32_t)cols * 2u;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(cbase, nrec);
   const int wrow = lane & 31;                 // slab row this lane writes
   const int wcol = 4 * (lane >> 5);           // first of its 4 columns in each 8-column group
-  const int rcol8 = 8 * (lane & 15);          // read: 8 consecutive columns ...
-  const int rrow = lane >> 4;                 // ... of slab rows rrow + 4 q
-  const int gcol = 128 * wn + rcol8;
+  const int rcol8 = 8 * (lane & 7);           // read: 8 consecutive columns ...
+  const int rrow = lane >> 3;                 // ... of slab rows rrow + 8 q
+  const int gcol = 64 * wn + rcol8;
   const bool col_ok = gcol < cols;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < TM; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         floatx4 v = {acc[i][j][4 * rr + 0], acc[i][j][4 * rr + 1], acc[i][j][4 * rr + 2], acc[i][j][4 * rr + 3]};
@@ -460,8 +557,8 @@ __device__ __forceinline__ void store_tile_bf16_lds(uint8_t* cbase, uint32_t ldc
       }
     // LDS operations of one wave complete in order: the reads see the writes.
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int r = rrow + 4 * q;
+    for (int q = 0; q < 4; ++q) {
+      const int r = rrow + 8 * q;
       const floatx4 lo = *reinterpret_cast<const floatx4*>(slab + r * kSlabPitch + 4 * rcol8);
       const floatx4 hi = *reinterpret_cast<const floatx4*>(slab + r * kSlabPitch + 4 * rcol8 + 16);
       u32x4 o = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
@@ -611,8 +708,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);     // wave index, held in a scalar register
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave >> 2;
+  const int wn = wave & 3;
   const int E = p.num_groups;
 
   decode_groups<MODE>(p, s_start, s_end, s_pref, s_scan, tid);
@@ -634,8 +731,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   const uint8_t* pa = reinterpret_cast<const uint8_t*>(p.a);
   const uint8_t* pb = reinterpret_cast<const uint8_t*>(p.b);
   uint8_t* pc = reinterpret_cast<uint8_t*>(p.c);
-  const FragAddr faa = frag_addr<A_STRIDED>(wm, lane);
-  const FragAddr fab = frag_addr<B_STRIDED>(wn, lane);
+  const FragAddr faa = frag_addr<A_STRIDED>(128 * wm, lane);
+  const FragAddr fab = frag_addr<B_STRIDED>(64 * wn, lane);
 
   for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
     Operand A, B;
@@ -718,11 +815,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
         out_cols_valid = B.rows;
       }
     }
-    floatx16 acc[4][4];
+    floatx16 acc[TM][TN];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
@@ -735,8 +832,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     if constexpr (OUT_F32) {
       store_tile<true>(cbase, ldc_bytes, out_rows, out_cols_valid, wm, wn, lane, acc);
     } else {
-      // each wave stages through its own 32 KB stage buffer (all idle here)
-      uint8_t* slab = smem + wave * STAGE_BYTES;
+      // each wave stages through its own 16 KB of the (idle) stage buffers
+      uint8_t* slab = smem + wave * (STAGE_BYTES / 2);
       store_tile_bf16_lds(cbase, ldc_bytes, out_rows, out_cols_valid, wm, wn, lane, acc, slab);
       // the next tile's first loads overwrite these arrays
       __builtin_amdgcn_s_waitcnt(0xC07F);
