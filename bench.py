@@ -15,10 +15,17 @@ and the other shapes as context, and the fp64 CPU oracle timed on a bounded
 sample of the same workload (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Profiling helpers (each prints one JSON line of its own, not the bench line):
+  --profile-pass {fwd,dgrad,wgrad}  run only that pass of the workload
+  --copy-calibration                run a plain device-to-device copy of known
+                                    size, to scale the FETCH_SIZE / WRITE_SIZE
+                                    counters into bytes
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -29,6 +36,22 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense)
 PEAK_HBM_GBS = 8000.0
+KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_ragged_amd", "csrc", "gg_kernels.hip")
+
+# HBM bytes per launch of each pass of the workload, from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE runs of `bench.py --profile-pass P`, each divided
+# by the factor the same counter reads for `bench.py --copy-calibration`.
+# Valid only for the kernel source they were taken on (sha256 below); for any
+# other source the roofline reports traffic as null.
+MEASURED_TRAFFIC = {
+    "kernel_sha256": "e2e276d1b0e0e7995acc324d75c230bec6f190613ee3e46f7c365051a848ad42",
+    "bytes": {"fwd": 23849564670, "dgrad": 28337767415, "wgrad": 25028869737},
+}
+
+
+def kernel_sha256():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def log(*a):
@@ -139,6 +162,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the other workloads reported as context")
+    ap.add_argument("--profile-pass", choices=("fwd", "dgrad", "wgrad"),
+                    help="run only this pass (for counter collection) and exit")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain copy of known size (counter calibration) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -154,6 +181,17 @@ def main():
     dev = torch.device("cuda:0")
     gg.load()
 
+    if args.copy_calibration:
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        _, msc = time_passes([("copy", lambda: dst.copy_(src))], args.steps, args.warmup, torch)
+        print(json.dumps({"copy_calibration": {"bytes_read": nbytes, "bytes_written": nbytes,
+                                               "launches": args.warmup + args.steps,
+                                               "ms": round(sum(msc["copy"]) / len(msc["copy"]), 4)}}),
+              flush=True)
+        return
+
     wl = synth.glm_up()
     log("generating", wl.name)
     t = synth.make_inputs(wl, dev)
@@ -165,6 +203,15 @@ def main():
         ("dgrad", lambda: gg.dgrad(t["dy"], t["w"], t["offs"], out=dx)),
         ("wgrad", lambda: gg.wgrad(t["x"], t["dy"], t["offs"], out=dw)),
     ]
+    if args.profile_pass:
+        one = [f for f in fns if f[0] == args.profile_pass]
+        _, msp = time_passes(one, args.steps, args.warmup, torch)
+        v = msp[args.profile_pass]
+        print(json.dumps({"profile_pass": args.profile_pass, "workload": wl.name,
+                          "launches": args.warmup + args.steps,
+                          "ms": round(sum(v) / len(v), 4),
+                          "TFLOP/s": round(wl.flops() / (sum(v) / len(v) * 1e-3) / 1e12, 2)}), flush=True)
+        return
     log("timing", args.steps, "steps after", args.warmup, "warmup steps")
     secs, ms = time_passes(fns, args.steps, args.warmup, torch)
     flop_pass = wl.flops()
@@ -181,6 +228,9 @@ def main():
     dom = max(per_pass, key=lambda k: per_pass[k]["ms"])
     kernel_names = {"fwd": "grouped_gemm_kernel<0,false>", "dgrad": "grouped_gemm_kernel<1,false>",
                     "wgrad": "grouped_gemm_kernel<2,true>"}
+    traffic = None
+    if MEASURED_TRAFFIC["kernel_sha256"] == kernel_sha256():
+        traffic = MEASURED_TRAFFIC["bytes"].get(dom)
     roofline = {
         "bound": "mfma",
         "kernel": f"{kernel_names[dom]} ({dom})",
@@ -188,7 +238,9 @@ def main():
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",
         "frac": round(per_pass[dom]["TFLOP/s"] / PEAK_BF16_TFLOPS, 4),
-        "traffic": None,
+        "traffic": traffic,
+        "traffic_unit": "bytes per launch (HBM, counter-measured)",
+        "algorithmic_bytes": algorithmic_bytes(wl, dom),
     }
 
     context = {}
