@@ -183,7 +183,7 @@ __device__ __forceinline__ DmaCtx dma_ctx(const Operand& op, int q0, int tid) {
 
 __device__ __forceinline__ void dma_load(const DmaCtx& c, uint8_t* lds_op, int wave, int j) {
   // the wave's first 1 KB block of this tile, recomputed per use
-  const uint32_t wbase = opaque_s((uint32_t)(2 * wave) * 1024u);
+  const uint32_t wbase = opaque_s((uint32_t)uniform(2 * wave * 1024));
   __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, LDS_PTR(lds_op + wbase + 1024 * j), 16, c.voff, j * c.step, 0, 0);
 }
 
@@ -310,13 +310,14 @@ __device__ __forceinline__ void stage_barrier_vm() {
 }
 
 // The reduction loop of one output tile.  Stage kt (BK = 32 reduction
-// values of both operands) lives in LDS buffer kt mod 4; the loads of stage
-// kt + 4 are issued as soon as stage kt is consumed, so three stages (96 KB)
-// are in flight while one is read.  Per stage and wave, in this order:
-//   MFMA sub-step 0 (fragments f0, read earlier)
+// values of both operands) lives in LDS buffer kt mod 4, and the loads run
+// three stages ahead.  Per stage and wave, in this order:
+//   MFMA sub-step 0 (fragments f0, read earlier), interleaved with the loads
+//   of the B half of stage kt+3 into the buffer of stage kt-1
 //   wait for stage kt+1, barrier
-//   MFMA sub-step 1 (f1), interleaved with the loads of stage kt+4 into the
-//   buffer of stage kt and the reads of sub-step 0 of stage kt+1 -> f0
+//   MFMA sub-step 1 (f1), interleaved with the loads of the A half of stage
+//   kt+4 into the buffer of stage kt and the reads of sub-step 0 of stage
+//   kt+1 -> f0
 //   read sub-step 1 of stage kt+1 -> f1
 // The four buffers are distinct restrict-qualified pointers and the loop is
 // unrolled by four so that every LDS access names its buffer: the compiler
@@ -324,30 +325,47 @@ __device__ __forceinline__ void stage_barrier_vm() {
 // buffer and does not make the read wait for it.  Loads past the reduction
 // end write zeros (never read for this tile); the caller waits for them
 // before the LDS is reused.
-#ifndef GG_LOAD_EVERY
-#define GG_LOAD_EVERY 2
-#endif
-#ifndef GG_SPLIT_LOADS
-#define GG_SPLIT_LOADS 1
-#endif
 #ifndef GG_SPLIT_GAP
 #define GG_SPLIT_GAP 4
 #endif
 #ifndef GG_SPLIT_AT
 #define GG_SPLIT_AT 1
 #endif
-constexpr int kLoadEvery = GG_LOAD_EVERY;
+
 constexpr int kSplitGap = GG_SPLIT_GAP;
 constexpr int kSplitAt = GG_SPLIT_AT;
 static_assert(kSplitAt < kSplitGap && kSplitGap + kSplitAt < TM * TN, "two loads per sub-step");
-static_assert(kLoadEvery >= 1 && 4 * kLoadEvery <= TM * TN + kLoadEvery - 1, "loads must fit in the sub-step");
+
+// The loads a tile's main loop expects in flight when it starts: stages
+// 0..2 and the A half of stage 3 (stage 0's first sub-step issues the B half
+// of stage 3).  Issued by the caller, so they can overlap the previous tile's
+// stores.  Only for tiles with at least one reduction step.
+template <bool A_STRIDED, bool B_STRIDED>
+__device__ __attribute__((always_inline)) inline void prologue_loads(
+    uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
+    uint8_t* __restrict__ s3, const uint8_t* __restrict__ a_origin,
+    const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid, int wave) {
+  A.origin = a_origin;
+  B.origin = b_origin;
+  load_stage<A_STRIDED, B_STRIDED>(A, B, 0, s0, tid, wave);
+  load_stage<A_STRIDED, B_STRIDED>(A, B, 1, s1, tid, wave);
+  load_stage<A_STRIDED, B_STRIDED>(A, B, 2, s2, tid, wave);
+  const DmaCtx ca = dma_ctx<A_STRIDED>(A, 3 * BK, tid);
+  dma_load(ca, s3, wave, 0);
+  dma_load(ca, s3, wave, 1);
+}
+constexpr int kPrologueLoads = 10;     // per wave, after stage 0's four
+
+// Stores a wave issues for one fp32 output tile (store_tile<true> issues
+// exactly this many, in or out of range).
+constexpr int kStoresF32 = TM * TN * 4;
 
 template <bool A_STRIDED, bool B_STRIDED>
 __device__ __attribute__((always_inline)) inline void mainloop(
     uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
     uint8_t* __restrict__ s3, const uint8_t* __restrict__ a_origin,
     const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid, int wave,
-    const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[TM][TN]) {
+    const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[TM][TN], bool after_stores) {
   // The global operands are only read here; deriving every load from these
   // restrict-qualified pointers (and every LDS access from s0..s3) lets each
   // global->LDS load carry the identity of the one stage buffer it writes.
@@ -356,29 +374,16 @@ __device__ __attribute__((always_inline)) inline void mainloop(
   const int nk = (A.red + BK - 1) / BK;
   if (nk <= 0) return;
   Frags f0, f1;
-#if GG_SPLIT_LOADS
-  // stages 0..2 and the A half of stage 3; stage 0's first sub-step issues
-  // the B half of stage 3
-  load_stage<A_STRIDED, B_STRIDED>(A, B, 0, s0, tid, wave);
-  load_stage<A_STRIDED, B_STRIDED>(A, B, 1, s1, tid, wave);
-  load_stage<A_STRIDED, B_STRIDED>(A, B, 2, s2, tid, wave);
-  {
-    const DmaCtx ca = dma_ctx<A_STRIDED>(A, 3 * BK, tid);
-    dma_load(ca, s3, wave, 0);
-    dma_load(ca, s3, wave, 1);
-  }
-  stage_barrier_vm<10>();                       // stage 0 landed
-#else
-  load_stage<A_STRIDED, B_STRIDED>(A, B, 0, s0, tid, wave);
-  load_stage<A_STRIDED, B_STRIDED>(A, B, 1, s1, tid, wave);
-  load_stage<A_STRIDED, B_STRIDED>(A, B, 2, s2, tid, wave);
-  load_stage<A_STRIDED, B_STRIDED>(A, B, 3, s3, tid, wave);
-  stage_barrier_vm<12>();                       // stage 0 landed
-#endif
+  // stage 0 landed (vector memory operations complete in issue order; when
+  // the previous tile's stores were issued after this tile's prologue loads,
+  // they may still be in flight)
+  if (after_stores)
+    stage_barrier_vm<kPrologueLoads + kStoresF32>();
+  else
+    stage_barrier_vm<kPrologueLoads>();
   read_stage_frags<A_STRIDED, B_STRIDED>(s0, s0 + OP_BYTES, faa, fab, 0, f0);
   read_stage_frags<A_STRIDED, B_STRIDED>(s0, s0 + OP_BYTES, faa, fab, 1, f1);
 
-#if GG_SPLIT_LOADS
 // One stage (buffers named directly, so every access is based on one of the
 // restrict-qualified parameters).  BC, BN, BP: the buffers of stages KT,
 // KT + 1 and KT - 1 (= KT + 3 mod 4).  A wave's global->LDS loads are
@@ -425,47 +430,6 @@ __device__ __attribute__((always_inline)) inline void mainloop(
     if (kt + 2 < nk) GG_STAGE(s2, s3, s1, kt + 2)
     if (kt + 3 < nk) GG_STAGE(s3, s0, s2, kt + 3)
   }
-#else
-// One stage (buffers named directly, so every access is based on one of the
-// restrict-qualified parameters).  The four loads of stage KT + 4 are spread
-// over the second sub-step's MFMAs, one after every kLoadEvery-th: a wave's
-// global->LDS loads are accepted at a bounded rate, and a load that cannot
-// issue yet stalls the (in-order) wave, so a burst of them right after the
-// barrier would idle the matrix core while both waves of a SIMD wait.
-#define GG_STAGE(BC, BN, KT)                                                              \
-  {                                                                                       \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    mfma_block(f0, acc);                                                                  \
-    mfma_fence(acc);                                                                      \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    stage_barrier_vm<8>(); /* stage KT+1 landed; stage KT consumed */                     \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    const DmaCtx ca = dma_ctx<A_STRIDED>(A, ((KT) + 4) * BK, tid);                        \
-    const DmaCtx cb = dma_ctx<B_STRIDED>(B, ((KT) + 4) * BK, tid);                        \
-    _Pragma("unroll") for (int q = 0; q < TM * TN; ++q) {                                 \
-      const int i = q / TN, j = q % TN;                                                   \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0); \
-      if (q % kLoadEvery == 0 && q / kLoadEvery < 4) {                                    \
-        const int l = q / kLoadEvery;                                                     \
-        if (l < 2) dma_load(ca, BC, wave, l); else dma_load(cb, (BC) + OP_BYTES, wave, l - 2); \
-      }                                                                                   \
-      if (q < TM) f0.a[q] = read_frag<A_STRIDED>(BN, faa, 0, q);                          \
-      else if (q < TM + TN) f0.b[q - TM] = read_frag<B_STRIDED>((BN) + OP_BYTES, fab, 0, q - TM); \
-      __builtin_amdgcn_sched_barrier(0);                                                  \
-    }                                                                                     \
-    mfma_fence(acc);                                                                      \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    read_stage_frags<A_STRIDED, B_STRIDED>(BN, (BN) + OP_BYTES, faa, fab, 1, f1);         \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-  }
-
-  for (int kt = 0; kt < nk; kt += 4) {
-    GG_STAGE(s0, s1, kt)
-    if (kt + 1 < nk) GG_STAGE(s1, s2, kt + 1)
-    if (kt + 2 < nk) GG_STAGE(s2, s3, kt + 2)
-    if (kt + 3 < nk) GG_STAGE(s3, s0, kt + 3)
-  }
-#endif
 #undef GG_STAGE
 }
 
@@ -507,15 +471,19 @@ __device__ __forceinline__ void store_tile(uint8_t* cbase, uint32_t ldc_bytes, i
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         const int col8 = 64 * wn + 32 * j + 8 * rr;       // first of 8 columns, wave-uniform
-        if (col8 >= cols) continue;
         const uint32_t imm = (uint32_t)(32 * j + 8 * rr) * esz;
         if constexpr (OUT_F32) {
+          // Column groups past the last valid column are stored out of
+          // range (dropped) rather than skipped, so every tile issues the
+          // same number of stores (the next tile's first wait counts them).
           // Built as a float vector and bit-cast whole: a u32x4 built from
           // per-element bit casts of accumulator values was miscompiled by
           // this hipcc (every lane of the vector got element 0).
           floatx4 v = {a[4 * rr + 0], a[4 * rr + 1], a[4 * rr + 2], a[4 * rr + 3]};
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, voff + imm, 0, 0);
+          const uint32_t off = col8 < cols ? voff + imm : kOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 0);
         } else {
+          if (col8 >= cols) continue;
           u32x2 v = {pack_bf16x2(a[4 * rr + 0], a[4 * rr + 1]), pack_bf16x2(a[4 * rr + 2], a[4 * rr + 3])};
           __builtin_amdgcn_raw_buffer_store_b64(v, rs, voff + imm, 0, 0);
         }
@@ -693,6 +661,21 @@ __device__ __forceinline__ void strip_order(int64_t u, int64_t rows, int cols, i
 
 // ---- the kernel ------------------------------------------------------------------
 
+// One output tile: its operands and output window.
+struct Tile {
+  Operand A, B;
+  uint8_t* cbase;       // output element (first row, first column) of the tile
+  uint32_t ldc_bytes;   // output row pitch
+  int rows, cols;       // valid output rows / columns of the tile
+};
+
+// LDS operations of this wave complete, then all waves meet (no wait on
+// global memory operations).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+  asm volatile("s_barrier" ::: "memory");
+}
+
 template <int MODE, bool OUT_F32>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   constexpr bool A_STRIDED = (MODE == WGRAD);
@@ -734,87 +717,101 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   const FragAddr faa = frag_addr<A_STRIDED>(128 * wm, lane);
   const FragAddr fab = frag_addr<B_STRIDED>(64 * wn, lane);
 
-  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
-    Operand A, B;
-    uint8_t* cbase;
-    uint32_t ldc_bytes;
-    int out_rows, out_cols_valid;
-    {
-      const int64_t u = xcd_tile(t, total);
-      int ct;
-      int64_t rt_all;
-      if constexpr (MODE == WGRAD) {
-        // per expert: a row_tiles_w x col_tiles grid in strip order
-        const int64_t per_g = (int64_t)row_tiles_w * col_tiles;
-        const int64_t gq = u / per_g;
-        int64_t rr;
-        strip_order(u - gq * per_g, row_tiles_w, col_tiles, rr, ct);
-        rt_all = gq * row_tiles_w + rr;
+  // Decode tile t (linear index over the output tile grid) into its
+  // operand descriptions and output window.
+  auto decode_tile = [&](int64_t t, Tile& T) __attribute__((always_inline)) {
+    const int64_t u = xcd_tile(t, total);
+    int ct;
+    int64_t rt_all;
+    if constexpr (MODE == WGRAD) {
+      // per expert: a row_tiles_w x col_tiles grid in strip order
+      const int64_t per_g = (int64_t)row_tiles_w * col_tiles;
+      const int64_t gq = u / per_g;
+      int64_t rr;
+      strip_order(u - gq * per_g, row_tiles_w, col_tiles, rr, ct);
+      rt_all = gq * row_tiles_w + rr;
+    } else {
+      strip_order(u, total / col_tiles, col_tiles, rt_all, ct);
+    }
+    const int col0 = ct * BN;
+    Operand& A = T.A;
+    Operand& B = T.B;
+    if constexpr (MODE == WGRAD) {
+      const int g = (int)(rt_all / row_tiles_w);
+      const int rt = (int)(rt_all % row_tiles_w);
+      const int row0 = rt * BM;                 // first k index of the tile
+      const int s = uniform(s_start[g]), e = uniform(s_end[g]);
+      // A(row kk, red i) = X[s + i, row0 + kk]
+      A.origin = pa + 2 * ((int64_t)s * p.k + row0);
+      A.ld_bytes = (uint32_t)(2 * p.k);
+      A.rows = (int)(p.k - row0 < BM ? p.k - row0 : BM);
+      A.red = e - s;
+      A.row_tail = (uint32_t)(2 * (p.k - row0));
+      // B(row n, red i) = dY[s + i, col0 + n]
+      B.origin = pb + 2 * ((int64_t)s * p.n + col0);
+      B.ld_bytes = (uint32_t)(2 * p.n);
+      B.rows = (int)(p.n - col0 < BN ? p.n - col0 : BN);
+      B.red = e - s;
+      B.row_tail = (uint32_t)(2 * (p.n - col0));
+      T.ldc_bytes = (uint32_t)(esz * p.n);
+      T.cbase = pc + esz * ((int64_t)g * p.k * p.n + (int64_t)row0 * p.n + col0);
+      T.rows = A.rows;
+      T.cols = B.rows;
+    } else {
+      const int g = uniform(find_group(s_pref, E, (int)rt_all));
+      const int rt = (int)rt_all - uniform(s_pref[g]);
+      const int s = uniform(s_start[g]), e = uniform(s_end[g]);
+      const int row0 = s + rt * BM;             // first expert row of the tile
+      const int rows = (e - row0) < BM ? (e - row0) : BM;
+      const int64_t arow = (MODE == MASKED) ? (int64_t)g * p.m + row0 : (int64_t)row0;
+      if constexpr (MODE == DGRAD) {
+        // A(row i, red j) = dY[arow + i, j];  B(row kk, red j) = W[g, col0 + kk, j]
+        A.origin = pa + 2 * (arow * p.n);
+        A.ld_bytes = (uint32_t)(2 * p.n);
+        A.rows = rows;
+        A.red = (int)p.n;
+        A.row_tail = 0;
+        B.origin = pb + 2 * ((int64_t)g * p.k * p.n + (int64_t)col0 * p.n);
+        B.ld_bytes = (uint32_t)(2 * p.n);
+        B.rows = (int)(p.k - col0 < BN ? p.k - col0 : BN);
+        B.red = (int)p.n;
+        B.row_tail = 0;
+        T.ldc_bytes = (uint32_t)(esz * p.k);
+        T.cbase = pc + esz * (arow * p.k + col0);
       } else {
-        strip_order(u, total / col_tiles, col_tiles, rt_all, ct);
-      }
-      const int col0 = ct * BN;
-      if constexpr (MODE == WGRAD) {
-        const int g = (int)(rt_all / row_tiles_w);
-        const int rt = (int)(rt_all % row_tiles_w);
-        const int row0 = rt * BM;                 // first k index of the tile
-        const int s = uniform(s_start[g]), e = uniform(s_end[g]);
-        // A(row kk, red i) = X[s + i, row0 + kk]
-        A.origin = pa + 2 * ((int64_t)s * p.k + row0);
+        // A(row i, red kk) = X[arow + i, kk];  B(row n, red kk) = W[g, kk, col0 + n]
+        A.origin = pa + 2 * (arow * p.k);
         A.ld_bytes = (uint32_t)(2 * p.k);
-        A.rows = (int)(p.k - row0 < BM ? p.k - row0 : BM);
-        A.red = e - s;
-        A.row_tail = (uint32_t)(2 * (p.k - row0));
-        // B(row n, red i) = dY[s + i, col0 + n]
-        B.origin = pb + 2 * ((int64_t)s * p.n + col0);
+        A.rows = rows;
+        A.red = (int)p.k;
+        A.row_tail = 0;
+        B.origin = pb + 2 * ((int64_t)g * p.k * p.n + col0);
         B.ld_bytes = (uint32_t)(2 * p.n);
         B.rows = (int)(p.n - col0 < BN ? p.n - col0 : BN);
-        B.red = e - s;
+        B.red = (int)p.k;
         B.row_tail = (uint32_t)(2 * (p.n - col0));
-        ldc_bytes = (uint32_t)(esz * p.n);
-        cbase = pc + esz * ((int64_t)g * p.k * p.n + (int64_t)row0 * p.n + col0);
-        out_rows = A.rows;
-        out_cols_valid = B.rows;
-      } else {
-        const int g = uniform(find_group(s_pref, E, (int)rt_all));
-        const int rt = (int)rt_all - uniform(s_pref[g]);
-        const int s = uniform(s_start[g]), e = uniform(s_end[g]);
-        const int row0 = s + rt * BM;             // first expert row of the tile
-        const int rows = (e - row0) < BM ? (e - row0) : BM;
-        const int64_t arow = (MODE == MASKED) ? (int64_t)g * p.m + row0 : (int64_t)row0;
-        if constexpr (MODE == DGRAD) {
-          // A(row i, red j) = dY[arow + i, j];  B(row kk, red j) = W[g, col0 + kk, j]
-          A.origin = pa + 2 * (arow * p.n);
-          A.ld_bytes = (uint32_t)(2 * p.n);
-          A.rows = rows;
-          A.red = (int)p.n;
-          A.row_tail = 0;
-          B.origin = pb + 2 * ((int64_t)g * p.k * p.n + (int64_t)col0 * p.n);
-          B.ld_bytes = (uint32_t)(2 * p.n);
-          B.rows = (int)(p.k - col0 < BN ? p.k - col0 : BN);
-          B.red = (int)p.n;
-          B.row_tail = 0;
-          ldc_bytes = (uint32_t)(esz * p.k);
-          cbase = pc + esz * (arow * p.k + col0);
-        } else {
-          // A(row i, red kk) = X[arow + i, kk];  B(row n, red kk) = W[g, kk, col0 + n]
-          A.origin = pa + 2 * (arow * p.k);
-          A.ld_bytes = (uint32_t)(2 * p.k);
-          A.rows = rows;
-          A.red = (int)p.k;
-          A.row_tail = 0;
-          B.origin = pb + 2 * ((int64_t)g * p.k * p.n + col0);
-          B.ld_bytes = (uint32_t)(2 * p.n);
-          B.rows = (int)(p.n - col0 < BN ? p.n - col0 : BN);
-          B.red = (int)p.k;
-          B.row_tail = (uint32_t)(2 * (p.n - col0));
-          ldc_bytes = (uint32_t)(esz * p.n);
-          cbase = pc + esz * (arow * p.n + col0);
-        }
-        out_rows = rows;
-        out_cols_valid = B.rows;
+        T.ldc_bytes = (uint32_t)(esz * p.n);
+        T.cbase = pc + esz * (arow * p.n + col0);
       }
+      T.rows = rows;
+      T.cols = B.rows;
     }
+  };
+  auto issue_prologue = [&](const Tile& T) __attribute__((always_inline)) {
+    if (T.A.red > 0)
+      prologue_loads<A_STRIDED, B_STRIDED>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
+                                           smem + 3 * STAGE_BYTES, T.A.origin, T.B.origin, T.A,
+                                           T.B, tid, wave);
+  };
+
+  if ((int64_t)blockIdx.x >= total) return;
+  // Decodes below use an index clamped into the grid, so every Tile is
+  // assigned on every path (it stays in scalar registers).
+  const int64_t last = total - 1;
+  Tile cur;
+  decode_tile(blockIdx.x, cur);
+  issue_prologue(cur);
+  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
     floatx16 acc[TM][TN];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -823,21 +820,38 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+    // fp32 tiles after the first start with the previous tile's stores
+    // still in flight behind their prologue loads
     mainloop<A_STRIDED, B_STRIDED>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
-                                   smem + 3 * STAGE_BYTES, A.origin, B.origin, A, B, tid, wave,
-                                   faa, fab, acc);
-    // loads of stages past the end may still be landing (zeros), and other
-    // waves may still read the last stage: settle before the LDS is reused
-    stage_barrier();
+                                   smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
+                                   cur.B, tid, wave, faa, fab, acc,
+                                   OUT_F32 && t != (int64_t)blockIdx.x);
+    const int64_t tn = t + gridDim.x;
     if constexpr (OUT_F32) {
-      store_tile<true>(cbase, ldc_bytes, out_rows, out_cols_valid, wm, wn, lane, acc);
+      // Every wave is done reading this tile's stages: issue the next
+      // tile's prologue loads first, then this tile's stores, so the
+      // stores drain while those loads are in flight.  (Loads of stages
+      // past this tile's end may still be landing zeros: they complete
+      // before the next tile's, in issue order.)
+      lds_barrier();
+      Tile nxt;
+      decode_tile(tn < total ? tn : last, nxt);
+      if (tn < total) issue_prologue(nxt);
+      store_tile<true>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane, acc);
+      cur = nxt;
     } else {
+      // loads of stages past the end may still be landing (zeros), and
+      // other waves may still read the last stage: settle before the LDS
+      // is reused as the epilogue's staging area
+      stage_barrier();
       // each wave stages through its own 16 KB of the (idle) stage buffers
       uint8_t* slab = smem + wave * (STAGE_BYTES / 2);
-      store_tile_bf16_lds(cbase, ldc_bytes, out_rows, out_cols_valid, wm, wn, lane, acc, slab);
+      store_tile_bf16_lds(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane, acc, slab);
       // the next tile's first loads overwrite these arrays
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __syncthreads();
+      decode_tile(tn < total ? tn : last, cur);
+      if (tn < total) issue_prologue(cur);
     }
   }
 }
