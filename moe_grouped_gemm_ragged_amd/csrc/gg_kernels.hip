@@ -251,11 +251,11 @@ __device__ __forceinline__ bf16x8 read_frag(const uint8_t* lds, const FragAddr& 
   }
 }
 
-template <bool A_STRIDED, bool B_STRIDED>
+template <bool A_STRIDED, bool B_STRIDED, int TMA>
 __device__ __forceinline__ void read_stage_frags(const uint8_t* As, const uint8_t* Bs, const FragAddr& faa,
                                                  const FragAddr& fab, int ks, Frags& f) {
 #pragma unroll
-  for (int i = 0; i < TM; ++i) f.a[i] = read_frag<A_STRIDED>(As, faa, ks, i);
+  for (int i = 0; i < TMA; ++i) f.a[i] = read_frag<A_STRIDED>(As, faa, ks, i);
 #pragma unroll
   for (int j = 0; j < TN; ++j) f.b[j] = read_frag<B_STRIDED>(Bs, fab, ks, j);
 }
@@ -271,17 +271,6 @@ __device__ __forceinline__ void mfma_fence(floatx16 (&acc)[TM][TN]) {
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) asm volatile("" : "+a"(acc[i][j]) :: "memory");
-}
-
-// The TM x TN MFMAs of one sub-step.  The B fragment is the MFMA's first
-// operand, so each 32 x 32 result block is C^T and a lane ends up holding 4
-// consecutive output columns of one output row (see store_tile).
-__device__ __forceinline__ void mfma_block(const Frags& f, floatx16 (&acc)[TM][TN]) {
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc[i][j], 0, 0, 0);
 }
 
 // ---- the main loop ---------------------------------------------------------------
@@ -325,16 +314,6 @@ __device__ __forceinline__ void stage_barrier_vm() {
 // buffer and does not make the read wait for it.  Loads past the reduction
 // end write zeros (never read for this tile); the caller waits for them
 // before the LDS is reused.
-#ifndef GG_SPLIT_GAP
-#define GG_SPLIT_GAP 4
-#endif
-#ifndef GG_SPLIT_AT
-#define GG_SPLIT_AT 1
-#endif
-
-constexpr int kSplitGap = GG_SPLIT_GAP;
-constexpr int kSplitAt = GG_SPLIT_AT;
-static_assert(kSplitAt < kSplitGap && kSplitGap + kSplitAt < TM * TN, "two loads per sub-step");
 
 // The loads a tile's main loop expects in flight when it starts: stages
 // 0..2 and the A half of stage 3 (stage 0's first sub-step issues the B half
@@ -356,16 +335,25 @@ __device__ __attribute__((always_inline)) inline void prologue_loads(
 }
 constexpr int kPrologueLoads = 10;     // per wave, after stage 0's four
 
-// Stores a wave issues for one fp32 output tile (store_tile<true> issues
-// exactly this many, in or out of range).
-constexpr int kStoresF32 = TM * TN * 4;
+// Stores a wave issues for one fp32 output tile of TMA active row blocks
+// (store_tile<true, TMA> issues exactly this many, in or out of range).
+template <int TMA>
+constexpr int stores_f32() { return TMA * TN * 4; }
 
-template <bool A_STRIDED, bool B_STRIDED>
+// TMA: active 32-row blocks of A per wave -- TM for a full 256-row tile, 2
+// for a half-height tile (an expert's last 128 rows or fewer), whose waves
+// then own 64 x 64 each.  prev_stores: fp32 stores issued after this tile's
+// prologue loads (the previous tile's), 0 if none.
+template <bool A_STRIDED, bool B_STRIDED, int TMA>
 __device__ __attribute__((always_inline)) inline void mainloop(
     uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
     uint8_t* __restrict__ s3, const uint8_t* __restrict__ a_origin,
     const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid, int wave,
-    const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[TM][TN], bool after_stores) {
+    const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[TM][TN], int prev_stores) {
+  // loads spread over each sub-step's MFMAs: two per sub-step, half a
+  // sub-step apart
+  constexpr int kSplitGap = TMA * TN / 2;
+  constexpr int kSplitAt = 1;
   // The global operands are only read here; deriving every load from these
   // restrict-qualified pointers (and every LDS access from s0..s3) lets each
   // global->LDS load carry the identity of the one stage buffer it writes.
@@ -377,12 +365,14 @@ __device__ __attribute__((always_inline)) inline void mainloop(
   // stage 0 landed (vector memory operations complete in issue order; when
   // the previous tile's stores were issued after this tile's prologue loads,
   // they may still be in flight)
-  if (after_stores)
-    stage_barrier_vm<kPrologueLoads + kStoresF32>();
+  if (prev_stores == stores_f32<TM>())
+    stage_barrier_vm<kPrologueLoads + stores_f32<TM>()>();
+  else if (prev_stores == stores_f32<2>())
+    stage_barrier_vm<kPrologueLoads + stores_f32<2>()>();
   else
     stage_barrier_vm<kPrologueLoads>();
-  read_stage_frags<A_STRIDED, B_STRIDED>(s0, s0 + OP_BYTES, faa, fab, 0, f0);
-  read_stage_frags<A_STRIDED, B_STRIDED>(s0, s0 + OP_BYTES, faa, fab, 1, f1);
+  read_stage_frags<A_STRIDED, B_STRIDED, TMA>(s0, s0 + OP_BYTES, faa, fab, 0, f0);
+  read_stage_frags<A_STRIDED, B_STRIDED, TMA>(s0, s0 + OP_BYTES, faa, fab, 1, f1);
 
 // One stage (buffers named directly, so every access is based on one of the
 // restrict-qualified parameters).  BC, BN, BP: the buffers of stages KT,
@@ -397,7 +387,7 @@ __device__ __attribute__((always_inline)) inline void mainloop(
   {                                                                                       \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     const DmaCtx cb = dma_ctx<B_STRIDED>(B, ((KT) + 3) * BK, tid);                        \
-    _Pragma("unroll") for (int q = 0; q < TM * TN; ++q) {                                 \
+    _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                \
       const int i = q / TN, j = q % TN;                                                   \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.b[j], f0.a[i], acc[i][j], 0, 0, 0); \
       if (q % kSplitGap == kSplitAt && q / kSplitGap < 2)                                 \
@@ -409,18 +399,18 @@ __device__ __attribute__((always_inline)) inline void mainloop(
     stage_barrier_vm<8>(); /* stage KT+1 landed; stage KT consumed */                     \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     const DmaCtx ca = dma_ctx<A_STRIDED>(A, ((KT) + 4) * BK, tid);                        \
-    _Pragma("unroll") for (int q = 0; q < TM * TN; ++q) {                                 \
+    _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                \
       const int i = q / TN, j = q % TN;                                                   \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0); \
       if (q % kSplitGap == kSplitAt && q / kSplitGap < 2)                                 \
         dma_load(ca, BC, wave, q / kSplitGap);                                            \
-      if (q < TM) f0.a[q] = read_frag<A_STRIDED>(BN, faa, 0, q);                          \
-      else if (q < TM + TN) f0.b[q - TM] = read_frag<B_STRIDED>((BN) + OP_BYTES, fab, 0, q - TM); \
+      if (q < TMA) f0.a[q] = read_frag<A_STRIDED>(BN, faa, 0, q);                         \
+      else if (q < TMA + TN) f0.b[q - TMA] = read_frag<B_STRIDED>((BN) + OP_BYTES, fab, 0, q - TMA); \
       __builtin_amdgcn_sched_barrier(0);                                                  \
     }                                                                                     \
     mfma_fence(acc);                                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                    \
-    read_stage_frags<A_STRIDED, B_STRIDED>(BN, (BN) + OP_BYTES, faa, fab, 1, f1);         \
+    read_stage_frags<A_STRIDED, B_STRIDED, TMA>(BN, (BN) + OP_BYTES, faa, fab, 1, f1);    \
     __builtin_amdgcn_sched_barrier(0);                                                    \
   }
 
@@ -438,7 +428,6 @@ __device__ __attribute__((always_inline)) inline void mainloop(
 typedef float floatx2 __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Two fp32 -> two bf16 (round to nearest even) packed in one dword, low
 // half first.
@@ -447,23 +436,23 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
 }
 
-// Accumulator block (i, j) holds C^T: element v of lane l is output row
-// 128 wm + 32 i + l % 32 and output column 64 wn + 32 j + 8 (v / 4) +
-// 4 (l / 32) + v % 4.  So each lane stores 4 consecutive columns at a time
-// (8 bytes of bf16 or 16 bytes of fp32).  Stores go through a buffer
-// resource ending at the tile's last valid element: rows past the valid ones
-// are dropped by the range check; a group of 8 columns past the valid ones
-// (cols is a multiple of 8) is skipped for the whole wave.
-template <bool OUT_F32>
-__device__ __forceinline__ void store_tile(uint8_t* cbase, uint32_t ldc_bytes, int rows, int cols,
-                                           int wm, int wn, int lane, const floatx16 (&acc)[TM][TN]) {
-  constexpr uint32_t esz = OUT_F32 ? 4 : 2;
+// fp32 output straight from the accumulators.  Accumulator block (i, j)
+// holds C^T: element v of lane l is output row 32 TMA wm + 32 i + l % 32 and
+// output column 64 wn + 32 j + 8 (v / 4) + 4 (l / 32) + v % 4, so each lane
+// stores 4 consecutive columns (16 bytes) at a time.  Stores go through a
+// buffer resource ending at the tile's last valid element: rows past the
+// valid ones are dropped by the range check, and a group of 8 columns past
+// the valid ones (cols is a multiple of 8) is sent out of range.
+template <int TMA>
+__device__ __forceinline__ void store_tile_f32(uint8_t* cbase, uint32_t ldc_bytes, int rows, int cols,
+                                               int wm, int wn, int lane, const floatx16 (&acc)[TM][TN]) {
+  constexpr uint32_t esz = 4;
   const uint32_t nrec = (uint32_t)(rows - 1) * ldc_bytes + (uint32_t)cols * esz;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(cbase, nrec);
-  const uint32_t lane_off = opaque_v((uint32_t)(128 * wm + (lane & 31)) * ldc_bytes +
+  const uint32_t lane_off = opaque_v((uint32_t)(32 * TMA * wm + (lane & 31)) * ldc_bytes +
                                      (uint32_t)(64 * wn + 4 * (lane >> 5)) * esz);
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < TMA; ++i) {
     const uint32_t voff = lane_off + (uint32_t)(32 * i) * ldc_bytes;
 #pragma unroll
     for (int j = 0; j < TN; ++j) {
@@ -472,21 +461,15 @@ __device__ __forceinline__ void store_tile(uint8_t* cbase, uint32_t ldc_bytes, i
       for (int rr = 0; rr < 4; ++rr) {
         const int col8 = 64 * wn + 32 * j + 8 * rr;       // first of 8 columns, wave-uniform
         const uint32_t imm = (uint32_t)(32 * j + 8 * rr) * esz;
-        if constexpr (OUT_F32) {
-          // Column groups past the last valid column are stored out of
-          // range (dropped) rather than skipped, so every tile issues the
-          // same number of stores (the next tile's first wait counts them).
-          // Built as a float vector and bit-cast whole: a u32x4 built from
-          // per-element bit casts of accumulator values was miscompiled by
-          // this hipcc (every lane of the vector got element 0).
-          floatx4 v = {a[4 * rr + 0], a[4 * rr + 1], a[4 * rr + 2], a[4 * rr + 3]};
-          const uint32_t off = col8 < cols ? voff + imm : kOutOfRange;
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 0);
-        } else {
-          if (col8 >= cols) continue;
-          u32x2 v = {pack_bf16x2(a[4 * rr + 0], a[4 * rr + 1]), pack_bf16x2(a[4 * rr + 2], a[4 * rr + 3])};
-          __builtin_amdgcn_raw_buffer_store_b64(v, rs, voff + imm, 0, 0);
-        }
+        // Column groups past the last valid column are stored out of range
+        // (dropped) rather than skipped, so every tile of a shape issues the
+        // same number of stores (the next tile's first wait counts them).
+        // Built as a float vector and bit-cast whole: a u32x4 built from
+        // per-element bit casts of accumulator values was miscompiled by
+        // this hipcc (every lane of the vector got element 0).
+        floatx4 v = {a[4 * rr + 0], a[4 * rr + 1], a[4 * rr + 2], a[4 * rr + 3]};
+        const uint32_t off = col8 < cols ? voff + imm : kOutOfRange;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, 0);
       }
     }
   }
@@ -499,10 +482,11 @@ __device__ __forceinline__ void store_tile(uint8_t* cbase, uint32_t ldc_bytes, i
 // the 16 rows a write touches fall on distinct banks), reads back 8
 // consecutive values per lane, packs them and stores 16 bytes per lane --
 // 8 lanes cover the 128 contiguous bytes of a slab row in the output.  Row
-// and column predication as in store_tile.  `slab` is this wave's LDS region
+// and column predication as in store_tile_f32.  `slab` is this wave's LDS region
 // (>= 32 * 272 bytes), free for the epilogue.
 constexpr int kSlabPitch = 64 * 4 + 16;
 
+template <int TMA>
 __device__ __forceinline__ void store_tile_bf16_lds(uint8_t* cbase, uint32_t ldc_bytes, int rows,
                                                     int cols, int wm, int wn, int lane,
                                                     const floatx16 (&acc)[TM][TN], uint8_t* slab) {
@@ -515,7 +499,7 @@ __device__ __forceinline__ void store_tile_bf16_lds(uint8_t* cbase, uint32_t ldc
   const int gcol = 64 * wn + rcol8;
   const bool col_ok = gcol < cols;
 #pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  for (int i = 0; i < TMA; ++i) {
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -531,7 +515,7 @@ __device__ __forceinline__ void store_tile_bf16_lds(uint8_t* cbase, uint32_t ldc
       const floatx4 hi = *reinterpret_cast<const floatx4*>(slab + r * kSlabPitch + 4 * rcol8 + 16);
       u32x4 o = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
                  pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
-      uint32_t voff = (uint32_t)(128 * wm + 32 * i + r) * ldc_bytes + (uint32_t)gcol * 2u;
+      uint32_t voff = (uint32_t)(32 * TMA * wm + 32 * i + r) * ldc_bytes + (uint32_t)gcol * 2u;
       if (!col_ok) voff = kOutOfRange;
       __builtin_amdgcn_raw_buffer_store_b128(o, rs, voff, 0, 0);
     }
@@ -715,6 +699,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   const uint8_t* pb = reinterpret_cast<const uint8_t*>(p.b);
   uint8_t* pc = reinterpret_cast<uint8_t*>(p.c);
   const FragAddr faa = frag_addr<A_STRIDED>(128 * wm, lane);
+  const FragAddr faa_half = frag_addr<A_STRIDED>(64 * wm, lane);   // half-height tiles
   const FragAddr fab = frag_addr<B_STRIDED>(64 * wn, lane);
 
   // Decode tile t (linear index over the output tile grid) into its
@@ -811,6 +796,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   Tile cur;
   decode_tile(blockIdx.x, cur);
   issue_prologue(cur);
+  int prev_stores = 0;    // fp32 stores issued after the current tile's prologue loads
   for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
     floatx16 acc[TM][TN];
 #pragma unroll
@@ -820,12 +806,19 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+    // An expert's last tile with 128 rows or fewer runs at half height:
+    // each wave computes 64 x 64, skipping the MFMAs of empty rows.
+    const bool half = (MODE != WGRAD) && cur.rows <= BM / 2;
     // fp32 tiles after the first start with the previous tile's stores
     // still in flight behind their prologue loads
-    mainloop<A_STRIDED, B_STRIDED>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
-                                   smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
-                                   cur.B, tid, wave, faa, fab, acc,
-                                   OUT_F32 && t != (int64_t)blockIdx.x);
+    if (half)
+      mainloop<A_STRIDED, B_STRIDED, 2>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
+                                        smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
+                                        cur.B, tid, wave, faa_half, fab, acc, prev_stores);
+    else
+      mainloop<A_STRIDED, B_STRIDED, TM>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
+                                         smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
+                                         cur.B, tid, wave, faa, fab, acc, prev_stores);
     const int64_t tn = t + gridDim.x;
     if constexpr (OUT_F32) {
       // Every wave is done reading this tile's stages: issue the next
@@ -837,7 +830,13 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
       Tile nxt;
       decode_tile(tn < total ? tn : last, nxt);
       if (tn < total) issue_prologue(nxt);
-      store_tile<true>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane, acc);
+      if (half) {
+        store_tile_f32<2>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane, acc);
+        prev_stores = stores_f32<2>();
+      } else {
+        store_tile_f32<TM>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane, acc);
+        prev_stores = stores_f32<TM>();
+      }
       cur = nxt;
     } else {
       // loads of stages past the end may still be landing (zeros), and
@@ -846,7 +845,10 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
       stage_barrier();
       // each wave stages through its own 16 KB of the (idle) stage buffers
       uint8_t* slab = smem + wave * (STAGE_BYTES / 2);
-      store_tile_bf16_lds(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane, acc, slab);
+      if (half)
+        store_tile_bf16_lds<2>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane, acc, slab);
+      else
+        store_tile_bf16_lds<TM>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane, acc, slab);
       // the next tile's first loads overwrite these arrays
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __syncthreads();
