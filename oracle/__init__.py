@@ -7,7 +7,9 @@ never touch it, and it shares no code with them: the arithmetic lives in
 module only marshals numpy arrays into it.
 
 What each function computes is stated, with the passages it follows, at the
-top of ``oracle.c``.  Parity is pinned against exact rational brute force,
+top of ``oracle.c``; ``apply_alpha_beta`` adds the scaled, accumulating form
+out = alpha * P + beta * C of every pass, combined in fp64 before the one
+rounding.  Parity is pinned against exact rational brute force,
 closed forms, the three-pass adjoint identity and numpy's float64 matmul in
 ``tests/test_oracle.py``; no function here is "parity unpinned".
 """
@@ -111,6 +113,34 @@ class Result:
         self.index = index          # the rows / pairs that were asked for
 
 
+def apply_alpha_beta(res: Result, alpha: float, beta: float, c_in=None) -> Result:
+    """The scaled, accumulating form of a pass: out = alpha * P + beta * C,
+    with P the grouped product the C oracle computed and C the output's prior
+    contents, combined in fp64 before the single rounding to the output type
+    -- fused accumulation, as opposed to adding an already rounded product
+    (TransformerEngine PR #3542, "Changes": explicit alpha/beta and fused
+    accumulation into fp32 outputs).  C is never read when beta == 0.
+
+    c_in: the prior output rows the result covers, same shape as res.value,
+    as bf16 bit patterns (uint16) or fp32 values.  S becomes |alpha| S +
+    |beta C| (the magnitude that bounds the rounding error).  Entries the
+    pass does not define (status 0) stay NaN."""
+    alpha = float(alpha)
+    beta = float(beta)
+    value = alpha * res.value
+    sabs = abs(alpha) * res.sabs
+    if beta != 0.0:
+        if c_in is None:
+            raise ValueError("beta != 0 needs the prior output c_in")
+        c = np.asarray(c_in)
+        c = decode_bf16(c) if c.dtype == np.uint16 else c.astype(np.float64)
+        assert c.shape == value.shape, (c.shape, value.shape)
+        ok = (res.status == 1)[:, None]
+        value = np.where(ok, value + beta * c, value)
+        sabs = np.where(ok, sabs + abs(beta) * np.abs(c), sabs)
+    return Result(value, sabs, res.status, res.index)
+
+
 def _run(fname, a, b, sel_arr, count, width, call_args):
     lib = _load()
     value = np.full((count, width), np.nan, dtype=np.float64)
@@ -124,10 +154,10 @@ def _run(fname, a, b, sel_arr, count, width, call_args):
     return value, sabs, status
 
 
-def forward(x, w, offs, rows=None) -> Result:
+def forward(x, w, offs, rows=None, alpha=1.0, beta=0.0, c_in=None) -> Result:
     """Y rows of the ragged forward (oracle_forward).  x: uint16 [M,K];
     w: uint16 [E,K,N]; offs: int32 [E] end offsets; rows: row indices or
-    None for all M rows."""
+    None for all M rows; alpha, beta, c_in: see apply_alpha_beta."""
     x, w = _u16(x), _u16(w)
     offs = np.ascontiguousarray(offs, dtype=np.int32)
     m, k = x.shape
@@ -138,10 +168,11 @@ def forward(x, w, offs, rows=None) -> Result:
     v, s, st = _run("oracle_forward", x, w, sel, count, n,
                     (_ptr(offs), ctypes.c_int64(m), ctypes.c_int64(k),
                      ctypes.c_int64(n), ctypes.c_int32(e)))
-    return Result(v, s, st, sel if sel is not None else np.arange(m))
+    res = Result(v, s, st, sel if sel is not None else np.arange(m))
+    return apply_alpha_beta(res, alpha, beta, c_in)
 
 
-def dgrad(dy, w, offs, rows=None) -> Result:
+def dgrad(dy, w, offs, rows=None, alpha=1.0, beta=0.0, c_in=None) -> Result:
     """dX rows of the ragged dgrad (oracle_dgrad).  dy: uint16 [M,N]."""
     dy, w = _u16(dy), _u16(w)
     offs = np.ascontiguousarray(offs, dtype=np.int32)
@@ -153,10 +184,11 @@ def dgrad(dy, w, offs, rows=None) -> Result:
     v, s, st = _run("oracle_dgrad", dy, w, sel, count, k,
                     (_ptr(offs), ctypes.c_int64(m), ctypes.c_int64(k),
                      ctypes.c_int64(n), ctypes.c_int32(e)))
-    return Result(v, s, st, sel if sel is not None else np.arange(m))
+    res = Result(v, s, st, sel if sel is not None else np.arange(m))
+    return apply_alpha_beta(res, alpha, beta, c_in)
 
 
-def wgrad(x, dy, offs, num_groups=None, pairs=None) -> Result:
+def wgrad(x, dy, offs, num_groups=None, pairs=None, alpha=1.0, beta=0.0, c_in=None) -> Result:
     """dW rows (expert g, k index kk) of the ragged wgrad (oracle_wgrad).
     pairs: int [P,2] of (g, kk), or None for all E*K rows in order."""
     x, dy = _u16(x), _u16(dy)
@@ -180,10 +212,10 @@ def wgrad(x, dy, offs, num_groups=None, pairs=None) -> Result:
         raise ValueError(f"oracle_wgrad rejected its arguments (code {rc})")
     idx = sel if sel is not None else np.stack(
         [np.repeat(np.arange(e), k), np.tile(np.arange(k), e)], axis=1)
-    return Result(value, sabs, status, idx)
+    return apply_alpha_beta(Result(value, sabs, status, idx), alpha, beta, c_in)
 
 
-def masked_forward(x, w, masked_m, rows=None) -> Result:
+def masked_forward(x, w, masked_m, rows=None, alpha=1.0, beta=0.0, c_in=None) -> Result:
     """Rows of the masked forward (oracle_masked_forward).  x: uint16
     [E, max_m, K]; rows: flat indices e*max_m + r, or None for all."""
     x, w = _u16(x), _u16(w)
@@ -196,4 +228,5 @@ def masked_forward(x, w, masked_m, rows=None) -> Result:
     v, s, st = _run("oracle_masked_forward", x, w, sel, count, n,
                     (_ptr(masked_m), ctypes.c_int64(max_m), ctypes.c_int64(k),
                      ctypes.c_int64(n), ctypes.c_int32(e)))
-    return Result(v, s, st, sel if sel is not None else np.arange(e * max_m))
+    res = Result(v, s, st, sel if sel is not None else np.arange(e * max_m))
+    return apply_alpha_beta(res, alpha, beta, c_in)

@@ -12,7 +12,10 @@
 * special cases equal to a library routine: numpy float64 matmul per expert,
   E = 1 is a dense GEMM, equal-size experts are a batched matmul, a fully
   active masked layout is a batched matmul;
-* the masked layout compacted into end offsets equals the ragged forward.
+* the masked layout compacted into end offsets equals the ragged forward;
+* alpha / beta: exact rational brute force of alpha * P + beta * C on every
+  pass, beta = 0 never reading C, alpha = 0 returning C, and accumulation
+  leaving an empty expert's dW unchanged.
 """
 import json
 import os
@@ -522,3 +525,112 @@ def test_sampled_rows_equal_full(oracle_lib):
     wpart = oracle.wgrad(x, dy, offs, pairs=pairs)
     for j, (g, kk) in enumerate(pairs):
         np.testing.assert_array_equal(wpart.value[j], wfull.value[g * wl.k + kk])
+
+
+# ---------------------------------------------------------------------------
+# alpha / beta: out = alpha * P + beta * C with one rounding (fused
+# accumulation; TransformerEngine PR #3542, "Changes")
+# ---------------------------------------------------------------------------
+
+ALPHA_BETA = [(1.0, 1.0), (-0.5, 2.0), (0.25, -1.0), (3.0, 0.5), (0.0, 1.0), (2.0, 0.0)]
+
+
+def _check_exact_ab(value, sabs, exact_num, c_vals, alpha, beta, length):
+    """fp64 oracle value vs the exact rational alpha * P + beta * C, then its
+    bf16 rounding vs the independent reference."""
+    for j in range(len(exact_num)):
+        q = Fraction(alpha) * Fraction(int(exact_num[j]), SCALE2)
+        if beta != 0.0:
+            q += Fraction(beta) * Fraction(float(c_vals[j]))
+        v = value[j]
+        assert abs(Fraction(v) - q) <= Fraction(length + 1) * Fraction(1, 2 ** 52) * Fraction(sabs[j]), (v, float(q))
+        assert oracle.round_bf16_scalar(v) == rne_bf16_reference(q) or q == 0
+
+
+@pytest.mark.parametrize("alpha,beta", ALPHA_BETA)
+@pytest.mark.parametrize("seed", range(6))
+def test_alpha_beta_exact(oracle_lib, seed, alpha, beta):
+    rng = np.random.default_rng(5000 + seed)
+    E = int(rng.integers(1, 5))
+    k = int(rng.choice([8, 16]))
+    n = int(rng.choice([8, 16]))
+    sizes = rng.integers(0, 9, E)
+    sizes[rng.random(E) < 0.3] = 0
+    used = int(sizes.sum())
+    m = max(used + int(rng.integers(0, 4)), 1)
+    offs = np.cumsum(sizes).astype(np.int32)
+    x = randn_bf16_bits(rng, (m, k))
+    w = randn_bf16_bits(rng, (E, k, n), std=0.5)
+    dy = randn_bf16_bits(rng, (m, n))
+    cy = randn_bf16_bits(rng, (m, n), std=4.0)          # prior Y (bf16 output)
+    cx = randn_bf16_bits(rng, (m, k), std=4.0)          # prior dX
+    cw = (rng.standard_normal((E * k, n)) * 3).astype(np.float32)   # prior dW (fp32 output)
+    y_ex, dx_ex, dw_ex = exact_ragged(x, w, dy, offs)
+    fw = oracle.forward(x, w, offs, alpha=alpha, beta=beta, c_in=cy)
+    dg = oracle.dgrad(dy, w, offs, alpha=alpha, beta=beta, c_in=cx)
+    wg = oracle.wgrad(x, dy, offs, alpha=alpha, beta=beta, c_in=cw)
+    for i in range(used):
+        _check_exact_ab(fw.value[i], fw.sabs[i], y_ex[i], dec(cy[i]), alpha, beta, k)
+        _check_exact_ab(dg.value[i], dg.sabs[i], dx_ex[i], dec(cx[i]), alpha, beta, n)
+    for i in range(used, m):
+        assert fw.status[i] == 0 and np.all(np.isnan(fw.value[i]))
+    dwv = wg.value.reshape(E, k, n)
+    dws = wg.sabs.reshape(E, k, n)
+    cwv = cw.reshape(E, k, n)
+    for g in range(E):
+        for kk in range(k):
+            _check_exact_ab(dwv[g, kk], dws[g, kk], dw_ex[g, kk], cwv[g, kk], alpha, beta,
+                            max(int(sizes[g]), 1))
+    # masked layout on the same numbers
+    max_m = int(max(int(sizes.max()), 1))
+    xm = np.full((E, max_m, k), 0x7FC0, dtype=np.uint16)
+    cm = np.full((E * max_m, n), 0x7FC0, dtype=np.uint16)
+    starts = np.concatenate([[0], offs[:-1]])
+    for g in range(E):
+        xm[g, :sizes[g]] = x[starts[g]:offs[g]]
+        cm[g * max_m:g * max_m + sizes[g]] = cy[starts[g]:offs[g]]
+    mk = oracle.masked_forward(xm, w, sizes.astype(np.int32), alpha=alpha, beta=beta, c_in=cm)
+    for g in range(E):
+        for r in range(int(sizes[g])):
+            flat = g * max_m + r
+            _check_exact_ab(mk.value[flat], mk.sabs[flat], y_ex[starts[g] + r], dec(cy[starts[g] + r]),
+                            alpha, beta, k)
+
+
+def test_beta_zero_never_reads_prior_output(oracle_lib):
+    rng = np.random.default_rng(77)
+    x = randn_bf16_bits(rng, (20, 16))
+    w = randn_bf16_bits(rng, (3, 16, 8))
+    offs = np.array([5, 5, 18], dtype=np.int32)
+    nan_c = np.full((20, 8), 0x7FC0, dtype=np.uint16)
+    a = oracle.forward(x, w, offs, alpha=-2.0, beta=0.0, c_in=nan_c)
+    b = oracle.forward(x, w, offs)
+    ok = b.status == 1
+    assert np.array_equal(a.value[ok], -2.0 * b.value[ok])
+    assert np.all(np.isfinite(a.value[ok]))
+
+
+def test_alpha_zero_beta_one_returns_prior_output(oracle_lib):
+    rng = np.random.default_rng(78)
+    x = randn_bf16_bits(rng, (20, 16))
+    dy = randn_bf16_bits(rng, (20, 8))
+    offs = np.array([5, 5, 18], dtype=np.int32)
+    c = (rng.standard_normal((3 * 16, 8)) * 5).astype(np.float32)
+    r = oracle.wgrad(x, dy, offs, alpha=0.0, beta=1.0, c_in=c)
+    assert np.array_equal(r.value, c.astype(np.float64))
+
+
+def test_accumulating_wgrad_keeps_empty_experts(oracle_lib):
+    """dW[g] += X_g^T dY_g: an expert with no rows keeps its prior dW."""
+    rng = np.random.default_rng(79)
+    x = randn_bf16_bits(rng, (12, 8))
+    dy = randn_bf16_bits(rng, (12, 8))
+    offs = np.array([0, 7, 7, 12], dtype=np.int32)
+    c = (rng.standard_normal((4 * 8, 8))).astype(np.float32)
+    acc = oracle.wgrad(x, dy, offs, alpha=1.0, beta=1.0, c_in=c).value.reshape(4, 8, 8)
+    plain = oracle.wgrad(x, dy, offs).value.reshape(4, 8, 8)
+    cc = c.astype(np.float64).reshape(4, 8, 8)
+    for g in (0, 2):
+        assert np.array_equal(acc[g], cc[g])
+    for g in (1, 3):
+        assert np.allclose(acc[g], plain[g] + cc[g], rtol=0, atol=1e-12)
