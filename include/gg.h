@@ -29,8 +29,8 @@
  *    device clamps them: end(g) = min(max(offs[g], end(g-1)), M) and
  *    active(e) = min(max(masked_m[e], 0), max_m).  Bad values therefore give
  *    empty or shortened experts, never an out-of-range access or a hang.
- *  - Outputs are overwritten (alpha = 1, beta = 0): an output element is
- *    written without being read.  Elements the operation does not define
+ *  - Outputs are overwritten (alpha = 1, beta = 0; the *_ex forms below
+ *    take other values): an output element is written without being read.  Elements the operation does not define
  *    are left untouched (TransformerEngine PR #3542, "Changes": unused
  *    capacity of caller-owned outputs is preserved; TileOPs issue #1566,
  *    "Summary": no output memset).
@@ -131,6 +131,41 @@ gg_status gg_masked_forward(const void* x, const void* w,
                             const int32_t* masked_m, void* y,
                             gg_dtype y_dtype, int64_t max_m, int64_t k,
                             int64_t n, int32_t num_groups, void* stream);
+
+/*
+ * Scaled and accumulating forms of the four passes:
+ *
+ *   out = alpha * P + beta * out          (P = the pass's grouped product)
+ *
+ * over exactly the elements the plain entry point writes (rows of experts;
+ * all of dW).  The combination happens in fp32 before the single rounding to
+ * the output type -- fused accumulation, so accumulating into an fp32
+ * main-grad (wgrad with beta = 1) loses nothing to an intermediate bf16
+ * round (TransformerEngine PR #3542, "Changes": explicit alpha/beta and fused
+ * accumulation into fp32 outputs are a distinct mode of the grouped GEMM).
+ * When beta == 0 the output is not read (NaN in it is overwritten), and
+ * alpha = 1, beta = 0 is the plain entry point.  When beta != 0 every element
+ * written is read first; an expert with no rows gets beta * dW[g] in wgrad.
+ * alpha and beta are IEEE fp32: NaN and infinity propagate.  Arguments,
+ * layouts, ownership and errors are those of the plain entry point.
+ */
+gg_status gg_forward_ex(const void* x, const void* w, const int32_t* offs,
+                        void* y, gg_dtype y_dtype, int64_t m, int64_t k,
+                        int64_t n, int32_t num_groups, float alpha,
+                        float beta, void* stream);
+gg_status gg_dgrad_ex(const void* dy, const void* w, const int32_t* offs,
+                      void* dx, gg_dtype dx_dtype, int64_t m, int64_t k,
+                      int64_t n, int32_t num_groups, float alpha, float beta,
+                      void* stream);
+gg_status gg_wgrad_ex(const void* x, const void* dy, const int32_t* offs,
+                      void* dw, gg_dtype dw_dtype, int64_t m, int64_t k,
+                      int64_t n, int32_t num_groups, float alpha, float beta,
+                      void* stream);
+gg_status gg_masked_forward_ex(const void* x, const void* w,
+                               const int32_t* masked_m, void* y,
+                               gg_dtype y_dtype, int64_t max_m, int64_t k,
+                               int64_t n, int32_t num_groups, float alpha,
+                               float beta, void* stream);
 
 /* Static description of a status code. */
 const char* gg_status_str(gg_status s);

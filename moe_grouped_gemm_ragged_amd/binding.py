@@ -66,6 +66,11 @@ def load():
         f = getattr(lib, name)
         f.argtypes = sig
         f.restype = ctypes.c_int
+    sig_ex = sig[:-1] + [ctypes.c_float, ctypes.c_float, P]
+    for name in ("gg_forward_ex", "gg_dgrad_ex", "gg_wgrad_ex", "gg_masked_forward_ex"):
+        f = getattr(lib, name)
+        f.argtypes = sig_ex
+        f.restype = ctypes.c_int
     lib.gg_status_str.argtypes = [ctypes.c_int]
     lib.gg_status_str.restype = ctypes.c_char_p
     lib.gg_last_error.argtypes = []
@@ -131,18 +136,33 @@ def _stream_handle(device) -> int:
     return int(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _invoke(name, a, b, groups, out, out_code, m, k, n, e, device):
-    rc = call_raw(name, a.data_ptr(), b.data_ptr(), groups.data_ptr(), out.data_ptr(), out_code,
-                  int(m), int(k), int(n), int(e), _stream_handle(device))
+def _invoke(name, a, b, groups, out, out_code, m, k, n, e, device, alpha=1.0, beta=0.0):
+    """Calls the plain entry point, or its *_ex form when alpha != 1 or
+    beta != 0."""
+    if float(alpha) == 1.0 and float(beta) == 0.0:
+        rc = call_raw(name, a.data_ptr(), b.data_ptr(), groups.data_ptr(), out.data_ptr(), out_code,
+                      int(m), int(k), int(n), int(e), _stream_handle(device))
+    else:
+        name = name + "_ex"
+        rc = call_raw(name, a.data_ptr(), b.data_ptr(), groups.data_ptr(), out.data_ptr(), out_code,
+                      int(m), int(k), int(n), int(e), float(alpha), float(beta), _stream_handle(device))
     if rc != 0:
         raise GGError(name, rc, last_error())
 
 
-def forward(x, w, offs, out: Optional["torch.Tensor"] = None, out_dtype=None):
+def _need_out(out, beta):
+    if float(beta) != 0.0 and out is None:
+        raise ValueError("beta != 0 accumulates into `out`, which must be given")
+
+
+def forward(x, w, offs, out: Optional["torch.Tensor"] = None, out_dtype=None, alpha=1.0, beta=0.0):
     """Y[rows of g] = X[rows of g] . W[g] (gg_forward).  x: bf16 [m,k];
     w: bf16 [E,k,n]; offs: int32 [E] cumulative end offsets on the device.
-    Rows of ``out`` at or past offs[-1] are left untouched."""
+    Rows of ``out`` at or past offs[-1] are left untouched.  With alpha /
+    beta, the written rows become alpha * product + beta * out
+    (gg_forward_ex)."""
     torch = _torch()
+    _need_out(out, beta)
     dev = x.device
     _check(x, "x", torch.bfloat16, 2, dev)
     _check(w, "w", torch.bfloat16, 3, dev)
@@ -156,13 +176,15 @@ def forward(x, w, offs, out: Optional["torch.Tensor"] = None, out_dtype=None):
     _check(out, "out", out.dtype, 2, dev)
     if tuple(out.shape) != (m, n):
         raise ValueError(f"out must be [{m}, {n}]")
-    _invoke("gg_forward", x, w, offs, out, _dtype_code(out.dtype), m, k, n, e, dev)
+    _invoke("gg_forward", x, w, offs, out, _dtype_code(out.dtype), m, k, n, e, dev, alpha, beta)
     return out
 
 
-def dgrad(dy, w, offs, out=None, out_dtype=None):
-    """dX[rows of g] = dY[rows of g] . W[g]^T (gg_dgrad).  dy: bf16 [m,n]."""
+def dgrad(dy, w, offs, out=None, out_dtype=None, alpha=1.0, beta=0.0):
+    """dX[rows of g] = dY[rows of g] . W[g]^T (gg_dgrad).  dy: bf16 [m,n].
+    alpha / beta as in forward (gg_dgrad_ex)."""
     torch = _torch()
+    _need_out(out, beta)
     dev = dy.device
     _check(dy, "dy", torch.bfloat16, 2, dev)
     _check(w, "w", torch.bfloat16, 3, dev)
@@ -176,14 +198,16 @@ def dgrad(dy, w, offs, out=None, out_dtype=None):
     _check(out, "out", out.dtype, 2, dev)
     if tuple(out.shape) != (m, k):
         raise ValueError(f"out must be [{m}, {k}]")
-    _invoke("gg_dgrad", dy, w, offs, out, _dtype_code(out.dtype), m, k, n, e, dev)
+    _invoke("gg_dgrad", dy, w, offs, out, _dtype_code(out.dtype), m, k, n, e, dev, alpha, beta)
     return out
 
 
-def wgrad(x, dy, offs, out=None, out_dtype=None):
+def wgrad(x, dy, offs, out=None, out_dtype=None, alpha=1.0, beta=0.0):
     """dW[g] = X[rows of g]^T . dY[rows of g] for every expert (gg_wgrad);
-    all of ``out`` [E,k,n] is written, empty experts get +0.0."""
+    all of ``out`` [E,k,n] is written, empty experts get +0.0.  beta = 1
+    accumulates into ``out`` (e.g. an fp32 main-grad; gg_wgrad_ex)."""
     torch = _torch()
+    _need_out(out, beta)
     dev = x.device
     _check(x, "x", torch.bfloat16, 2, dev)
     _check(dy, "dy", torch.bfloat16, 2, dev)
@@ -198,14 +222,16 @@ def wgrad(x, dy, offs, out=None, out_dtype=None):
     _check(out, "out", out.dtype, 3, dev)
     if tuple(out.shape) != (e, k, n):
         raise ValueError(f"out must be [{e}, {k}, {n}]")
-    _invoke("gg_wgrad", x, dy, offs, out, _dtype_code(out.dtype), m, k, n, e, dev)
+    _invoke("gg_wgrad", x, dy, offs, out, _dtype_code(out.dtype), m, k, n, e, dev, alpha, beta)
     return out
 
 
-def masked_forward(x, w, masked_m, out=None, out_dtype=None):
+def masked_forward(x, w, masked_m, out=None, out_dtype=None, alpha=1.0, beta=0.0):
     """Y[e, r] = X[e, r] . W[e] for r < masked_m[e] (gg_masked_forward).
-    x: bf16 [E, max_m, k]; inactive rows are neither read nor written."""
+    x: bf16 [E, max_m, k]; inactive rows are neither read nor written.
+    alpha / beta as in forward (gg_masked_forward_ex)."""
     torch = _torch()
+    _need_out(out, beta)
     dev = x.device
     _check(x, "x", torch.bfloat16, 3, dev)
     _check(w, "w", torch.bfloat16, 3, dev)
@@ -219,5 +245,6 @@ def masked_forward(x, w, masked_m, out=None, out_dtype=None):
     _check(out, "out", out.dtype, 3, dev)
     if tuple(out.shape) != (e, max_m, n):
         raise ValueError(f"out must be [{e}, {max_m}, {n}]")
-    _invoke("gg_masked_forward", x, w, masked_m, out, _dtype_code(out.dtype), max_m, k, n, e, dev)
+    _invoke("gg_masked_forward", x, w, masked_m, out, _dtype_code(out.dtype), max_m, k, n, e, dev,
+            alpha, beta)
     return out

@@ -73,11 +73,11 @@ gg_status check(const void* p0, const void* p1, const void* groups, const void* 
 }
 
 gg_status run(int mode, const void* a, const void* b, const int32_t* groups, void* c, gg_dtype dt,
-              int64_t m, int64_t k, int64_t n, int32_t E, void* stream) {
+              int64_t m, int64_t k, int64_t n, int32_t E, float alpha, float beta, void* stream) {
   int cus = 0;
   gg_status s = device_cus(&cus);
   if (s != GG_OK) return s;
-  hipError_t e = gg::launch(mode, a, b, groups, c, dt == GG_F32, m, k, n, E, cus,
+  hipError_t e = gg::launch(mode, a, b, groups, c, dt == GG_F32, m, k, n, E, alpha, beta, cus,
                             static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_error = std::string("kernel launch: ") + hipGetErrorString(e);
@@ -87,39 +87,70 @@ gg_status run(int mode, const void* a, const void* b, const int32_t* groups, voi
   return GG_OK;
 }
 
+gg_status masked_rows(int64_t max_m, int32_t E) {
+  if ((double)E * (double)max_m > 2147483647.0)
+    return fail(GG_ERR_BAD_DIM, "num_groups * max_m exceeds 2^31 - 1");
+  return GG_OK;
+}
+
 }  // namespace
 
 extern "C" {
 
-gg_status gg_forward(const void* x, const void* w, const int32_t* offs, void* y, gg_dtype y_dtype,
-                     int64_t m, int64_t k, int64_t n, int32_t num_groups, void* stream) {
+gg_status gg_forward_ex(const void* x, const void* w, const int32_t* offs, void* y, gg_dtype y_dtype,
+                        int64_t m, int64_t k, int64_t n, int32_t num_groups, float alpha,
+                        float beta, void* stream) {
   gg_status s = check(x, w, offs, y, y_dtype, m, k, n, num_groups);
   if (s != GG_OK) return s;
-  return run(0, x, w, offs, y, y_dtype, m, k, n, num_groups, stream);
+  return run(0, x, w, offs, y, y_dtype, m, k, n, num_groups, alpha, beta, stream);
+}
+
+gg_status gg_dgrad_ex(const void* dy, const void* w, const int32_t* offs, void* dx, gg_dtype dx_dtype,
+                      int64_t m, int64_t k, int64_t n, int32_t num_groups, float alpha, float beta,
+                      void* stream) {
+  gg_status s = check(dy, w, offs, dx, dx_dtype, m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  return run(1, dy, w, offs, dx, dx_dtype, m, k, n, num_groups, alpha, beta, stream);
+}
+
+gg_status gg_wgrad_ex(const void* x, const void* dy, const int32_t* offs, void* dw, gg_dtype dw_dtype,
+                      int64_t m, int64_t k, int64_t n, int32_t num_groups, float alpha, float beta,
+                      void* stream) {
+  gg_status s = check(x, dy, offs, dw, dw_dtype, m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  return run(2, x, dy, offs, dw, dw_dtype, m, k, n, num_groups, alpha, beta, stream);
+}
+
+gg_status gg_masked_forward_ex(const void* x, const void* w, const int32_t* masked_m, void* y,
+                               gg_dtype y_dtype, int64_t max_m, int64_t k, int64_t n,
+                               int32_t num_groups, float alpha, float beta, void* stream) {
+  gg_status s = check(x, w, masked_m, y, y_dtype, max_m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  s = masked_rows(max_m, num_groups);
+  if (s != GG_OK) return s;
+  return run(3, x, w, masked_m, y, y_dtype, max_m, k, n, num_groups, alpha, beta, stream);
+}
+
+gg_status gg_forward(const void* x, const void* w, const int32_t* offs, void* y, gg_dtype y_dtype,
+                     int64_t m, int64_t k, int64_t n, int32_t num_groups, void* stream) {
+  return gg_forward_ex(x, w, offs, y, y_dtype, m, k, n, num_groups, 1.0f, 0.0f, stream);
 }
 
 gg_status gg_dgrad(const void* dy, const void* w, const int32_t* offs, void* dx, gg_dtype dx_dtype,
                    int64_t m, int64_t k, int64_t n, int32_t num_groups, void* stream) {
-  gg_status s = check(dy, w, offs, dx, dx_dtype, m, k, n, num_groups);
-  if (s != GG_OK) return s;
-  return run(1, dy, w, offs, dx, dx_dtype, m, k, n, num_groups, stream);
+  return gg_dgrad_ex(dy, w, offs, dx, dx_dtype, m, k, n, num_groups, 1.0f, 0.0f, stream);
 }
 
 gg_status gg_wgrad(const void* x, const void* dy, const int32_t* offs, void* dw, gg_dtype dw_dtype,
                    int64_t m, int64_t k, int64_t n, int32_t num_groups, void* stream) {
-  gg_status s = check(x, dy, offs, dw, dw_dtype, m, k, n, num_groups);
-  if (s != GG_OK) return s;
-  return run(2, x, dy, offs, dw, dw_dtype, m, k, n, num_groups, stream);
+  return gg_wgrad_ex(x, dy, offs, dw, dw_dtype, m, k, n, num_groups, 1.0f, 0.0f, stream);
 }
 
 gg_status gg_masked_forward(const void* x, const void* w, const int32_t* masked_m, void* y,
                             gg_dtype y_dtype, int64_t max_m, int64_t k, int64_t n,
                             int32_t num_groups, void* stream) {
-  gg_status s = check(x, w, masked_m, y, y_dtype, max_m, k, n, num_groups);
-  if (s != GG_OK) return s;
-  if ((double)num_groups * (double)max_m > 2147483647.0)
-    return fail(GG_ERR_BAD_DIM, "num_groups * max_m exceeds 2^31 - 1");
-  return run(3, x, w, masked_m, y, y_dtype, max_m, k, n, num_groups, stream);
+  return gg_masked_forward_ex(x, w, masked_m, y, y_dtype, max_m, k, n, num_groups, 1.0f, 0.0f,
+                              stream);
 }
 
 const char* gg_status_str(gg_status s) {

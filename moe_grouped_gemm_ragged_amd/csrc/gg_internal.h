@@ -9,9 +9,10 @@
 
 namespace gg {
 // mode: 0 forward, 1 dgrad, 2 wgrad, 3 masked forward.  Arguments were
-// validated by the caller.  Launches one persistent grid of at most
-// num_cus workgroups on `stream`.
+// validated by the caller.  Writes alpha * product + beta * (prior output)
+// (the prior output is not read when beta == 0).  Launches one persistent
+// grid of at most num_cus workgroups on `stream`.
 hipError_t launch(int mode, const void* a, const void* b, const int32_t* groups, void* c,
                   bool out_f32, int64_t m, int64_t k, int64_t n, int32_t num_groups,
-                  int num_cus, hipStream_t stream);
+                  float alpha, float beta, int num_cus, hipStream_t stream);
 }  // namespace gg

@@ -91,6 +91,8 @@ struct Params {
   int64_t k;
   int64_t n;
   int32_t num_groups;
+  float alpha;              // out = alpha * product + beta * out
+  float beta;               // (the output is not read when beta == 0)
 };
 
 // One operand tile: element (tile row r, reduction index q) of the tile
@@ -475,29 +477,39 @@ __device__ __forceinline__ void store_tile_f32(uint8_t* cbase, uint32_t ldc_byte
   }
 }
 
-// bf16 output through LDS.  Packing to bf16 needs the values in ordinary
+// Output through LDS: the bf16 epilogue, and the scaled form (alpha, beta)
+// of either output type.  Packing or combining needs the values in ordinary
 // registers; moving all 128 accumulators there at once overflows them, so
 // each wave instead writes one 32 x 64 fp32 slab (block row i) from its
 // accumulator registers into its own LDS region (rows padded by 16 bytes so
-// the 16 rows a write touches fall on distinct banks), reads back 8
-// consecutive values per lane, packs them and stores 16 bytes per lane --
-// 8 lanes cover the 128 contiguous bytes of a slab row in the output.  Row
-// and column predication as in store_tile_f32.  `slab` is this wave's LDS region
-// (>= 32 * 272 bytes), free for the epilogue.
+// the 16 rows a write touches fall on distinct banks) and reads back 8
+// consecutive values per lane.  Those become alpha * v + beta * c, with c the
+// 8 prior output values of the same elements (read only when beta != 0,
+// through the same range-checked resource: out of range reads as zero),
+// then one rounding to the output type; 8 lanes cover a slab row's 64
+// contiguous output columns.  Row and column predication as in
+// store_tile_f32.  `slab` is this wave's LDS region (>= 32 * 272 bytes),
+// free for the epilogue.
 constexpr int kSlabPitch = 64 * 4 + 16;
 
-template <int TMA>
-__device__ __forceinline__ void store_tile_bf16_lds(uint8_t* cbase, uint32_t ldc_bytes, int rows,
-                                                    int cols, int wm, int wn, int lane,
-                                                    const floatx16 (&acc)[TM][TN], uint8_t* slab) {
-  const uint32_t nrec = (uint32_t)(rows - 1) * ldc_bytes + (uint32_t)cols * 2u;
+template <int TMA, bool OUT_F32, bool SCALED>
+__device__ __forceinline__ void store_tile_lds(uint8_t* cbase, uint32_t ldc_bytes, int rows, int cols,
+                                               int wm, int wn, int lane, const floatx16 (&acc)[TM][TN],
+                                               uint8_t* slab, float alpha, float beta) {
+  constexpr uint32_t esz = OUT_F32 ? 4 : 2;
+  const uint32_t nrec = (uint32_t)(rows - 1) * ldc_bytes + (uint32_t)cols * esz;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(cbase, nrec);
-  const int wrow = lane & 31;                 // slab row this lane writes
-  const int wcol = 4 * (lane >> 5);           // first of its 4 columns in each 8-column group
-  const int rcol8 = 8 * (lane & 7);           // read: 8 consecutive columns ...
-  const int rrow = lane >> 3;                 // ... of slab rows rrow + 8 q
-  const int gcol = 64 * wn + rcol8;
+  // Lane-dependent offsets, recomputed per call rather than hoisted out of
+  // the tile loop (where they would stay live across the main loop):
+  // write: slab row l % 32, its 4 columns 4 (l / 32) of each 8-column group;
+  // read: 8 consecutive columns 8 (l % 8) of slab rows l / 8 + 8 q.
+  const uint32_t wslab = opaque_v((uint32_t)((lane & 31) * kSlabPitch + 16 * (lane >> 5)));
+  const uint32_t rslab = opaque_v((uint32_t)((lane >> 3) * kSlabPitch + 32 * (lane & 7)));
+  const int gcol = 64 * wn + 8 * (lane & 7);
   const bool col_ok = gcol < cols;
+  const uint32_t gbase = col_ok ? opaque_v((uint32_t)(32 * TMA * wm + (lane >> 3)) * ldc_bytes +
+                                           (uint32_t)gcol * esz)
+                                : kOutOfRange;
 #pragma unroll
   for (int i = 0; i < TMA; ++i) {
 #pragma unroll
@@ -505,19 +517,46 @@ __device__ __forceinline__ void store_tile_bf16_lds(uint8_t* cbase, uint32_t ldc
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
         floatx4 v = {acc[i][j][4 * rr + 0], acc[i][j][4 * rr + 1], acc[i][j][4 * rr + 2], acc[i][j][4 * rr + 3]};
-        *reinterpret_cast<floatx4*>(slab + wrow * kSlabPitch + 4 * (32 * j + 8 * rr + wcol)) = v;
+        *reinterpret_cast<floatx4*>(slab + wslab + 4 * (32 * j + 8 * rr)) = v;
       }
     // LDS operations of one wave complete in order: the reads see the writes.
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const int r = rrow + 8 * q;
-      const floatx4 lo = *reinterpret_cast<const floatx4*>(slab + r * kSlabPitch + 4 * rcol8);
-      const floatx4 hi = *reinterpret_cast<const floatx4*>(slab + r * kSlabPitch + 4 * rcol8 + 16);
-      u32x4 o = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
-                 pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
-      uint32_t voff = (uint32_t)(32 * TMA * wm + 32 * i + r) * ldc_bytes + (uint32_t)gcol * 2u;
-      if (!col_ok) voff = kOutOfRange;
-      __builtin_amdgcn_raw_buffer_store_b128(o, rs, voff, 0, 0);
+      floatx4 lo = *reinterpret_cast<const floatx4*>(slab + rslab + 8 * q * kSlabPitch);
+      floatx4 hi = *reinterpret_cast<const floatx4*>(slab + rslab + 8 * q * kSlabPitch + 16);
+      // rows 32 TMA wm + 32 i + l / 8 + 8 q (out of range stays out of range)
+      const uint32_t voff = gbase + (uint32_t)(32 * i + 8 * q) * ldc_bytes;
+      if constexpr (SCALED) {
+        lo = lo * alpha;
+        hi = hi * alpha;
+        if (beta != 0.0f) {
+          floatx4 clo, chi;
+          if constexpr (OUT_F32) {
+            clo = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+            chi = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16, 0, 0));
+          } else {
+            // 8 bf16 values: each is the high half of its fp32 pattern
+            const u32x4 c = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, voff, 0, 0));
+            clo = floatx4{__builtin_bit_cast(float, c[0] << 16), __builtin_bit_cast(float, c[0] & 0xFFFF0000u),
+                          __builtin_bit_cast(float, c[1] << 16), __builtin_bit_cast(float, c[1] & 0xFFFF0000u)};
+            chi = floatx4{__builtin_bit_cast(float, c[2] << 16), __builtin_bit_cast(float, c[2] & 0xFFFF0000u),
+                          __builtin_bit_cast(float, c[3] << 16), __builtin_bit_cast(float, c[3] & 0xFFFF0000u)};
+          }
+          lo = lo + clo * beta;
+          hi = hi + chi * beta;
+        }
+      }
+      if constexpr (OUT_F32) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), rs, voff, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), rs, voff + 16, 0, 0);
+      } else {
+        u32x4 o = {pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                   pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(o, rs, voff, 0, 0);
+      }
+      // one slab row group at a time (hoisting the prior-output loads of
+      // all four would need 32 more registers)
+      if constexpr (SCALED) __builtin_amdgcn_sched_barrier(0);
     }
     // the next block row rewrites the slab: wait for this row's reads
     __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
@@ -797,6 +836,9 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   decode_tile(blockIdx.x, cur);
   issue_prologue(cur);
   int prev_stores = 0;    // fp32 stores issued after the current tile's prologue loads
+  // The scaled form (alpha != 1 or beta != 0) goes through the LDS epilogue
+  // for both output types.
+  const bool scaled = p.alpha != 1.0f || p.beta != 0.0f;
   for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
     floatx16 acc[TM][TN];
 #pragma unroll
@@ -820,7 +862,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
                                          smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
                                          cur.B, tid, wave, faa, fab, acc, prev_stores);
     const int64_t tn = t + gridDim.x;
-    if constexpr (OUT_F32) {
+    if (OUT_F32 && !scaled) {
       // Every wave is done reading this tile's stages: issue the next
       // tile's prologue loads first, then this tile's stores, so the
       // stores drain while those loads are in flight.  (Loads of stages
@@ -845,10 +887,22 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
       stage_barrier();
       // each wave stages through its own 16 KB of the (idle) stage buffers
       uint8_t* slab = smem + wave * (STAGE_BYTES / 2);
-      if (half)
-        store_tile_bf16_lds<2>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane, acc, slab);
-      else
-        store_tile_bf16_lds<TM>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane, acc, slab);
+      if (scaled) {
+        if (half)
+          store_tile_lds<2, OUT_F32, true>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane,
+                                           acc, slab, p.alpha, p.beta);
+        else
+          store_tile_lds<TM, OUT_F32, true>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane,
+                                            acc, slab, p.alpha, p.beta);
+      } else if constexpr (!OUT_F32) {
+        if (half)
+          store_tile_lds<2, false, false>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane,
+                                          acc, slab, 1.0f, 0.0f);
+        else
+          store_tile_lds<TM, false, false>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane,
+                                           acc, slab, 1.0f, 0.0f);
+      }
+      prev_stores = 0;
       // the next tile's first loads overwrite these arrays
       __builtin_amdgcn_s_waitcnt(0xC07F);
       __syncthreads();
@@ -884,7 +938,7 @@ static int64_t max_tiles(int mode, int64_t m, int64_t k, int64_t n, int64_t E) {
 
 hipError_t launch(int mode, const void* a, const void* b, const int32_t* groups, void* c,
                   bool out_f32, int64_t m, int64_t k, int64_t n, int32_t num_groups,
-                  int num_cus, hipStream_t stream) {
+                  float alpha, float beta, int num_cus, hipStream_t stream) {
   Params p;
   p.a = static_cast<const uint16_t*>(a);
   p.b = static_cast<const uint16_t*>(b);
@@ -894,6 +948,8 @@ hipError_t launch(int mode, const void* a, const void* b, const int32_t* groups,
   p.k = k;
   p.n = n;
   p.num_groups = num_groups;
+  p.alpha = alpha;
+  p.beta = beta;
   const int64_t tiles = max_tiles(mode, m, k, n, num_groups);
   if (tiles <= 0) return hipSuccess;
   const int grid = (int)(tiles < num_cus ? tiles : num_cus);

@@ -80,3 +80,31 @@ def test_binding_rejects_bad_tensors():
         gg.forward(x, w, offs)
     with pytest.raises(ValueError):
         gg.forward(torch.zeros(8, 16, dtype=torch.bfloat16), w, offs)
+
+
+EX_ENTRY = [e + "_ex" for e in ENTRY]
+
+
+def call_ex(name, alpha=1.0, beta=0.0, **kw):
+    v = dict(OK, **kw)
+    return gg.call_raw(name, v["a"], v["b"], v["g"], v["c"], v["dt"], v["m"], v["k"], v["n"],
+                       v["e"], alpha, beta, v["s"])
+
+
+@pytest.mark.parametrize("name", EX_ENTRY)
+@pytest.mark.parametrize("case,status", [
+    (dict(a=0), 1), (dict(c=0), 1), (dict(k=12), 2), (dict(n=0), 2), (dict(c=A + 4), 3),
+    (dict(dt=5), 4), (dict(e=0), 5), (dict(e=4096), 5),
+])
+def test_scaled_entry_points_check_like_the_plain_ones(lib, name, case, status):
+    rc = call_ex(name, 0.5, 1.0, **case)
+    assert rc == status, (name, case, rc, gg.last_error())
+
+
+def test_binding_needs_out_to_accumulate():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(8, 8, dtype=torch.bfloat16)
+    dy = torch.zeros(8, 8, dtype=torch.bfloat16)
+    offs = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        gg.wgrad(x, dy, offs, beta=1.0)
