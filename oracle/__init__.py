@@ -52,7 +52,7 @@ def _load():
     I32 = ctypes.c_int32
     sig = [P, P, P, I64, I64, I64, I32, P, I64, P, P, P]
     for name in ("oracle_forward", "oracle_dgrad", "oracle_wgrad",
-                 "oracle_masked_forward"):
+                 "oracle_masked_forward", "oracle_masked_dgrad", "oracle_masked_wgrad"):
         f = getattr(lib, name)
         f.argtypes = sig
         f.restype = ctypes.c_int
@@ -230,3 +230,47 @@ def masked_forward(x, w, masked_m, rows=None, alpha=1.0, beta=0.0, c_in=None) ->
                      ctypes.c_int64(n), ctypes.c_int32(e)))
     res = Result(v, s, st, sel if sel is not None else np.arange(e * max_m))
     return apply_alpha_beta(res, alpha, beta, c_in)
+
+
+def masked_dgrad(dy, w, masked_m, rows=None, alpha=1.0, beta=0.0, c_in=None) -> Result:
+    """Rows of the masked dgrad (oracle_masked_dgrad).  dy: uint16
+    [E, max_m, N]; w: uint16 [E, K, N]; rows: flat indices e*max_m + r, or
+    None for all; the result rows are dX[e, r, :K]."""
+    dy, w = _u16(dy), _u16(w)
+    masked_m = np.ascontiguousarray(masked_m, dtype=np.int32)
+    e, max_m, n = dy.shape
+    e2, k, n2 = w.shape
+    assert e2 == e and n2 == n and masked_m.shape == (e,)
+    sel = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    count = e * max_m if sel is None else len(sel)
+    v, s, st = _run("oracle_masked_dgrad", dy, w, sel, count, k,
+                    (_ptr(masked_m), ctypes.c_int64(max_m), ctypes.c_int64(k),
+                     ctypes.c_int64(n), ctypes.c_int32(e)))
+    res = Result(v, s, st, sel if sel is not None else np.arange(e * max_m))
+    return apply_alpha_beta(res, alpha, beta, c_in)
+
+
+def masked_wgrad(x, dy, masked_m, pairs=None, alpha=1.0, beta=0.0, c_in=None) -> Result:
+    """dW rows (expert e, k index kk) of the masked wgrad
+    (oracle_masked_wgrad).  x: uint16 [E, max_m, K]; dy: uint16
+    [E, max_m, N]; pairs: int [P, 2] of (e, kk), or None for all E*K rows."""
+    x, dy = _u16(x), _u16(dy)
+    masked_m = np.ascontiguousarray(masked_m, dtype=np.int32)
+    e, max_m, k = x.shape
+    e2, max_m2, n = dy.shape
+    assert e2 == e and max_m2 == max_m and masked_m.shape == (e,)
+    sel = None if pairs is None else np.ascontiguousarray(pairs, dtype=np.int64).reshape(-1, 2)
+    count = e * k if sel is None else len(sel)
+    lib = _load()
+    value = np.full((count, n), np.nan, dtype=np.float64)
+    sabs = np.full((count, n), np.nan, dtype=np.float64)
+    status = np.zeros(count, dtype=np.int32)
+    rc = lib.oracle_masked_wgrad(_ptr(x), _ptr(dy), _ptr(masked_m), ctypes.c_int64(max_m),
+                                 ctypes.c_int64(k), ctypes.c_int64(n), ctypes.c_int32(e),
+                                 _ptr(sel), ctypes.c_int64(0 if sel is None else len(sel)),
+                                 _ptr(value), _ptr(sabs), _ptr(status))
+    if rc != 0:
+        raise ValueError(f"oracle_masked_wgrad rejected its arguments (code {rc})")
+    idx = sel if sel is not None else np.stack(
+        [np.repeat(np.arange(e), k), np.tile(np.arange(k), e)], axis=1)
+    return apply_alpha_beta(Result(value, sabs, status, idx), alpha, beta, c_in)

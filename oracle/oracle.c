@@ -21,7 +21,9 @@
  *  - Masked layout (sglang PR #32385, "Evidence", reproduction and operand
  *    table): A[E, max_m, K], W[E, K, N], D[E, max_m, N] and a per-expert
  *    count masked_m[e]; rows r < masked_m[e] of expert e are active, the rest
- *    are inactive and neither read nor written.
+ *    are inactive and neither read nor written.  Its backward on the same
+ *    layout: dX[e, r] = dY[e, r] W[e]^T on active rows and dW[e] = X[e]^T
+ *    dY[e] over active rows (+0.0 for an expert with none).
  *
  * Readings taken where the pages are silent:
  *  - Offsets are clamped into a monotone sequence, end(g) = min(max(offs[g],
@@ -249,6 +251,87 @@ int oracle_masked_forward(const uint16_t* x, const uint16_t* w,
             for (int64_t j = 0; j < n; ++j) {
                 double p = a * bf16_decode(we[kk * n + j]);
                 yr[j] += p;
+                sr[j] += fabs(p);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Active rows of expert e in the masked layout: masked_m[e] clamped into
+ * [0, max_m]. */
+static int64_t masked_active(const int32_t* masked_m, int64_t e, int64_t max_m) {
+    int64_t a = masked_m[e];
+    if (a < 0) a = 0;
+    if (a > max_m) a = max_m;
+    return a;
+}
+
+/* ---- masked dgrad: dX[e, r, :] = dY[e, r, :] . W[e]^T, r < masked_m[e] ---- */
+/* The backward of the masked forward through its activation: inactive rows
+ * of dY are never read and of dX never written (sglang PR #32385, "Cause":
+ * consumers of the masked layout must not depend on inactive rows).
+ * rows: flat indices e*max_m + r; NULL = all E*max_m. */
+int oracle_masked_dgrad(const uint16_t* dy, const uint16_t* w,
+                        const int32_t* masked_m, int64_t max_m, int64_t k,
+                        int64_t n, int32_t num_groups,
+                        const int64_t* rows, int64_t nrows,
+                        double* dx, double* s, int32_t* status) {
+    if (num_groups < 1) return -1;
+    int64_t total = (int64_t)num_groups * max_m;
+    int64_t count = rows ? nrows : total;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < count; ++r) {
+        int64_t flat = rows ? rows[r] : r;
+        int ok = flat >= 0 && flat < total;
+        int64_t e = ok ? flat / max_m : 0, row = ok ? flat % max_m : 0;
+        if (ok) ok = row < masked_active(masked_m, e, max_m);
+        status[r] = ok;
+        if (!ok) continue;
+        const uint16_t* we = w + e * k * n;
+        const uint16_t* dyr = dy + flat * n;
+        for (int64_t kk = 0; kk < k; ++kk) {
+            double acc = 0.0, sabs = 0.0;
+            for (int64_t j = 0; j < n; ++j) {
+                double p = bf16_decode(dyr[j]) * bf16_decode(we[kk * n + j]);
+                acc += p;
+                sabs += fabs(p);
+            }
+            dx[r * k + kk] = acc;
+            s[r * k + kk] = sabs;
+        }
+    }
+    return 0;
+}
+
+/* ---- masked wgrad: dW[e, kk, :] = sum over active rows r of X[e, r, kk] *
+ * dY[e, r, :] ------------------------------------------------------------- */
+/* pairs: nsel (expert, kk) pairs as int64 [nsel, 2]; NULL = all E*k rows of
+ * dW in order.  An expert with no active rows gives +0.0 everywhere. */
+int oracle_masked_wgrad(const uint16_t* x, const uint16_t* dy,
+                        const int32_t* masked_m, int64_t max_m, int64_t k,
+                        int64_t n, int32_t num_groups,
+                        const int64_t* pairs, int64_t nsel,
+                        double* dw, double* s, int32_t* status) {
+    if (num_groups < 1) return -1;
+    int64_t count = pairs ? nsel : (int64_t)num_groups * k;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < count; ++r) {
+        int64_t e = pairs ? pairs[2 * r] : r / k;
+        int64_t kk = pairs ? pairs[2 * r + 1] : r % k;
+        int ok = e >= 0 && e < num_groups && kk >= 0 && kk < k;
+        status[r] = ok;
+        if (!ok) continue;
+        double* out = dw + r * n;
+        double* sr = s + r * n;
+        for (int64_t j = 0; j < n; ++j) { out[j] = 0.0; sr[j] = 0.0; }
+        int64_t active = masked_active(masked_m, e, max_m);
+        for (int64_t row = 0; row < active; ++row) {
+            double a = bf16_decode(x[(e * max_m + row) * k + kk]);
+            const uint16_t* dyr = dy + (e * max_m + row) * n;
+            for (int64_t j = 0; j < n; ++j) {
+                double p = a * bf16_decode(dyr[j]);
+                out[j] += p;
                 sr[j] += fabs(p);
             }
         }

@@ -13,6 +13,9 @@
   E = 1 is a dense GEMM, equal-size experts are a batched matmul, a fully
   active masked layout is a batched matmul;
 * the masked layout compacted into end offsets equals the ragged forward;
+* the masked backward (dgrad, wgrad): exact brute force over active rows,
+  equality with the ragged passes on the compacted rows, and the adjoint
+  identity on the masked layout;
 * alpha / beta: exact rational brute force of alpha * P + beta * C on every
   pass, beta = 0 never reading C, alpha = 0 returning C, and accumulation
   leaving an empty expert's dW unchanged.
@@ -634,3 +637,84 @@ def test_accumulating_wgrad_keeps_empty_experts(oracle_lib):
         assert np.array_equal(acc[g], cc[g])
     for g in (1, 3):
         assert np.allclose(acc[g], plain[g] + cc[g], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# masked dgrad / wgrad: the backward of the masked forward over active rows
+# (sglang PR #32385, "Evidence" and "Cause")
+# ---------------------------------------------------------------------------
+
+def _masked_case(rng, E, max_m, k, n):
+    act = rng.integers(0, max_m + 1, E)
+    act[rng.random(E) < 0.25] = 0
+    dy = np.full((E, max_m, n), 0x7FC0, dtype=np.uint16)     # NaN in inactive rows
+    x = np.full((E, max_m, k), 0x7FC0, dtype=np.uint16)
+    for e in range(E):
+        dy[e, :act[e]] = randn_bf16_bits(rng, (int(act[e]), n))
+        x[e, :act[e]] = randn_bf16_bits(rng, (int(act[e]), k))
+    w = randn_bf16_bits(rng, (E, k, n), std=0.5)
+    return act.astype(np.int32), x, dy, w
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_masked_backward_exact(oracle_lib, seed):
+    rng = np.random.default_rng(7000 + seed)
+    E = int(rng.integers(1, 5))
+    max_m = int(rng.integers(1, 9))
+    k = int(rng.choice([8, 16]))
+    n = int(rng.choice([8, 16]))
+    act, x, dy, w = _masked_case(rng, E, max_m, k, n)
+    dg = oracle.masked_dgrad(dy, w, act)
+    wg = oracle.masked_wgrad(x, dy, act)
+    W = bits_to_exact_int(w)
+    for e in range(E):
+        DY = bits_to_exact_int(dy[e, :act[e]])
+        X = bits_to_exact_int(x[e, :act[e]])
+        for r in range(max_m):
+            flat = e * max_m + r
+            if r < act[e]:
+                assert dg.status[flat] == 1
+                _check_exact(dg.value[flat], dg.sabs[flat], DY[r:r + 1].dot(W[e].T)[0], n)
+            else:
+                assert dg.status[flat] == 0 and np.all(np.isnan(dg.value[flat]))
+        dwe = X.T.dot(DY) if act[e] > 0 else np.zeros((k, n), dtype=object)
+        for kk in range(k):
+            row = e * k + kk
+            _check_exact(wg.value[row], wg.sabs[row], dwe[kk], max(int(act[e]), 1))
+        if act[e] == 0:
+            v = wg.value[e * k:(e + 1) * k]
+            assert np.all(v == 0.0) and not np.any(np.signbit(v))
+
+
+def test_masked_backward_compacts_to_ragged(oracle_lib):
+    """The masked passes on active rows equal the ragged passes on the same
+    rows packed densely (offsets = cumsum(masked_m))."""
+    rng = np.random.default_rng(91)
+    E, max_m, k, n = 5, 24, 32, 40
+    act, x, dy, w = _masked_case(rng, E, max_m, k, n)
+    xr = np.concatenate([x[e, :act[e]] for e in range(E)])
+    dyr = np.concatenate([dy[e, :act[e]] for e in range(E)])
+    offs = np.cumsum(act).astype(np.int32)
+    mdg = oracle.masked_dgrad(dy, w, act)
+    rdg = oracle.dgrad(dyr, w, offs)
+    mwg = oracle.masked_wgrad(x, dy, act)
+    rwg = oracle.wgrad(xr, dyr, offs)
+    flat = np.concatenate([np.arange(act[e]) + e * max_m for e in range(E)])
+    assert np.array_equal(mdg.value[flat], rdg.value)
+    assert np.array_equal(mwg.value, rwg.value)
+
+
+def test_masked_adjoint_identity(oracle_lib):
+    """<fwd(X,W), dY> = <X, dgrad(dY,W)> = <W, wgrad(X,dY)> on active rows."""
+    rng = np.random.default_rng(92)
+    E, max_m, k, n = 4, 16, 24, 32
+    act, x, dy, w = _masked_case(rng, E, max_m, k, n)
+    fw = oracle.masked_forward(x, w, act)
+    dg = oracle.masked_dgrad(dy, w, act)
+    wg = oracle.masked_wgrad(x, dy, act)
+    ok = fw.status == 1
+    X, DY, W = dec(x).reshape(E * max_m, k), dec(dy).reshape(E * max_m, n), dec(w).reshape(E * k, n)
+    a = float(np.sum(fw.value[ok] * DY[ok]))
+    b = float(np.sum(X[ok] * dg.value[ok]))
+    c = float(np.sum(W * wg.value))
+    assert abs(a - b) <= 1e-9 * max(1.0, abs(a)) and abs(a - c) <= 1e-9 * max(1.0, abs(a))
