@@ -133,7 +133,34 @@ gg_status gg_masked_forward(const void* x, const void* w,
                             int64_t n, int32_t num_groups, void* stream);
 
 /*
- * Scaled and accumulating forms of the four passes:
+ * gg_masked_dgrad -- dX[e, r, :] = dY[e, r, :] . W[e]^T for r < masked_m[e].
+ *   dy       [E, max_m, n]  bf16; inactive rows are never read
+ *   w        [E, k, n]      bf16
+ *   masked_m [E]            int32 active-row counts, device memory
+ *   dx       [E, max_m, k]  dx_dtype; only active rows are written
+ * gg_masked_wgrad -- dW[e] = X[e, :a]^T . dY[e, :a] with a = the clamped
+ * masked_m[e], for every expert.
+ *   x        [E, max_m, k]  bf16; inactive rows are never read
+ *   dy       [E, max_m, n]  bf16; inactive rows are never read
+ *   dw       [E, k, n]      dw_dtype; ALL of it is written, an expert with
+ *                           no active rows gets +0.0 everywhere
+ * The backward of gg_masked_forward on the same layout: the masked grouped
+ * GEMM (sglang PR #32385, "Evidence") runs on the dispatched activations of
+ * an expert-parallel MoE layer, whose training step needs the input and
+ * weight gradients over the same active rows; inactive rows stay out of
+ * every result ("Cause": consumers must not depend on them).
+ */
+gg_status gg_masked_dgrad(const void* dy, const void* w,
+                          const int32_t* masked_m, void* dx,
+                          gg_dtype dx_dtype, int64_t max_m, int64_t k,
+                          int64_t n, int32_t num_groups, void* stream);
+gg_status gg_masked_wgrad(const void* x, const void* dy,
+                          const int32_t* masked_m, void* dw,
+                          gg_dtype dw_dtype, int64_t max_m, int64_t k,
+                          int64_t n, int32_t num_groups, void* stream);
+
+/*
+ * Scaled and accumulating forms of the six passes:
  *
  *   out = alpha * P + beta * out          (P = the pass's grouped product)
  *
@@ -166,6 +193,16 @@ gg_status gg_masked_forward_ex(const void* x, const void* w,
                                gg_dtype y_dtype, int64_t max_m, int64_t k,
                                int64_t n, int32_t num_groups, float alpha,
                                float beta, void* stream);
+gg_status gg_masked_dgrad_ex(const void* dy, const void* w,
+                             const int32_t* masked_m, void* dx,
+                             gg_dtype dx_dtype, int64_t max_m, int64_t k,
+                             int64_t n, int32_t num_groups, float alpha,
+                             float beta, void* stream);
+gg_status gg_masked_wgrad_ex(const void* x, const void* dy,
+                             const int32_t* masked_m, void* dw,
+                             gg_dtype dw_dtype, int64_t max_m, int64_t k,
+                             int64_t n, int32_t num_groups, float alpha,
+                             float beta, void* stream);
 
 /* Static description of a status code. */
 const char* gg_status_str(gg_status s);

@@ -62,12 +62,14 @@ def load():
     I64 = ctypes.c_int64
     I32 = ctypes.c_int32
     sig = [P, P, P, P, ctypes.c_int, I64, I64, I64, I32, P]
-    for name in ("gg_forward", "gg_dgrad", "gg_wgrad", "gg_masked_forward"):
+    for name in ("gg_forward", "gg_dgrad", "gg_wgrad", "gg_masked_forward", "gg_masked_dgrad",
+                 "gg_masked_wgrad"):
         f = getattr(lib, name)
         f.argtypes = sig
         f.restype = ctypes.c_int
     sig_ex = sig[:-1] + [ctypes.c_float, ctypes.c_float, P]
-    for name in ("gg_forward_ex", "gg_dgrad_ex", "gg_wgrad_ex", "gg_masked_forward_ex"):
+    for name in ("gg_forward_ex", "gg_dgrad_ex", "gg_wgrad_ex", "gg_masked_forward_ex",
+                 "gg_masked_dgrad_ex", "gg_masked_wgrad_ex"):
         f = getattr(lib, name)
         f.argtypes = sig_ex
         f.restype = ctypes.c_int
@@ -246,5 +248,52 @@ def masked_forward(x, w, masked_m, out=None, out_dtype=None, alpha=1.0, beta=0.0
     if tuple(out.shape) != (e, max_m, n):
         raise ValueError(f"out must be [{e}, {max_m}, {n}]")
     _invoke("gg_masked_forward", x, w, masked_m, out, _dtype_code(out.dtype), max_m, k, n, e, dev,
+            alpha, beta)
+    return out
+
+
+def masked_dgrad(dy, w, masked_m, out=None, out_dtype=None, alpha=1.0, beta=0.0):
+    """dX[e, r] = dY[e, r] . W[e]^T for r < masked_m[e] (gg_masked_dgrad).
+    dy: bf16 [E, max_m, n]; w: bf16 [E, k, n]; only active rows of ``out``
+    [E, max_m, k] are written."""
+    torch = _torch()
+    _need_out(out, beta)
+    dev = dy.device
+    _check(dy, "dy", torch.bfloat16, 3, dev)
+    _check(w, "w", torch.bfloat16, 3, dev)
+    _check(masked_m, "masked_m", torch.int32, 1, dev)
+    e, max_m, n = dy.shape
+    e2, k, n2 = w.shape
+    if e2 != e or n2 != n or masked_m.shape[0] != e:
+        raise ValueError("shape mismatch between dy, w and masked_m")
+    if out is None:
+        out = torch.empty((e, max_m, k), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check(out, "out", out.dtype, 3, dev)
+    if tuple(out.shape) != (e, max_m, k):
+        raise ValueError(f"out must be [{e}, {max_m}, {k}]")
+    _invoke("gg_masked_dgrad", dy, w, masked_m, out, _dtype_code(out.dtype), max_m, k, n, e, dev,
+            alpha, beta)
+    return out
+
+
+def masked_wgrad(x, dy, masked_m, out=None, out_dtype=None, alpha=1.0, beta=0.0):
+    """dW[e] = X[e, :a]^T . dY[e, :a], a = masked_m[e] clamped, for every
+    expert (gg_masked_wgrad); all of ``out`` [E, k, n] is written."""
+    torch = _torch()
+    _need_out(out, beta)
+    dev = x.device
+    _check(x, "x", torch.bfloat16, 3, dev)
+    _check(dy, "dy", torch.bfloat16, 3, dev)
+    _check(masked_m, "masked_m", torch.int32, 1, dev)
+    e, max_m, k = x.shape
+    e2, max_m2, n = dy.shape
+    if e2 != e or max_m2 != max_m or masked_m.shape[0] != e:
+        raise ValueError("shape mismatch between x, dy and masked_m")
+    if out is None:
+        out = torch.empty((e, k, n), dtype=out_dtype or torch.float32, device=dev)
+    _check(out, "out", out.dtype, 3, dev)
+    if tuple(out.shape) != (e, k, n):
+        raise ValueError(f"out must be [{e}, {k}, {n}]")
+    _invoke("gg_masked_wgrad", x, dy, masked_m, out, _dtype_code(out.dtype), max_m, k, n, e, dev,
             alpha, beta)
     return out

@@ -131,6 +131,40 @@ gg_status gg_masked_forward_ex(const void* x, const void* w, const int32_t* mask
   return run(3, x, w, masked_m, y, y_dtype, max_m, k, n, num_groups, alpha, beta, stream);
 }
 
+gg_status gg_masked_dgrad_ex(const void* dy, const void* w, const int32_t* masked_m, void* dx,
+                             gg_dtype dx_dtype, int64_t max_m, int64_t k, int64_t n,
+                             int32_t num_groups, float alpha, float beta, void* stream) {
+  gg_status s = check(dy, w, masked_m, dx, dx_dtype, max_m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  s = masked_rows(max_m, num_groups);
+  if (s != GG_OK) return s;
+  return run(4, dy, w, masked_m, dx, dx_dtype, max_m, k, n, num_groups, alpha, beta, stream);
+}
+
+gg_status gg_masked_wgrad_ex(const void* x, const void* dy, const int32_t* masked_m, void* dw,
+                             gg_dtype dw_dtype, int64_t max_m, int64_t k, int64_t n,
+                             int32_t num_groups, float alpha, float beta, void* stream) {
+  gg_status s = check(x, dy, masked_m, dw, dw_dtype, max_m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  s = masked_rows(max_m, num_groups);
+  if (s != GG_OK) return s;
+  return run(5, x, dy, masked_m, dw, dw_dtype, max_m, k, n, num_groups, alpha, beta, stream);
+}
+
+gg_status gg_masked_dgrad(const void* dy, const void* w, const int32_t* masked_m, void* dx,
+                          gg_dtype dx_dtype, int64_t max_m, int64_t k, int64_t n,
+                          int32_t num_groups, void* stream) {
+  return gg_masked_dgrad_ex(dy, w, masked_m, dx, dx_dtype, max_m, k, n, num_groups, 1.0f, 0.0f,
+                            stream);
+}
+
+gg_status gg_masked_wgrad(const void* x, const void* dy, const int32_t* masked_m, void* dw,
+                          gg_dtype dw_dtype, int64_t max_m, int64_t k, int64_t n,
+                          int32_t num_groups, void* stream) {
+  return gg_masked_wgrad_ex(x, dy, masked_m, dw, dw_dtype, max_m, k, n, num_groups, 1.0f, 0.0f,
+                            stream);
+}
+
 gg_status gg_forward(const void* x, const void* w, const int32_t* offs, void* y, gg_dtype y_dtype,
                      int64_t m, int64_t k, int64_t n, int32_t num_groups, void* stream) {
   return gg_forward_ex(x, w, offs, y, y_dtype, m, k, n, num_groups, 1.0f, 0.0f, stream);

@@ -8,7 +8,8 @@
 #define GG_MAX_GROUPS_DEV 2048
 
 namespace gg {
-// mode: 0 forward, 1 dgrad, 2 wgrad, 3 masked forward.  Arguments were
+// mode: 0 forward, 1 dgrad, 2 wgrad, 3 masked forward, 4 masked dgrad,
+// 5 masked wgrad.  Arguments were
 // validated by the caller.  Writes alpha * product + beta * (prior output)
 // (the prior output is not read when beta == 0).  Launches one persistent
 // grid of at most num_cus workgroups on `stream`.

@@ -5,11 +5,13 @@
 // and the passages that define them).  Each pass is the same tile engine fed
 // by a different operand description:
 //
-//   pass     out tile rows x cols      reduction   A operand           B operand
-//   forward  expert rows  x n          k           X   (red-contig)    W[g] (red-strided)
-//   dgrad    expert rows  x k          n           dY  (red-contig)    W[g] (red-contig)
-//   wgrad    k            x n          expert rows X   (red-strided)   dY   (red-strided)
-//   masked   active rows  x n          k           X[e] (red-contig)   W[e] (red-strided)
+//   pass           out tile rows x cols   reduction    A operand          B operand
+//   forward        expert rows x n        k            X    (red-contig)  W[g] (red-strided)
+//   dgrad          expert rows x k        n            dY   (red-contig)  W[g] (red-contig)
+//   wgrad          k x n                  expert rows  X    (red-strided) dY   (red-strided)
+//   masked fwd     active rows x n        k            X[e] (red-contig)  W[e] (red-strided)
+//   masked dgrad   active rows x k        n            dY[e](red-contig)  W[e] (red-contig)
+//   masked wgrad   k x n                  active rows  X[e] (red-strided) dY[e](red-strided)
 //
 // "red-contig" means the reduction index is the contiguous one in memory;
 // "red-strided" means the tile's row index is.
@@ -80,7 +82,13 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-enum Mode { FWD = 0, DGRAD = 1, WGRAD = 2, MASKED = 3 };
+enum Mode { FWD = 0, DGRAD = 1, WGRAD = 2, MASKED = 3, MASKED_DGRAD = 4, MASKED_WGRAD = 5 };
+
+// The masked modes are the ragged passes on the masked layout: expert e's
+// rows start at e * max_m and its active count is masked_m[e].
+constexpr bool is_masked(int mode) { return mode >= MASKED; }
+constexpr bool is_wgrad(int mode) { return mode == WGRAD || mode == MASKED_WGRAD; }
+constexpr bool is_dgrad(int mode) { return mode == DGRAD || mode == MASKED_DGRAD; }
 
 struct Params {
   const uint16_t* a;        // forward/masked/wgrad: X;  dgrad: dY
@@ -582,7 +590,8 @@ __device__ __forceinline__ int block_scan_incl(int v, int* scratch, int tid) {
 }
 
 // Fills s_start/s_end with the clamped row range of every group and, unless
-// WGRAD, s_pref[0..E] with the exclusive prefix of per-group row-tile counts.
+// a wgrad mode, s_pref[0..E] with the exclusive prefix of per-group row-tile
+// counts.
 template <int MODE>
 __device__ void decode_groups(const Params& p, int32_t* s_start, int32_t* s_end, int32_t* s_pref,
                               int* scratch, int tid) {
@@ -590,7 +599,7 @@ __device__ void decode_groups(const Params& p, int32_t* s_start, int32_t* s_end,
   const int per = (E + NT - 1) / NT;
   const int g0 = tid * per;
   const int g1 = g0 + per < E ? g0 + per : E;
-  if constexpr (MODE == MASKED) {
+  if constexpr (is_masked(MODE)) {
     for (int g = g0; g < g1; ++g) {
       int a = p.groups[g];
       a = a < 0 ? 0 : a;
@@ -620,7 +629,7 @@ __device__ void decode_groups(const Params& p, int32_t* s_start, int32_t* s_end,
     for (int g = g0; g < g1; ++g) s_start[g] = g == 0 ? 0 : s_end[g - 1];
   }
   __syncthreads();
-  if constexpr (MODE != WGRAD) {
+  if constexpr (!is_wgrad(MODE)) {
     int local = 0;
     for (int g = g0; g < g1; ++g) local += (s_end[g] - s_start[g] + BM - 1) / BM;
     const int incl = block_scan_incl<false>(local, scratch, tid);
@@ -701,8 +710,8 @@ __device__ __forceinline__ void lds_barrier() {
 
 template <int MODE, bool OUT_F32>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
-  constexpr bool A_STRIDED = (MODE == WGRAD);
-  constexpr bool B_STRIDED = (MODE != DGRAD);
+  constexpr bool A_STRIDED = is_wgrad(MODE);
+  constexpr bool B_STRIDED = !is_dgrad(MODE);
 
   // LDS: NSTAGE stage buffers of 32 KB (A tile, then B tile).
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE_BYTES];
@@ -721,11 +730,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   decode_groups<MODE>(p, s_start, s_end, s_pref, s_scan, tid);
 
   // Output tile grid.
-  const int64_t out_cols = (MODE == DGRAD) ? p.k : p.n;
+  const int64_t out_cols = is_dgrad(MODE) ? p.k : p.n;
   const int col_tiles = (int)((out_cols + BN - 1) / BN);
   int64_t total;
   int row_tiles_w = 0;
-  if constexpr (MODE == WGRAD) {
+  if constexpr (is_wgrad(MODE)) {
     row_tiles_w = (int)((p.k + BM - 1) / BM);
     total = (int64_t)E * row_tiles_w * col_tiles;
   } else {
@@ -747,7 +756,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     const int64_t u = xcd_tile(t, total);
     int ct;
     int64_t rt_all;
-    if constexpr (MODE == WGRAD) {
+    if constexpr (is_wgrad(MODE)) {
       // per expert: a row_tiles_w x col_tiles grid in strip order
       const int64_t per_g = (int64_t)row_tiles_w * col_tiles;
       const int64_t gq = u / per_g;
@@ -760,19 +769,21 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     const int col0 = ct * BN;
     Operand& A = T.A;
     Operand& B = T.B;
-    if constexpr (MODE == WGRAD) {
+    if constexpr (is_wgrad(MODE)) {
       const int g = (int)(rt_all / row_tiles_w);
       const int rt = (int)(rt_all % row_tiles_w);
       const int row0 = rt * BM;                 // first k index of the tile
       const int s = uniform(s_start[g]), e = uniform(s_end[g]);
-      // A(row kk, red i) = X[s + i, row0 + kk]
-      A.origin = pa + 2 * ((int64_t)s * p.k + row0);
+      // first memory row of the expert's rows (masked: expert g's block)
+      const int64_t srow = (is_masked(MODE) ? (int64_t)g * p.m : 0) + s;
+      // A(row kk, red i) = X[srow + i, row0 + kk]
+      A.origin = pa + 2 * (srow * p.k + row0);
       A.ld_bytes = (uint32_t)(2 * p.k);
       A.rows = (int)(p.k - row0 < BM ? p.k - row0 : BM);
       A.red = e - s;
       A.row_tail = (uint32_t)(2 * (p.k - row0));
-      // B(row n, red i) = dY[s + i, col0 + n]
-      B.origin = pb + 2 * ((int64_t)s * p.n + col0);
+      // B(row n, red i) = dY[srow + i, col0 + n]
+      B.origin = pb + 2 * (srow * p.n + col0);
       B.ld_bytes = (uint32_t)(2 * p.n);
       B.rows = (int)(p.n - col0 < BN ? p.n - col0 : BN);
       B.red = e - s;
@@ -787,8 +798,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
       const int s = uniform(s_start[g]), e = uniform(s_end[g]);
       const int row0 = s + rt * BM;             // first expert row of the tile
       const int rows = (e - row0) < BM ? (e - row0) : BM;
-      const int64_t arow = (MODE == MASKED) ? (int64_t)g * p.m + row0 : (int64_t)row0;
-      if constexpr (MODE == DGRAD) {
+      const int64_t arow = is_masked(MODE) ? (int64_t)g * p.m + row0 : (int64_t)row0;
+      if constexpr (is_dgrad(MODE)) {
         // A(row i, red j) = dY[arow + i, j];  B(row kk, red j) = W[g, col0 + kk, j]
         A.origin = pa + 2 * (arow * p.n);
         A.ld_bytes = (uint32_t)(2 * p.n);
@@ -850,7 +861,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
 
     // An expert's last tile with 128 rows or fewer runs at half height:
     // each wave computes 64 x 64, skipping the MFMAs of empty rows.
-    const bool half = (MODE != WGRAD) && cur.rows <= BM / 2;
+    const bool half = !is_wgrad(MODE) && cur.rows <= BM / 2;
     // fp32 tiles after the first start with the previous tile's stores
     // still in flight behind their prologue loads
     if (half)
@@ -929,10 +940,10 @@ static hipError_t launch_mode(const Params& p, bool out_f32, int grid, hipStream
 // (the device knows the exact count).  Each expert adds at most one partial
 // row tile beyond ceil(rows / BM).
 static int64_t max_tiles(int mode, int64_t m, int64_t k, int64_t n, int64_t E) {
-  if (mode == WGRAD) return E * ((k + BM - 1) / BM) * ((n + BN - 1) / BN);
-  const int64_t cols = mode == DGRAD ? k : n;
+  if (is_wgrad(mode)) return E * ((k + BM - 1) / BM) * ((n + BN - 1) / BN);
+  const int64_t cols = is_dgrad(mode) ? k : n;
   const int64_t ct = (cols + BN - 1) / BN;
-  if (mode == MASKED) return E * ((m + BM - 1) / BM) * ct;
+  if (is_masked(mode)) return E * ((m + BM - 1) / BM) * ct;
   return ((m + BM - 1) / BM + E) * ct;
 }
 
@@ -958,6 +969,8 @@ hipError_t launch(int mode, const void* a, const void* b, const int32_t* groups,
     case DGRAD: return launch_mode<DGRAD>(p, out_f32, grid, stream);
     case WGRAD: return launch_mode<WGRAD>(p, out_f32, grid, stream);
     case MASKED: return launch_mode<MASKED>(p, out_f32, grid, stream);
+    case MASKED_DGRAD: return launch_mode<MASKED_DGRAD>(p, out_f32, grid, stream);
+    case MASKED_WGRAD: return launch_mode<MASKED_WGRAD>(p, out_f32, grid, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -285,7 +285,8 @@ def make_inputs(wl: Workload, device="cpu", need=("x", "w", "dy")):
 
     Returns a dict with any of ``x``, ``w``, ``dy`` (bf16 tensors) and
     ``offs`` / ``masked_m`` (int32 tensors).  For the masked layout the
-    inactive rows of X hold bf16 quiet NaN, so a read of them would show.
+    inactive rows of X and dY hold bf16 quiet NaN, so a read of them would
+    show.
     """
     import torch
     out = {}
@@ -301,8 +302,14 @@ def make_inputs(wl: Workload, device="cpu", need=("x", "w", "dy")):
         out["w"] = _randn_bf16(wl.w_shape(), wl.w_std, wl.seed, 2, device)
     if "dy" in need:
         if wl.layout == "masked":
-            raise ValueError("the masked layout has a forward pass only")
-        out["dy"] = _randn_bf16((wl.m, wl.n), wl.dy_std, wl.seed, 3, device)
+            dy = _randn_bf16((wl.num_groups, wl.m, wl.n), wl.dy_std, wl.seed, 3, device)
+            sizes = wl.group_sizes()
+            dyi = dy.view(torch.int16)
+            for e in range(wl.num_groups):
+                dyi[e, int(sizes[e]):, :] = BF16_QNAN
+            out["dy"] = dy
+        else:
+            out["dy"] = _randn_bf16((wl.m, wl.n), wl.dy_std, wl.seed, 3, device)
     if wl.layout == "masked":
         out["masked_m"] = torch.from_numpy(wl.masked_m.astype(np.int32)).to(device)
     else:

@@ -8,7 +8,7 @@ import pytest
 
 from moe_grouped_gemm_ragged_amd import binding as gg
 
-ENTRY = ["gg_forward", "gg_dgrad", "gg_wgrad", "gg_masked_forward"]
+ENTRY = ["gg_forward", "gg_dgrad", "gg_wgrad", "gg_masked_forward", "gg_masked_dgrad", "gg_masked_wgrad"]
 
 
 @pytest.fixture(scope="module")
@@ -66,8 +66,9 @@ def test_bad_arguments_rejected_before_launch(lib, name, case, status):
     assert gg.last_error() != ""
 
 
-def test_masked_row_limit(lib):
-    rc = call("gg_masked_forward", m=1 << 24, e=256)
+@pytest.mark.parametrize("name", ["gg_masked_forward", "gg_masked_dgrad", "gg_masked_wgrad"])
+def test_masked_row_limit(lib, name):
+    rc = call(name, m=1 << 24, e=256)
     assert rc == 2 and "max_m" in gg.last_error()
 
 
