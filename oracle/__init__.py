@@ -274,3 +274,48 @@ def masked_wgrad(x, dy, masked_m, pairs=None, alpha=1.0, beta=0.0, c_in=None) ->
     idx = sel if sel is not None else np.stack(
         [np.repeat(np.arange(e), k), np.tile(np.arange(k), e)], axis=1)
     return apply_alpha_beta(Result(value, sabs, status, idx), alpha, beta, c_in)
+
+
+def _silu_mul(gate: Result, up: Result) -> Result:
+    """out = silu(G) * U with silu(z) = z / (1 + exp(-z)), on the fp64 gate
+    and up products, before the one rounding (the activation step between
+    the gate/up and down GEMMs: sglang PR #32385, "Cause"; fused into the
+    gate/up epilogue).  S is replaced by a magnitude that bounds the
+    propagated accumulation error: with d silu(z)/dz = s(z) (1 + z (1 - s(z)))
+    and s the logistic function,
+        S' = |silu'(G)| |U| S_G + |silu(G)| S_U + 4 |out|,
+    the last term standing for the fp32 evaluation of silu * mul (the checks
+    scale S by 2 L 2^-24, so it allows at least 8 fp32 ulps of the result)."""
+    g, u = gate.value, up.value
+    with np.errstate(over="ignore"):
+        sig = 1.0 / (1.0 + np.exp(-g))
+    silu = g * sig
+    dsilu = sig * (1.0 + g * (1.0 - sig))
+    value = silu * u
+    sabs = np.abs(dsilu) * np.abs(u) * gate.sabs + np.abs(silu) * up.sabs + 4.0 * np.abs(value)
+    return Result(value, sabs, gate.status, gate.index)
+
+
+def forward_silu_mul(x, w13, offs, rows=None) -> Result:
+    """Rows of the ragged gate/up forward with the SiLU-mul activation:
+    A[i, c] = silu((X W13[g])[i, c]) * (X W13[g])[i, I + c], c < I, where
+    w13 is [E, K, 2I] (gate columns first, then up).  Built on forward()."""
+    w13 = _u16(w13)
+    e, k, n2 = w13.shape
+    assert n2 % 2 == 0
+    i = n2 // 2
+    gate = forward(x, np.ascontiguousarray(w13[:, :, :i]), offs, rows=rows)
+    up = forward(x, np.ascontiguousarray(w13[:, :, i:]), offs, rows=rows)
+    return _silu_mul(gate, up)
+
+
+def masked_forward_silu_mul(x, w13, masked_m, rows=None) -> Result:
+    """The masked layout's gate/up forward with the SiLU-mul activation
+    (output [E, max_m, I], active rows only).  Built on masked_forward()."""
+    w13 = _u16(w13)
+    e, k, n2 = w13.shape
+    assert n2 % 2 == 0
+    i = n2 // 2
+    gate = masked_forward(x, np.ascontiguousarray(w13[:, :, :i]), masked_m, rows=rows)
+    up = masked_forward(x, np.ascontiguousarray(w13[:, :, i:]), masked_m, rows=rows)
+    return _silu_mul(gate, up)

@@ -16,6 +16,10 @@
 * the masked backward (dgrad, wgrad): exact brute force over active rows,
   equality with the ragged passes on the compacted rows, and the adjoint
   identity on the masked layout;
+* the SiLU-mul activation on the gate/up forward: torch's SiLU on the exact
+  products, the odd and even parts (silu(z) - silu(-z) = z, silu(z) +
+  silu(-z) = z tanh(z/2)) via negated gate weights, the gate/up column
+  order, and masked = ragged on compacted rows;
 * alpha / beta: exact rational brute force of alpha * P + beta * C on every
   pass, beta = 0 never reading C, alpha = 0 returning C, and accumulation
   leaving an empty expert's dW unchanged.
@@ -718,3 +722,92 @@ def test_masked_adjoint_identity(oracle_lib):
     b = float(np.sum(X[ok] * dg.value[ok]))
     c = float(np.sum(W * wg.value))
     assert abs(a - b) <= 1e-9 * max(1.0, abs(a)) and abs(a - c) <= 1e-9 * max(1.0, abs(a))
+
+
+# ---------------------------------------------------------------------------
+# SiLU-mul activation on the gate/up forward (sglang PR #32385, "Cause")
+# ---------------------------------------------------------------------------
+
+def _silu_case(seed, E=3, k=16, i=8):
+    rng = np.random.default_rng(seed)
+    sizes = np.array([5, 0, 9][:E])
+    offs = np.cumsum(sizes).astype(np.int32)
+    m = int(offs[-1]) + 2
+    x = randn_bf16_bits(rng, (m, k))
+    w13 = randn_bf16_bits(rng, (E, k, 2 * i))
+    return x, w13, offs, i
+
+
+def test_silu_mul_matches_library_silu(oracle_lib):
+    """torch's SiLU in fp64 on the oracle's exact gate and up products."""
+    torch = pytest.importorskip("torch")
+    x, w13, offs, i = _silu_case(1)
+    r = oracle.forward_silu_mul(x, w13, offs)
+    g = oracle.forward(x, np.ascontiguousarray(w13[:, :, :i]), offs)
+    u = oracle.forward(x, np.ascontiguousarray(w13[:, :, i:]), offs)
+    ok = r.status == 1
+    lib = torch.nn.functional.silu(torch.from_numpy(g.value[ok])).numpy() * u.value[ok]
+    assert np.allclose(r.value[ok], lib, rtol=1e-13, atol=0)
+    assert np.all(r.status == g.status)
+
+
+def test_silu_odd_part_is_identity(oracle_lib):
+    """silu(z) - silu(-z) = z: negating the gate weights negates the gate
+    exactly, so out(W) - out(W with -gate) = gate * up."""
+    x, w13, offs, i = _silu_case(2)
+    neg = w13.copy()
+    neg[:, :, :i] ^= 0x8000
+    a = oracle.forward_silu_mul(x, w13, offs)
+    b = oracle.forward_silu_mul(x, neg, offs)
+    g = oracle.forward(x, np.ascontiguousarray(w13[:, :, :i]), offs)
+    u = oracle.forward(x, np.ascontiguousarray(w13[:, :, i:]), offs)
+    ok = a.status == 1
+    want = g.value[ok] * u.value[ok]
+    assert np.allclose(a.value[ok] - b.value[ok], want, rtol=1e-12, atol=1e-12)
+
+
+def test_silu_even_part_is_tanh(oracle_lib):
+    """silu(z) + silu(-z) = z tanh(z / 2)."""
+    x, w13, offs, i = _silu_case(3)
+    neg = w13.copy()
+    neg[:, :, :i] ^= 0x8000
+    a = oracle.forward_silu_mul(x, w13, offs)
+    b = oracle.forward_silu_mul(x, neg, offs)
+    g = oracle.forward(x, np.ascontiguousarray(w13[:, :, :i]), offs)
+    u = oracle.forward(x, np.ascontiguousarray(w13[:, :, i:]), offs)
+    ok = a.status == 1
+    want = g.value[ok] * np.tanh(g.value[ok] / 2) * u.value[ok]
+    assert np.allclose(a.value[ok] + b.value[ok], want, rtol=1e-12, atol=1e-12)
+
+
+def test_silu_zero_gate_gives_zero_and_layout(oracle_lib):
+    """Gate weights of zero give silu(0) = 0 whatever the up half holds; and
+    the gate is the FIRST half of the columns: zeroing the second half
+    (the up projection) zeroes the output instead."""
+    x, w13, offs, i = _silu_case(4)
+    zg = w13.copy()
+    zg[:, :, :i] = 0
+    r = oracle.forward_silu_mul(x, zg, offs)
+    ok = r.status == 1
+    assert np.all(r.value[ok] == 0.0)
+    zu = w13.copy()
+    zu[:, :, i:] = 0
+    r2 = oracle.forward_silu_mul(x, zu, offs)
+    assert np.all(r2.value[ok] == 0.0)
+    assert np.any(oracle.forward_silu_mul(x, w13, offs).value[ok] != 0.0)
+
+
+def test_masked_silu_mul_compacts_to_ragged(oracle_lib):
+    rng = np.random.default_rng(95)
+    E, max_m, k, i = 4, 12, 16, 8
+    act = np.array([3, 0, 12, 7], dtype=np.int32)
+    x = np.full((E, max_m, k), 0x7FC0, dtype=np.uint16)
+    for e in range(E):
+        x[e, :act[e]] = randn_bf16_bits(rng, (int(act[e]), k))
+    w13 = randn_bf16_bits(rng, (E, k, 2 * i))
+    m = oracle.masked_forward_silu_mul(x, w13, act)
+    xr = np.concatenate([x[e, :act[e]] for e in range(E)])
+    r = oracle.forward_silu_mul(xr, w13, np.cumsum(act).astype(np.int32))
+    flat = np.concatenate([np.arange(act[e]) + e * max_m for e in range(E)])
+    assert np.array_equal(m.value[flat], r.value)
+    assert int((m.status == 1).sum()) == int(act.sum())
