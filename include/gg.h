@@ -160,6 +160,34 @@ gg_status gg_masked_wgrad(const void* x, const void* dy,
                           int64_t n, int32_t num_groups, void* stream);
 
 /*
+ * gg_forward_silu_mul -- the gate/up forward with the SiLU-mul activation
+ * fused into its epilogue:
+ *   out[i, c] = silu(G[i, c]) * U[i, c],  silu(z) = z / (1 + exp(-z)),
+ *   G = X[rows of g] . W13[g][:, 0:I],  U = X[rows of g] . W13[g][:, I:2I]
+ * for c < I = n / 2, evaluated in fp32 on the accumulators and rounded once.
+ *   x    [m, k]       bf16
+ *   w13  [E, k, n]    bf16, n = 2 I: the I gate columns, then the I up columns
+ *   offs [E]          int32 cumulative end offsets, device memory
+ *   out  [m, I]       out_dtype; rows [0, end(E-1)) are written, the rest
+ *                     untouched
+ * gg_masked_forward_silu_mul -- the same on the masked layout:
+ *   x [E, max_m, k], out [E, max_m, I]; only active rows are read or written.
+ * Requires n % 16 == 0 (I a multiple of 8).  The activation step between the
+ * gate/up and down grouped GEMMs (sglang PR #32385, "Cause": the SiLU-mul
+ * step on the masked layout writes only rows below masked_m), fused here so
+ * the 2 I-wide gate/up product never reaches memory.
+ */
+gg_status gg_forward_silu_mul(const void* x, const void* w13,
+                              const int32_t* offs, void* out,
+                              gg_dtype out_dtype, int64_t m, int64_t k,
+                              int64_t n, int32_t num_groups, void* stream);
+gg_status gg_masked_forward_silu_mul(const void* x, const void* w13,
+                                     const int32_t* masked_m, void* out,
+                                     gg_dtype out_dtype, int64_t max_m,
+                                     int64_t k, int64_t n,
+                                     int32_t num_groups, void* stream);
+
+/*
  * Scaled and accumulating forms of the six passes:
  *
  *   out = alpha * P + beta * out          (P = the pass's grouped product)

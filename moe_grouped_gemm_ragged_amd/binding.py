@@ -63,7 +63,7 @@ def load():
     I32 = ctypes.c_int32
     sig = [P, P, P, P, ctypes.c_int, I64, I64, I64, I32, P]
     for name in ("gg_forward", "gg_dgrad", "gg_wgrad", "gg_masked_forward", "gg_masked_dgrad",
-                 "gg_masked_wgrad"):
+                 "gg_masked_wgrad", "gg_forward_silu_mul", "gg_masked_forward_silu_mul"):
         f = getattr(lib, name)
         f.argtypes = sig
         f.restype = ctypes.c_int
@@ -296,4 +296,48 @@ def masked_wgrad(x, dy, masked_m, out=None, out_dtype=None, alpha=1.0, beta=0.0)
         raise ValueError(f"out must be [{e}, {k}, {n}]")
     _invoke("gg_masked_wgrad", x, dy, masked_m, out, _dtype_code(out.dtype), max_m, k, n, e, dev,
             alpha, beta)
+    return out
+
+
+def forward_silu_mul(x, w13, offs, out=None, out_dtype=None):
+    """out[i, c] = silu(G)[i, c] * U[i, c] with [G | U] = X[rows of g] .
+    W13[g] (gg_forward_silu_mul).  x: bf16 [m, k]; w13: bf16 [E, k, 2I]
+    (gate columns, then up); returns [m, I]."""
+    torch = _torch()
+    dev = x.device
+    _check(x, "x", torch.bfloat16, 2, dev)
+    _check(w13, "w13", torch.bfloat16, 3, dev)
+    _check(offs, "offs", torch.int32, 1, dev)
+    m, k = x.shape
+    e, k2, n = w13.shape
+    if k2 != k or offs.shape[0] != e or n % 2:
+        raise ValueError("shape mismatch between x, w13 and offs")
+    if out is None:
+        out = torch.empty((m, n // 2), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check(out, "out", out.dtype, 2, dev)
+    if tuple(out.shape) != (m, n // 2):
+        raise ValueError(f"out must be [{m}, {n // 2}]")
+    _invoke("gg_forward_silu_mul", x, w13, offs, out, _dtype_code(out.dtype), m, k, n, e, dev)
+    return out
+
+
+def masked_forward_silu_mul(x, w13, masked_m, out=None, out_dtype=None):
+    """The masked layout's gate/up forward with the SiLU-mul activation
+    (gg_masked_forward_silu_mul): x bf16 [E, max_m, k] -> [E, max_m, I]."""
+    torch = _torch()
+    dev = x.device
+    _check(x, "x", torch.bfloat16, 3, dev)
+    _check(w13, "w13", torch.bfloat16, 3, dev)
+    _check(masked_m, "masked_m", torch.int32, 1, dev)
+    e, max_m, k = x.shape
+    e2, k2, n = w13.shape
+    if e2 != e or k2 != k or masked_m.shape[0] != e or n % 2:
+        raise ValueError("shape mismatch between x, w13 and masked_m")
+    if out is None:
+        out = torch.empty((e, max_m, n // 2), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check(out, "out", out.dtype, 3, dev)
+    if tuple(out.shape) != (e, max_m, n // 2):
+        raise ValueError(f"out must be [{e}, {max_m}, {n // 2}]")
+    _invoke("gg_masked_forward_silu_mul", x, w13, masked_m, out, _dtype_code(out.dtype), max_m, k, n,
+            e, dev)
     return out

@@ -165,6 +165,26 @@ gg_status gg_masked_wgrad(const void* x, const void* dy, const int32_t* masked_m
                             stream);
 }
 
+gg_status gg_forward_silu_mul(const void* x, const void* w13, const int32_t* offs, void* out,
+                              gg_dtype out_dtype, int64_t m, int64_t k, int64_t n,
+                              int32_t num_groups, void* stream) {
+  gg_status s = check(x, w13, offs, out, out_dtype, m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  if (n % 16 != 0) return fail(GG_ERR_BAD_DIM, "n (= 2 I) must be a multiple of 16");
+  return run(6, x, w13, offs, out, out_dtype, m, k, n, num_groups, 1.0f, 0.0f, stream);
+}
+
+gg_status gg_masked_forward_silu_mul(const void* x, const void* w13, const int32_t* masked_m,
+                                     void* out, gg_dtype out_dtype, int64_t max_m, int64_t k,
+                                     int64_t n, int32_t num_groups, void* stream) {
+  gg_status s = check(x, w13, masked_m, out, out_dtype, max_m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  if (n % 16 != 0) return fail(GG_ERR_BAD_DIM, "n (= 2 I) must be a multiple of 16");
+  s = masked_rows(max_m, num_groups);
+  if (s != GG_OK) return s;
+  return run(7, x, w13, masked_m, out, out_dtype, max_m, k, n, num_groups, 1.0f, 0.0f, stream);
+}
+
 gg_status gg_forward(const void* x, const void* w, const int32_t* offs, void* y, gg_dtype y_dtype,
                      int64_t m, int64_t k, int64_t n, int32_t num_groups, void* stream) {
   return gg_forward_ex(x, w, offs, y, y_dtype, m, k, n, num_groups, 1.0f, 0.0f, stream);

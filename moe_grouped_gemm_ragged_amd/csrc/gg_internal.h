@@ -9,7 +9,8 @@
 
 namespace gg {
 // mode: 0 forward, 1 dgrad, 2 wgrad, 3 masked forward, 4 masked dgrad,
-// 5 masked wgrad.  Arguments were
+// 5 masked wgrad, 6 forward with the SiLU-mul activation, 7 masked forward
+// with the SiLU-mul activation.  Arguments were
 // validated by the caller.  Writes alpha * product + beta * (prior output)
 // (the prior output is not read when beta == 0).  Launches one persistent
 // grid of at most num_cus workgroups on `stream`.

@@ -82,11 +82,18 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 
 #define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-enum Mode { FWD = 0, DGRAD = 1, WGRAD = 2, MASKED = 3, MASKED_DGRAD = 4, MASKED_WGRAD = 5 };
+enum Mode {
+  FWD = 0, DGRAD = 1, WGRAD = 2, MASKED = 3, MASKED_DGRAD = 4, MASKED_WGRAD = 5,
+  FWD_SILU = 6, MASKED_SILU = 7
+};
 
 // The masked modes are the ragged passes on the masked layout: expert e's
-// rows start at e * max_m and its active count is masked_m[e].
-constexpr bool is_masked(int mode) { return mode >= MASKED; }
+// rows start at e * max_m and its active count is masked_m[e].  The SiLU
+// modes are forwards whose epilogue applies the gate/up activation.
+constexpr bool is_masked(int mode) {
+  return mode == MASKED || mode == MASKED_DGRAD || mode == MASKED_WGRAD || mode == MASKED_SILU;
+}
+constexpr bool is_silu(int mode) { return mode == FWD_SILU || mode == MASKED_SILU; }
 constexpr bool is_wgrad(int mode) { return mode == WGRAD || mode == MASKED_WGRAD; }
 constexpr bool is_dgrad(int mode) { return mode == DGRAD || mode == MASKED_DGRAD; }
 
@@ -112,6 +119,8 @@ struct Operand {
   int32_t rows;       // red-contig: valid tile rows (>= 1)
   int32_t red;        // valid reduction length
   uint32_t row_tail;  // red-strided: bytes from the tile's first row to the end of a memory row
+  uint32_t split;     // red-strided: extra byte offset of tile rows 128.. (the up half of a
+                      // gate/up panel; 0 otherwise)
 };
 
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // gfx9 raw buffer, 32-bit dwords
@@ -174,7 +183,8 @@ __device__ __forceinline__ DmaCtx dma_ctx(const Operand& op, int q0, int tid) {
     const uint32_t nrec = left > 0 ? (uint32_t)(left - 1) * op.ld_bytes + op.row_tail : 0u;
     c.rs = make_rsrc(op.origin + (int64_t)q0 * op.ld_bytes, nrec);
     const int chunk = (lane & 7) ^ (4 * ((lane >> 4) & 1));
-    c.voff = (uint32_t)((lane >> 3) + 16 * (w & 1)) * op.ld_bytes + (uint32_t)(128 * (w >> 1) + 16 * chunk);
+    c.voff = (uint32_t)((lane >> 3) + 16 * (w & 1)) * op.ld_bytes + (uint32_t)(128 * (w >> 1) + 16 * chunk) +
+             (w >= 4 ? op.split : 0u);
     c.step = 8u * op.ld_bytes;
   } else {
     // load j of wave w covers tile rows 32 w + 16 j .. + 15; lane i: row
@@ -296,6 +306,13 @@ __device__ __forceinline__ void load_stage(const Operand& A, const Operand& B, i
   for (int j = 0; j < 2; ++j) dma_load(ca, buf, wave, j);
 #pragma unroll
   for (int j = 0; j < 2; ++j) dma_load(cb, buf + OP_BYTES, wave, j);
+}
+
+// LDS operations of this wave complete, then all waves meet (no wait on
+// global memory operations).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
+  asm volatile("s_barrier" ::: "memory");
 }
 
 // Wait until at most n global->LDS loads of this wave are in flight, then
@@ -571,6 +588,71 @@ __device__ __forceinline__ void store_tile_lds(uint8_t* cbase, uint32_t ldc_byte
   }
 }
 
+// The SiLU-mul epilogue of a gate/up tile: waves 0, 1 (mod 4) hold the gate
+// columns 64 wn .. of the tile's 128 activation columns and waves 2, 3 the
+// matching up columns, so the two halves meet in LDS.  Per block row every
+// wave writes its 32 x 64 fp32 slab (as store_tile_lds does), all waves
+// meet, then each gate wave reads 8 consecutive gate values per lane from
+// its own slab and the 8 matching up values from its partner's (wave + 2),
+// writes silu(g) * u = g / (1 + exp(-g)) * u in fp32, rounded once to the
+// output type, and all waves meet again before the slabs are rewritten.
+// `slabs` is the idle stage-buffer area; each wave's slab is 16 KB apart.
+template <int TMA, bool OUT_F32>
+__device__ __forceinline__ void store_tile_silu(uint8_t* cbase, uint32_t ldc_bytes, int rows, int cols,
+                                                int wave, int wm, int wn, int lane,
+                                                const floatx16 (&acc)[TM][TN], uint8_t* slabs) {
+  constexpr uint32_t esz = OUT_F32 ? 4 : 2;
+  constexpr uint32_t kSlabStride = STAGE_BYTES / 2;
+  const uint32_t nrec = (uint32_t)(rows - 1) * ldc_bytes + (uint32_t)cols * esz;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(cbase, nrec);
+  uint8_t* own = slabs + wave * kSlabStride;
+  const uint8_t* partner = slabs + (wave + 2) * kSlabStride;     // read by gate waves only
+  const uint32_t wslab = opaque_v((uint32_t)((lane & 31) * kSlabPitch + 16 * (lane >> 5)));
+  const uint32_t rslab = opaque_v((uint32_t)((lane >> 3) * kSlabPitch + 32 * (lane & 7)));
+  const bool gate_wave = wn < 2;
+  const int gcol = 64 * wn + 8 * (lane & 7);      // activation column (gate waves)
+  const bool col_ok = gcol < cols;
+  const uint32_t gbase = col_ok ? opaque_v((uint32_t)(32 * TMA * wm + (lane >> 3)) * ldc_bytes +
+                                           (uint32_t)gcol * esz)
+                                : kOutOfRange;
+#pragma unroll
+  for (int i = 0; i < TMA; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        floatx4 v = {acc[i][j][4 * rr + 0], acc[i][j][4 * rr + 1], acc[i][j][4 * rr + 2], acc[i][j][4 * rr + 3]};
+        *reinterpret_cast<floatx4*>(own + wslab + 4 * (32 * j + 8 * rr)) = v;
+      }
+    lds_barrier();
+    if (gate_wave) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float g[8], u[8], o[8];
+        *reinterpret_cast<floatx4*>(&g[0]) = *reinterpret_cast<const floatx4*>(own + rslab + 8 * q * kSlabPitch);
+        *reinterpret_cast<floatx4*>(&g[4]) = *reinterpret_cast<const floatx4*>(own + rslab + 8 * q * kSlabPitch + 16);
+        *reinterpret_cast<floatx4*>(&u[0]) = *reinterpret_cast<const floatx4*>(partner + rslab + 8 * q * kSlabPitch);
+        *reinterpret_cast<floatx4*>(&u[4]) = *reinterpret_cast<const floatx4*>(partner + rslab + 8 * q * kSlabPitch + 16);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = g[e] / (1.0f + __expf(-g[e])) * u[e];
+        const uint32_t voff = gbase + (uint32_t)(32 * i + 8 * q) * ldc_bytes;
+        if constexpr (OUT_F32) {
+          const floatx4 lo = {o[0], o[1], o[2], o[3]};
+          const floatx4 hi = {o[4], o[5], o[6], o[7]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), rs, voff, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), rs, voff + 16, 0, 0);
+        } else {
+          const u32x4 w = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]),
+                           pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+          __builtin_amdgcn_raw_buffer_store_b128(w, rs, voff, 0, 0);
+        }
+      }
+    }
+    // every slab is rewritten by the next block row
+    lds_barrier();
+  }
+}
+
 // ---- group decode (prologue) ---------------------------------------------------
 
 // Block-wide inclusive scan of one int per thread (sum or max).
@@ -701,12 +783,6 @@ struct Tile {
   int rows, cols;       // valid output rows / columns of the tile
 };
 
-// LDS operations of this wave complete, then all waves meet (no wait on
-// global memory operations).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt unconstrained
-  asm volatile("s_barrier" ::: "memory");
-}
 
 template <int MODE, bool OUT_F32>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
@@ -729,9 +805,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
 
   decode_groups<MODE>(p, s_start, s_end, s_pref, s_scan, tid);
 
-  // Output tile grid.
-  const int64_t out_cols = is_dgrad(MODE) ? p.k : p.n;
-  const int col_tiles = (int)((out_cols + BN - 1) / BN);
+  // Output tile grid.  A SiLU tile writes 128 activation columns from a
+  // 256-column panel: 128 gate columns and the 128 matching up columns.
+  constexpr int kOutCols = is_silu(MODE) ? BN / 2 : BN;
+  const int64_t out_cols = is_dgrad(MODE) ? p.k : is_silu(MODE) ? p.n / 2 : p.n;
+  const int col_tiles = (int)((out_cols + kOutCols - 1) / kOutCols);
   int64_t total;
   int row_tiles_w = 0;
   if constexpr (is_wgrad(MODE)) {
@@ -766,9 +844,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     } else {
       strip_order(u, total / col_tiles, col_tiles, rt_all, ct);
     }
-    const int col0 = ct * BN;
+    const int col0 = ct * kOutCols;
     Operand& A = T.A;
     Operand& B = T.B;
+    A.split = 0;
+    B.split = 0;
     if constexpr (is_wgrad(MODE)) {
       const int g = (int)(rt_all / row_tiles_w);
       const int rt = (int)(rt_all % row_tiles_w);
@@ -827,6 +907,15 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
         B.row_tail = (uint32_t)(2 * (p.n - col0));
         T.ldc_bytes = (uint32_t)(esz * p.n);
         T.cbase = pc + esz * (arow * p.n + col0);
+        if constexpr (is_silu(MODE)) {
+          // gate columns col0.. in tile rows 0..127, up columns I + col0..
+          // in tile rows 128..255; the output is the I-wide activation
+          const int64_t half_n = p.n / 2;
+          B.split = (uint32_t)(2 * (half_n - BN / 2));
+          B.rows = (int)(half_n - col0 < kOutCols ? half_n - col0 : kOutCols);
+          T.ldc_bytes = (uint32_t)(esz * half_n);
+          T.cbase = pc + esz * (arow * half_n + col0);
+        }
       }
       T.rows = rows;
       T.cols = B.rows;
@@ -873,7 +962,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
                                          smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
                                          cur.B, tid, wave, faa, fab, acc, prev_stores);
     const int64_t tn = t + gridDim.x;
-    if (OUT_F32 && !scaled) {
+    if (OUT_F32 && !scaled && !is_silu(MODE)) {
       // Every wave is done reading this tile's stages: issue the next
       // tile's prologue loads first, then this tile's stores, so the
       // stores drain while those loads are in flight.  (Loads of stages
@@ -898,7 +987,14 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
       stage_barrier();
       // each wave stages through its own 16 KB of the (idle) stage buffers
       uint8_t* slab = smem + wave * (STAGE_BYTES / 2);
-      if (scaled) {
+      if constexpr (is_silu(MODE)) {
+        if (half)
+          store_tile_silu<2, OUT_F32>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wave, wm, wn, lane,
+                                      acc, smem);
+        else
+          store_tile_silu<TM, OUT_F32>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wave, wm, wn, lane,
+                                       acc, smem);
+      } else if (scaled) {
         if (half)
           store_tile_lds<2, OUT_F32, true>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane,
                                            acc, slab, p.alpha, p.beta);
@@ -941,6 +1037,11 @@ static hipError_t launch_mode(const Params& p, bool out_f32, int grid, hipStream
 // row tile beyond ceil(rows / BM).
 static int64_t max_tiles(int mode, int64_t m, int64_t k, int64_t n, int64_t E) {
   if (is_wgrad(mode)) return E * ((k + BM - 1) / BM) * ((n + BN - 1) / BN);
+  if (is_silu(mode)) {
+    const int64_t ct = (n / 2 + BN / 2 - 1) / (BN / 2);
+    if (is_masked(mode)) return E * ((m + BM - 1) / BM) * ct;
+    return ((m + BM - 1) / BM + E) * ct;
+  }
   const int64_t cols = is_dgrad(mode) ? k : n;
   const int64_t ct = (cols + BN - 1) / BN;
   if (is_masked(mode)) return E * ((m + BM - 1) / BM) * ct;
@@ -971,6 +1072,8 @@ hipError_t launch(int mode, const void* a, const void* b, const int32_t* groups,
     case MASKED: return launch_mode<MASKED>(p, out_f32, grid, stream);
     case MASKED_DGRAD: return launch_mode<MASKED_DGRAD>(p, out_f32, grid, stream);
     case MASKED_WGRAD: return launch_mode<MASKED_WGRAD>(p, out_f32, grid, stream);
+    case FWD_SILU: return launch_mode<FWD_SILU>(p, out_f32, grid, stream);
+    case MASKED_SILU: return launch_mode<MASKED_SILU>(p, out_f32, grid, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -102,6 +102,16 @@ def test_scaled_entry_points_check_like_the_plain_ones(lib, name, case, status):
     assert rc == status, (name, case, rc, gg.last_error())
 
 
+@pytest.mark.parametrize("name", ["gg_forward_silu_mul", "gg_masked_forward_silu_mul"])
+@pytest.mark.parametrize("case,status", [
+    (dict(a=0), 1), (dict(k=12), 2), (dict(n=24), 2), (dict(c=A + 4), 3), (dict(dt=9), 4),
+    (dict(e=0), 5),
+])
+def test_silu_mul_entry_points_check_arguments(lib, name, case, status):
+    rc = call(name, **case)
+    assert rc == status, (name, case, rc, gg.last_error())
+
+
 def test_binding_needs_out_to_accumulate():
     torch = pytest.importorskip("torch")
     x = torch.zeros(8, 8, dtype=torch.bfloat16)
