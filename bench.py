@@ -228,6 +228,14 @@ def main():
     dom = max(per_pass, key=lambda k: per_pass[k]["ms"])
     kernel_names = {"fwd": "grouped_gemm_kernel<0,false>", "dgrad": "grouped_gemm_kernel<1,false>",
                     "wgrad": "grouped_gemm_kernel<2,true>"}
+    # wgrad accumulating into the fp32 main-grad (beta = 1), same workload
+    _, msa = time_passes([("wgrad_acc", lambda: gg.wgrad(t["x"], t["dy"], t["offs"], out=dw, beta=1.0))],
+                         3, 1, torch)
+    acc_ms = sorted(msa["wgrad_acc"])[1]
+    per_pass["wgrad_accumulate"] = {"ms": round(acc_ms, 4),
+                                    "TFLOP/s": round(flop_pass / (acc_ms * 1e-3) / 1e12, 2),
+                                    "note": "dW += X^T dY into fp32 (gg_wgrad_ex, beta = 1); not in the step"}
+
     traffic = None
     if MEASURED_TRAFFIC["kernel_sha256"] == kernel_sha256():
         traffic = MEASURED_TRAFFIC["bytes"].get(dom)
@@ -263,17 +271,58 @@ def main():
                             "algorithmic_GB/s": round(algorithmic_bytes(w2, p) / (avg * 1e-3) / 1e9, 1)}
             context[name] = entry
             del t2, y2, dx2, dw2
+        # masked down-projection: forward and backward.  Its weights (201 MB)
+        # fit in the 256 MB MALL, so they rotate over three copies and every
+        # call streams them from HBM as a real layer would.
         wm = synth.masked_down()
-        tm = synth.make_inputs(wm, dev, need=("x", "w"))
+        tm = synth.make_inputs(wm, dev, need=("x", "w", "dy"))
+        wcopies = [tm["w"]] + [tm["w"].clone() for _ in range(2)]
         ym = torch.empty((wm.num_groups, wm.m, wm.n), dtype=torch.bfloat16, device=dev)
-        _, msm = time_passes([("masked", lambda: gg.masked_forward(tm["x"], tm["w"], tm["masked_m"], out=ym))],
-                             50, 5, torch)
-        avg = sorted(msm["masked"])[len(msm["masked"]) // 2]
+        dxm = torch.empty((wm.num_groups, wm.m, wm.k), dtype=torch.bfloat16, device=dev)
+        dwm = [torch.empty((wm.num_groups, wm.k, wm.n), dtype=torch.float32, device=dev) for _ in range(3)]
+        rot = {"i": 0}
+
+        def nxt():
+            rot["i"] = (rot["i"] + 1) % 3
+            return rot["i"]
         live = int((wm.group_sizes() > 0).sum())
-        mbytes = 2 * wm.active_rows() * (wm.k + wm.n) + 2 * live * wm.k * wm.n
-        context["masked_down"] = {"ms": round(avg, 4),
-                                  "TFLOP/s": round(wm.flops() / (avg * 1e-3) / 1e12, 2),
-                                  "algorithmic_GB/s": round(mbytes / (avg * 1e-3) / 1e9, 1)}
+        act_rows = wm.active_rows()
+        mb = {"masked_fwd": 2 * act_rows * (wm.k + wm.n) + 2 * live * wm.k * wm.n,
+              "masked_dgrad": 2 * act_rows * (wm.k + wm.n) + 2 * live * wm.k * wm.n,
+              "masked_wgrad": 2 * act_rows * (wm.k + wm.n) + 4 * wm.num_groups * wm.k * wm.n}
+        fm = [("masked_fwd", lambda: gg.masked_forward(tm["x"], wcopies[nxt()], tm["masked_m"], out=ym)),
+              ("masked_dgrad", lambda: gg.masked_dgrad(tm["dy"], wcopies[nxt()], tm["masked_m"], out=dxm)),
+              ("masked_wgrad", lambda: gg.masked_wgrad(tm["x"], tm["dy"], tm["masked_m"], out=dwm[nxt()]))]
+        _, msm = time_passes(fm, 30, 5, torch)
+        entry = {"weights": "rotated over 3 copies (HBM-resident per call)"}
+        for name, v in msm.items():
+            avg = sorted(v)[len(v) // 2]
+            entry[name] = {"ms": round(avg, 4), "TFLOP/s": round(wm.flops() / (avg * 1e-3) / 1e12, 2),
+                           "algorithmic_GB/s": round(mb[name] / (avg * 1e-3) / 1e9, 1)}
+        context["masked_down"] = entry
+        del tm, wcopies, ym, dxm, dwm
+        torch.cuda.empty_cache()
+
+        # Qwen3 gate/up with the SiLU-mul activation fused into the epilogue,
+        # against the plain forward followed by torch's SiLU-mul
+        wq = synth.qwen3_gateup()
+        tq = synth.make_inputs(wq, dev, need=("x", "w"))
+        inter = wq.n // 2
+        aq = torch.empty((wq.m, inter), dtype=torch.bfloat16, device=dev)
+        hq = torch.empty((wq.m, wq.n), dtype=torch.bfloat16, device=dev)
+
+        def unfused():
+            gg.forward(tq["x"], tq["w"], tq["offs"], out=hq)
+            torch.mul(torch.nn.functional.silu(hq[:, :inter]), hq[:, inter:], out=aq)
+        _, msq = time_passes([("fused", lambda: gg.forward_silu_mul(tq["x"], tq["w"], tq["offs"], out=aq)),
+                              ("unfused", unfused)], 10, 3, torch)
+        fq = {k: sorted(v)[len(v) // 2] for k, v in msq.items()}
+        context["qwen3_gateup_silu_mul"] = {
+            "fused_ms": round(fq["fused"], 4),
+            "fused_TFLOP/s": round(wq.flops() / (fq["fused"] * 1e-3) / 1e12, 2),
+            "unfused_ms": round(fq["unfused"], 4),
+            "unfused": "gg_forward to a bf16 [M, 2I] buffer, then torch silu(G) * U"}
+        del tq, aq, hq
         torch.cuda.empty_cache()
 
     cpu = None

@@ -591,10 +591,11 @@ __device__ __forceinline__ void store_tile_lds(uint8_t* cbase, uint32_t ldc_byte
 // The SiLU-mul epilogue of a gate/up tile: waves 0, 1 (mod 4) hold the gate
 // columns 64 wn .. of the tile's 128 activation columns and waves 2, 3 the
 // matching up columns, so the two halves meet in LDS.  Per block row every
-// wave writes its 32 x 64 fp32 slab (as store_tile_lds does), all waves
-// meet, then each gate wave reads 8 consecutive gate values per lane from
-// its own slab and the 8 matching up values from its partner's (wave + 2),
-// writes silu(g) * u = g / (1 + exp(-g)) * u in fp32, rounded once to the
+// wave writes its 32 x 64 fp32 slab (as store_tile_lds does) and all waves
+// meet; then the gate wave and its up partner (wave + 2) share the slab
+// pair, the gate wave taking slab rows 0..15 and the up wave rows 16..31:
+// each lane reads 8 consecutive gate values and the 8 matching up values,
+// writes silu(g) * u = g * rcp(1 + exp(-g)) * u in fp32, rounded once to the
 // output type, and all waves meet again before the slabs are rewritten.
 // `slabs` is the idle stage-buffer area; each wave's slab is 16 KB apart.
 template <int TMA, bool OUT_F32>
@@ -606,11 +607,13 @@ __device__ __forceinline__ void store_tile_silu(uint8_t* cbase, uint32_t ldc_byt
   const uint32_t nrec = (uint32_t)(rows - 1) * ldc_bytes + (uint32_t)cols * esz;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(cbase, nrec);
   uint8_t* own = slabs + wave * kSlabStride;
-  const uint8_t* partner = slabs + (wave + 2) * kSlabStride;     // read by gate waves only
+  const bool gate_wave = wn < 2;
+  const uint8_t* gslab = slabs + (gate_wave ? wave : wave - 2) * kSlabStride;
+  const uint8_t* uslab = gslab + 2 * kSlabStride;
+  const int q0 = gate_wave ? 0 : 2;                // slab row groups this wave combines
   const uint32_t wslab = opaque_v((uint32_t)((lane & 31) * kSlabPitch + 16 * (lane >> 5)));
   const uint32_t rslab = opaque_v((uint32_t)((lane >> 3) * kSlabPitch + 32 * (lane & 7)));
-  const bool gate_wave = wn < 2;
-  const int gcol = 64 * wn + 8 * (lane & 7);      // activation column (gate waves)
+  const int gcol = 64 * (wn & 1) + 8 * (lane & 7);   // activation column
   const bool col_ok = gcol < cols;
   const uint32_t gbase = col_ok ? opaque_v((uint32_t)(32 * TMA * wm + (lane >> 3)) * ldc_bytes +
                                            (uint32_t)gcol * esz)
@@ -625,16 +628,17 @@ __device__ __forceinline__ void store_tile_silu(uint8_t* cbase, uint32_t ldc_byt
         *reinterpret_cast<floatx4*>(own + wslab + 4 * (32 * j + 8 * rr)) = v;
       }
     lds_barrier();
-    if (gate_wave) {
+    {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int qq = 0; qq < 2; ++qq) {
+        const int q = q0 + qq;
         float g[8], u[8], o[8];
-        *reinterpret_cast<floatx4*>(&g[0]) = *reinterpret_cast<const floatx4*>(own + rslab + 8 * q * kSlabPitch);
-        *reinterpret_cast<floatx4*>(&g[4]) = *reinterpret_cast<const floatx4*>(own + rslab + 8 * q * kSlabPitch + 16);
-        *reinterpret_cast<floatx4*>(&u[0]) = *reinterpret_cast<const floatx4*>(partner + rslab + 8 * q * kSlabPitch);
-        *reinterpret_cast<floatx4*>(&u[4]) = *reinterpret_cast<const floatx4*>(partner + rslab + 8 * q * kSlabPitch + 16);
+        *reinterpret_cast<floatx4*>(&g[0]) = *reinterpret_cast<const floatx4*>(gslab + rslab + 8 * q * kSlabPitch);
+        *reinterpret_cast<floatx4*>(&g[4]) = *reinterpret_cast<const floatx4*>(gslab + rslab + 8 * q * kSlabPitch + 16);
+        *reinterpret_cast<floatx4*>(&u[0]) = *reinterpret_cast<const floatx4*>(uslab + rslab + 8 * q * kSlabPitch);
+        *reinterpret_cast<floatx4*>(&u[4]) = *reinterpret_cast<const floatx4*>(uslab + rslab + 8 * q * kSlabPitch + 16);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = g[e] / (1.0f + __expf(-g[e])) * u[e];
+        for (int e = 0; e < 8; ++e) o[e] = g[e] * __builtin_amdgcn_rcpf(1.0f + __expf(-g[e])) * u[e];
         const uint32_t voff = gbase + (uint32_t)(32 * i + 8 * q) * ldc_bytes;
         if constexpr (OUT_F32) {
           const floatx4 lo = {o[0], o[1], o[2], o[3]};
