@@ -659,14 +659,14 @@ __device__ __forceinline__ void store_tile_silu(uint8_t* cbase, uint32_t ldc_byt
 
 // ---- group decode (prologue) ---------------------------------------------------
 
-// Block-wide inclusive scan of one int per thread (sum or max).
-template <bool MAX>
-__device__ __forceinline__ int block_scan_incl(int v, int* scratch, int tid) {
+// Block-wide inclusive scan of one value per thread (sum or max).
+template <bool MAX, typename T>
+__device__ __forceinline__ T block_scan_incl(T v, T* scratch, int tid) {
   scratch[tid] = v;
   __syncthreads();
 #pragma unroll
   for (int d = 1; d < NT; d <<= 1) {
-    int o = tid >= d ? scratch[tid - d] : (MAX ? 0 : 0);
+    T o = tid >= d ? scratch[tid - d] : T(0);
     __syncthreads();
     if (tid >= d) v = MAX ? (v > o ? v : o) : v + o;
     scratch[tid] = v;
@@ -675,12 +675,27 @@ __device__ __forceinline__ int block_scan_incl(int v, int* scratch, int tid) {
   return v;
 }
 
-// Fills s_start/s_end with the clamped row range of every group and, unless
-// a wgrad mode, s_pref[0..E] with the exclusive prefix of per-group row-tile
-// counts.
+// First row of group g within its row range (the ragged layout's groups
+// follow one another; a masked group's rows start at 0 of its block).
 template <int MODE>
-__device__ void decode_groups(const Params& p, int32_t* s_start, int32_t* s_end, int32_t* s_pref,
-                              int* scratch, int tid) {
+__device__ __forceinline__ int group_start(const int32_t* s_end, int g) {
+  return is_masked(MODE) || g == 0 ? 0 : s_end[g - 1];
+}
+
+// A group's last row tile runs at half height when it holds BM/2 rows or
+// fewer; every other row tile runs at full height.
+__device__ __forceinline__ int half_tiles(int rows) {
+  const int r = rows % BM;
+  return r != 0 && r <= BM / 2 ? 1 : 0;
+}
+
+// Fills s_end with the clamped end row of every group and, unless a wgrad
+// mode, s_pref[0..E] with the exclusive prefix of the groups' full-height
+// row-tile counts and s_half[0..E] with that of their half-height last
+// tiles (0 or 1 per group).
+template <int MODE>
+__device__ void decode_groups(const Params& p, int32_t* s_end, int32_t* s_pref, int32_t* s_half,
+                              int64_t* scratch, int tid) {
   const int E = p.num_groups;
   const int per = (E + NT - 1) / NT;
   const int g0 = tid * per;
@@ -690,7 +705,6 @@ __device__ void decode_groups(const Params& p, int32_t* s_start, int32_t* s_end,
       int a = p.groups[g];
       a = a < 0 ? 0 : a;
       a = a > p.m ? (int)p.m : a;
-      s_start[g] = 0;
       s_end[g] = a;
     }
   } else {
@@ -701,41 +715,51 @@ __device__ void decode_groups(const Params& p, int32_t* s_start, int32_t* s_end,
       run = o > run ? o : run;
       s_end[g] = run;
     }
-    const int incl = block_scan_incl<true>(run, scratch, tid);
-    int before = 0;
-    if (tid > 0) before = scratch[tid - 1];
-    (void)incl;
+    block_scan_incl<true, int64_t>(run, scratch, tid);
+    const int before = tid > 0 ? (int)scratch[tid - 1] : 0;
     __syncthreads();
     const int mcap = (int)p.m;
     for (int g = g0; g < g1; ++g) {
       int e = s_end[g] > before ? s_end[g] : before;
       s_end[g] = e < mcap ? e : mcap;
     }
-    __syncthreads();
-    for (int g = g0; g < g1; ++g) s_start[g] = g == 0 ? 0 : s_end[g - 1];
   }
   __syncthreads();
   if constexpr (!is_wgrad(MODE)) {
-    int local = 0;
-    for (int g = g0; g < g1; ++g) local += (s_end[g] - s_start[g] + BM - 1) / BM;
-    const int incl = block_scan_incl<false>(local, scratch, tid);
-    int run = incl - local;
+    // (full, half) counts packed as full + half * 2^32: both stay below 2^31
+    int64_t local = 0;
     for (int g = g0; g < g1; ++g) {
-      s_pref[g] = run;
-      run += (s_end[g] - s_start[g] + BM - 1) / BM;
+      const int rows = s_end[g] - group_start<MODE>(s_end, g);
+      const int h = half_tiles(rows);
+      local += (int64_t)((rows + BM - 1) / BM - h) + ((int64_t)h << 32);
     }
-    if (tid == NT - 1) s_pref[E] = incl;
+    const int64_t incl = block_scan_incl<false, int64_t>(local, scratch, tid);
+    int full = (int)((incl - local) & 0xffffffff);
+    int half = (int)((incl - local) >> 32);
+    for (int g = g0; g < g1; ++g) {
+      s_pref[g] = full;
+      s_half[g] = half;
+      const int rows = s_end[g] - group_start<MODE>(s_end, g);
+      const int h = half_tiles(rows);
+      full += (rows + BM - 1) / BM - h;
+      half += h;
+    }
+    if (tid == NT - 1) {
+      s_pref[E] = (int)(incl & 0xffffffff);
+      s_half[E] = (int)(incl >> 32);
+    }
     __syncthreads();
   }
 }
 
-// Largest g in [0, E) with s_pref[g] <= t (s_pref is non-decreasing,
-// s_pref[0] = 0 <= t).
-__device__ __forceinline__ int find_group(const int32_t* s_pref, int E, int t) {
-  int lo = 0, hi = E;          // invariant: s_pref[lo] <= t < s_pref[hi] (s_pref[E] = total)
+// Largest g in [0, E) with pref[g] <= t (pref is a non-decreasing
+// exclusive prefix, pref[0] = 0 <= t < pref[E]).  That group's count is
+// non-zero: pref[g] <= t < pref[g + 1].
+__device__ __forceinline__ int find_group(const int32_t* pref, int E, int t) {
+  int lo = 0, hi = E;          // invariant: pref[lo] <= t < pref[hi]
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
-    if (s_pref[mid] <= t) lo = mid; else hi = mid;
+    if (pref[mid] <= t) lo = mid; else hi = mid;
   }
   return lo;
 }
@@ -795,10 +819,10 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
 
   // LDS: NSTAGE stage buffers of 32 KB (A tile, then B tile).
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE_BYTES];
-  __shared__ int32_t s_start[GG_MAX_GROUPS_DEV];
   __shared__ int32_t s_end[GG_MAX_GROUPS_DEV];
   __shared__ int32_t s_pref[GG_MAX_GROUPS_DEV + 1];
-  __shared__ int s_scan[NT];
+  __shared__ int32_t s_half[GG_MAX_GROUPS_DEV + 1];
+  __shared__ int64_t s_scan[NT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -807,20 +831,25 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   const int wn = wave & 3;
   const int E = p.num_groups;
 
-  decode_groups<MODE>(p, s_start, s_end, s_pref, s_scan, tid);
+  decode_groups<MODE>(p, s_end, s_pref, s_half, s_scan, tid);
 
   // Output tile grid.  A SiLU tile writes 128 activation columns from a
   // 256-column panel: 128 gate columns and the 128 matching up columns.
   constexpr int kOutCols = is_silu(MODE) ? BN / 2 : BN;
   const int64_t out_cols = is_dgrad(MODE) ? p.k : is_silu(MODE) ? p.n / 2 : p.n;
   const int col_tiles = (int)((out_cols + kOutCols - 1) / kOutCols);
+  // Non-wgrad tiles come in two phases: every full-height row tile, then
+  // the half-height last tiles.  Tiles of one phase take the same time, so
+  // the workgroups of an XCD stay in step and share their panels in L2.
   int64_t total;
+  int64_t full_tiles = 0;
   int row_tiles_w = 0;
   if constexpr (is_wgrad(MODE)) {
     row_tiles_w = (int)((p.k + BM - 1) / BM);
     total = (int64_t)E * row_tiles_w * col_tiles;
   } else {
-    total = (int64_t)uniform(s_pref[E]) * col_tiles;
+    full_tiles = (int64_t)uniform(s_pref[E]) * col_tiles;
+    total = full_tiles + (int64_t)uniform(s_half[E]) * col_tiles;
   }
 
 
@@ -845,8 +874,10 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
       int64_t rr;
       strip_order(u - gq * per_g, row_tiles_w, col_tiles, rr, ct);
       rt_all = gq * row_tiles_w + rr;
+    } else if (u < full_tiles) {
+      strip_order(u, full_tiles / col_tiles, col_tiles, rt_all, ct);
     } else {
-      strip_order(u, total / col_tiles, col_tiles, rt_all, ct);
+      strip_order(u - full_tiles, (total - full_tiles) / col_tiles, col_tiles, rt_all, ct);
     }
     const int col0 = ct * kOutCols;
     Operand& A = T.A;
@@ -857,7 +888,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
       const int g = (int)(rt_all / row_tiles_w);
       const int rt = (int)(rt_all % row_tiles_w);
       const int row0 = rt * BM;                 // first k index of the tile
-      const int s = uniform(s_start[g]), e = uniform(s_end[g]);
+      const int s = uniform(group_start<MODE>(s_end, g)), e = uniform(s_end[g]);
       // first memory row of the expert's rows (masked: expert g's block)
       const int64_t srow = (is_masked(MODE) ? (int64_t)g * p.m : 0) + s;
       // A(row kk, red i) = X[srow + i, row0 + kk]
@@ -877,9 +908,12 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
       T.rows = A.rows;
       T.cols = B.rows;
     } else {
-      const int g = uniform(find_group(s_pref, E, (int)rt_all));
-      const int rt = (int)rt_all - uniform(s_pref[g]);
-      const int s = uniform(s_start[g]), e = uniform(s_end[g]);
+      // full phase: row tile rt_all - s_pref[g] of group g; half phase:
+      // the last row tile of group g
+      const bool in_full = u < full_tiles;
+      const int g = uniform(find_group(in_full ? s_pref : s_half, E, (int)rt_all));
+      const int s = uniform(group_start<MODE>(s_end, g)), e = uniform(s_end[g]);
+      const int rt = in_full ? (int)rt_all - uniform(s_pref[g]) : (e - s - 1) / BM;
       const int row0 = s + rt * BM;             // first expert row of the tile
       const int rows = (e - row0) < BM ? (e - row0) : BM;
       const int64_t arow = is_masked(MODE) ? (int64_t)g * p.m + row0 : (int64_t)row0;
