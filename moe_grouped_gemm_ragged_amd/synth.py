@@ -317,6 +317,114 @@ def make_inputs(wl: Workload, device="cpu", need=("x", "w", "dy")):
     return out
 
 
+# ---------------------------------------------------------------------------
+# fp8 (e4m3) operands with power-of-two block scales
+# ---------------------------------------------------------------------------
+
+E4M3_NAN = 0x7F                     # the e4m3 NaN code, marker for never-read rows
+SCALE_GARBAGE_F32 = 0.3             # a non-power-of-two scale, marker for never-read rows
+
+
+def fp8_masked_down(scale: str = "full") -> Workload:
+    """The masked down-projection of sglang PR #32385 in fp8 (its fp8
+    rollout: "Evidence", operand table, down A/B: 64 experts x 256 rows,
+    K = 768 (G = 6 scale blocks), N = 2048)."""
+    if scale == "full":
+        E, MAXM, K, N, seed = 64, 256, 768, 2048, 21
+    else:
+        E, MAXM, K, N, seed = 8, 256, 256, 320, 31
+    mm = uniform_masked_m(E, MAXM, seed)
+    return Workload("fp8_masked_down" + ("" if scale == "full" else "_small"),
+                    "masked", E, MAXM, K, N, seed=seed, masked_m=mm)
+
+
+def fp8_masked_gateup(scale: str = "full") -> Workload:
+    """The masked gate/up projection of the same step (operand table,
+    gateup A/B: 64 experts x 256 rows, K = 2048 (G = 16), N = 1536)."""
+    if scale == "full":
+        E, MAXM, K, N, seed = 64, 256, 2048, 1536, 22
+    else:
+        E, MAXM, K, N, seed = 8, 256, 384, 384, 32
+    mm = uniform_masked_m(E, MAXM, seed)
+    return Workload("fp8_masked_gateup" + ("" if scale == "full" else "_small"),
+                    "masked", E, MAXM, K, N, seed=seed, masked_m=mm)
+
+
+def fp8_repro() -> Workload:
+    """The minimal reproduction of sglang PR #32385 ("Evidence" 1): 8
+    experts, max_m 128, K = 768, N = 2048, 8 active rows per expert."""
+    return Workload("fp8_repro", "masked", 8, 128, 768, 2048, seed=23,
+                    masked_m=np.full(8, 8, dtype=np.int32))
+
+
+def fp8_qwen3_gateup(scale: str = "full") -> Workload:
+    """The ragged Qwen3 gate/up recipe (see qwen3_gateup) in fp8."""
+    wl = qwen3_gateup(scale)
+    wl.name = "fp8_" + wl.name
+    return wl
+
+
+def fp8_glm_up(scale: str = "full") -> Workload:
+    """The GLM-up recipe (see glm_up) in fp8."""
+    wl = glm_up(scale)
+    wl.name = "fp8_" + wl.name
+    return wl
+
+
+FULL.update({"fp8_masked_down": fp8_masked_down, "fp8_masked_gateup": fp8_masked_gateup,
+             "fp8_repro": lambda scale="full": fp8_repro(),
+             "fp8_qwen3_gateup": fp8_qwen3_gateup, "fp8_glm_up": fp8_glm_up})
+
+
+def _quantize_e4m3_blocks(t):
+    """Per row and per 128 values along the last dim: a power-of-two scale
+    2^ceil(log2(amax / 448)) (1.0 for an all-zero block; the rounding rule of
+    the quantizer in sglang PR #32385, "Cause") and the e4m3 codes of t /
+    scale by torch's cast.  Returns (uint8 codes, fp32 scales [..., G])."""
+    import torch
+    *lead, k = t.shape
+    g = (k + 127) // 128
+    pad = g * 128 - k
+    tp = torch.nn.functional.pad(t, (0, pad)) if pad else t
+    blocks = tp.reshape(*lead, g, 128)
+    amax = blocks.abs().amax(dim=-1)
+    scale = torch.where(amax > 0, torch.exp2(torch.ceil(torch.log2(amax / 448.0))),
+                        torch.ones_like(amax))
+    q = (blocks / scale.unsqueeze(-1)).reshape(*lead, g * 128)[..., :k]
+    codes = q.to(torch.float8_e4m3fn).view(torch.uint8)
+    return codes.contiguous(), scale.to(torch.float32).contiguous()
+
+
+def make_fp8_inputs(wl: Workload, device="cpu"):
+    """Draw the fp8 operands of ``wl`` on ``device``: ``x8`` uint8 e4m3
+    [M, K] (masked: [E, max_m, K]) with ``sx`` fp32 [..., ceil(K/128)], and
+    ``w8`` uint8 e4m3 [E, N, K] (K contiguous) with ``sw`` fp32
+    [E, N, ceil(K/128)]; every scale a power of two.  In the masked layout
+    the inactive rows hold the e4m3 NaN code and the non-power-of-two scale
+    0.3, so a read of either would show."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(wl.seed) * 1000003 + 11)
+    x = torch.randn(wl.x_shape(), generator=g, device=device, dtype=torch.float32) * wl.x_std
+    g.manual_seed(int(wl.seed) * 1000003 + 12)
+    w = torch.randn((wl.num_groups, wl.n, wl.k), generator=g, device=device,
+                    dtype=torch.float32) * wl.w_std
+    x8, sx = _quantize_e4m3_blocks(x)
+    del x
+    w8, sw = _quantize_e4m3_blocks(w)
+    del w
+    out = {"x8": x8, "sx": sx, "w8": w8, "sw": sw}
+    if wl.layout == "masked":
+        sizes = wl.group_sizes()
+        for e in range(wl.num_groups):
+            x8[e, int(sizes[e]):, :] = E4M3_NAN
+            sx[e, int(sizes[e]):, :] = SCALE_GARBAGE_F32
+        out["masked_m"] = torch.from_numpy(wl.masked_m.astype(np.int32)).to(device)
+    else:
+        out["offs"] = torch.from_numpy(wl.offs.astype(np.int32)).to(device)
+    return out
+
+
 def bf16_bits(t) -> np.ndarray:
     """A bf16 torch tensor's bit patterns as a host uint16 array."""
     import torch

@@ -1,4 +1,5 @@
-"""fp64 CPU oracle for the bf16 grouped GEMM -- TEST INFRASTRUCTURE ONLY.
+"""fp64 CPU oracle for the bf16 grouped GEMM and its fp8 block-scaled
+forward -- TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The HIP library and its Python binding
@@ -11,7 +12,9 @@ top of ``oracle.c``; ``apply_alpha_beta`` adds the scaled, accumulating form
 out = alpha * P + beta * C of every pass, combined in fp64 before the one
 rounding.  Parity is pinned against exact rational brute force,
 closed forms, the three-pass adjoint identity and numpy's float64 matmul in
-``tests/test_oracle.py``; no function here is "parity unpinned".
+``tests/test_oracle.py``, and the fp8 functions against torch's e4m3
+decoding, exact rational brute force and numpy's matmul in
+``tests/test_oracle_fp8.py``; no function here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -62,6 +65,12 @@ def _load():
     lib.oracle_round_bf16_array.restype = None
     lib.oracle_decode_bf16.argtypes = [ctypes.c_uint16]
     lib.oracle_decode_bf16.restype = ctypes.c_double
+    for name in ("oracle_fp8_forward", "oracle_fp8_masked_forward"):
+        f = getattr(lib, name)
+        f.argtypes = [P, P, P, P, P, I64, I64, I64, I32, P, I64, P, P, P]
+        f.restype = ctypes.c_int
+    lib.oracle_decode_e4m3.argtypes = [ctypes.c_uint8]
+    lib.oracle_decode_e4m3.restype = ctypes.c_double
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ctypes.c_int
     _lib = lib
@@ -319,3 +328,94 @@ def masked_forward_silu_mul(x, w13, masked_m, rows=None) -> Result:
     gate = masked_forward(x, np.ascontiguousarray(w13[:, :, :i]), masked_m, rows=rows)
     up = masked_forward(x, np.ascontiguousarray(w13[:, :, i:]), masked_m, rows=rows)
     return _silu_mul(gate, up)
+
+
+# ---- FP8 (e4m3) block-scaled forward ------------------------------------------
+
+def decode_e4m3(b: int) -> float:
+    """One e4m3 byte -> its value (oracle_decode_e4m3: OCP E4M3, bias 7,
+    NaN only at S.1111.111, no infinities)."""
+    return float(_load().oracle_decode_e4m3(int(b) & 0xFF))
+
+
+def _u8(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint8:
+        raise TypeError("fp8 operands are passed as uint8 byte arrays")
+    return a
+
+
+def _f32(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.float32)
+
+
+def fp8_forward(x, sx, w, sw, offs, rows=None) -> Result:
+    """Rows of the ragged fp8 block-scaled forward (oracle_fp8_forward):
+    Y[i, n] = sum_k x[i, k] sx[i, k // 128] w[g, n, k] sw[g, n, k // 128].
+    x: uint8 e4m3 [M, K]; sx: fp32 [M, ceil(K/128)]; w: uint8 e4m3
+    [E, N, K]; sw: fp32 [E, N, ceil(K/128)]; offs: int32 [E] end offsets."""
+    x, w = _u8(x), _u8(w)
+    sx, sw = _f32(sx), _f32(sw)
+    offs = np.ascontiguousarray(offs, dtype=np.int32)
+    m, k = x.shape
+    e, n, k2 = w.shape
+    kb = (k + 127) // 128
+    assert k2 == k and offs.shape == (e,) and sx.shape == (m, kb) and sw.shape == (e, n, kb)
+    sel = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    count = m if sel is None else len(sel)
+    lib = _load()
+    value = np.full((count, n), np.nan, dtype=np.float64)
+    sabs = np.full((count, n), np.nan, dtype=np.float64)
+    status = np.zeros(count, dtype=np.int32)
+    rc = lib.oracle_fp8_forward(_ptr(x), _ptr(sx), _ptr(w), _ptr(sw), _ptr(offs),
+                                ctypes.c_int64(m), ctypes.c_int64(k), ctypes.c_int64(n),
+                                ctypes.c_int32(e), _ptr(sel),
+                                ctypes.c_int64(0 if sel is None else len(sel)),
+                                _ptr(value), _ptr(sabs), _ptr(status))
+    if rc != 0:
+        raise ValueError(f"oracle_fp8_forward rejected its arguments (code {rc})")
+    return Result(value, sabs, status, sel if sel is not None else np.arange(m))
+
+
+def fp8_masked_forward(x, sx, w, sw, masked_m, rows=None) -> Result:
+    """Rows of the masked fp8 block-scaled forward
+    (oracle_fp8_masked_forward).  x: uint8 [E, max_m, K]; sx: fp32
+    [E, max_m, ceil(K/128)]; w, sw as in fp8_forward; rows: flat indices
+    e*max_m + r, or None for all.  Inactive rows' values and scales are
+    never read."""
+    x, w = _u8(x), _u8(w)
+    sx, sw = _f32(sx), _f32(sw)
+    masked_m = np.ascontiguousarray(masked_m, dtype=np.int32)
+    e, max_m, k = x.shape
+    e2, n, k2 = w.shape
+    kb = (k + 127) // 128
+    assert e2 == e and k2 == k and masked_m.shape == (e,)
+    assert sx.shape == (e, max_m, kb) and sw.shape == (e, n, kb)
+    sel = None if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+    count = e * max_m if sel is None else len(sel)
+    lib = _load()
+    value = np.full((count, n), np.nan, dtype=np.float64)
+    sabs = np.full((count, n), np.nan, dtype=np.float64)
+    status = np.zeros(count, dtype=np.int32)
+    rc = lib.oracle_fp8_masked_forward(_ptr(x), _ptr(sx), _ptr(w), _ptr(sw), _ptr(masked_m),
+                                       ctypes.c_int64(max_m), ctypes.c_int64(k),
+                                       ctypes.c_int64(n), ctypes.c_int32(e), _ptr(sel),
+                                       ctypes.c_int64(0 if sel is None else len(sel)),
+                                       _ptr(value), _ptr(sabs), _ptr(status))
+    if rc != 0:
+        raise ValueError(f"oracle_fp8_masked_forward rejected its arguments (code {rc})")
+    return Result(value, sabs, status, sel if sel is not None else np.arange(e * max_m))
+
+
+def ue8m0_violations(scales, active=None) -> int:
+    """Number of fp32 scales that are not UE8M0: whose sign or mantissa bits
+    are set (sglang PR #32385, "Problem": the check masks an fp32 with
+    0x807fffff and wants zero, which admits +0.0 and every positive power of
+    two).  active: a boolean mask of the same shape selecting the entries
+    that count (inactive rows are not validated, "Rejected alternatives"),
+    or None for all."""
+    bits = np.ascontiguousarray(scales, dtype=np.float32).view(np.uint32)
+    bad = (bits & np.uint32(0x807FFFFF)) != 0
+    if active is not None:
+        bad = bad & np.asarray(active, dtype=bool)
+    return int(bad.sum())

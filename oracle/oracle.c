@@ -1,6 +1,7 @@
 /*
  * oracle.c -- plain, slow, fp64 CPU oracle for the bf16 grouped (ragged,
- * per-expert) GEMM.  TEST INFRASTRUCTURE ONLY: the HIP library never links,
+ * per-expert) GEMM and its fp8 block-scaled forward (stated with the fp8
+ * functions below).  TEST INFRASTRUCTURE ONLY: the HIP library never links,
  * loads or calls this file, and this file shares no code with it.
  *
  * What it computes (restated from the pages, not copied):
@@ -335,6 +336,109 @@ int oracle_masked_wgrad(const uint16_t* x, const uint16_t* dy,
                 sr[j] += fabs(p);
             }
         }
+    }
+    return 0;
+}
+
+/* ---- FP8 (e4m3) block-scaled forward ------------------------------------- */
+/*
+ * sglang PR #32385 runs the masked MoE GEMMs of its fp8 rollout on fp8
+ * operands with one scale per 128 reduction values ("Cause": G = D / 128 in
+ * the table of models; "Evidence": activation scales of shape (E, max_m, G)
+ * and weight scales per (expert, output column, k-block) in the operand
+ * table), every scale a positive power of two -- UE8M0 -- checked by
+ * masking an fp32's sign and mantissa bits ("Problem").  The weight is the
+ * "nt" operand of that call: W[E, N, K], K contiguous.  So
+ *
+ *   Y[i, n] = sum_kk  x(i, kk) sx[i, kk / 128]  *  w(g, n, kk) sw[g, n, kk / 128]
+ *
+ * over the rows i of expert g, with x, w the e4m3 values and sx, sw the
+ * scales (fp32 values).  The sums run in fp64; a product of two e4m3 values
+ * and two powers of two is exact there.
+ *
+ * e4m3 here is the OCP 8-bit float with 4 exponent bits (bias 7) and 3
+ * mantissa bits, no infinities, and NaN only at S.1111.111: a normal value
+ * is (1 + m/8) 2^(e-7), a subnormal (e = 0) is m 2^-9, the largest 448. */
+static double e4m3_decode(uint8_t b) {
+    int sgn = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp((double)(8 + m), e - 10);   /* (1 + m/8) 2^(e-7) */
+    return sgn ? -v : v;
+}
+
+double oracle_decode_e4m3(uint8_t b) { return e4m3_decode(b); }
+
+/* One output row of the fp8 forward: xr, sxr the row's values and scales,
+ * wg, swg the expert's weight [n, k] and scales [n, kb]. */
+static void fp8_row(const uint8_t* xr, const float* sxr, const uint8_t* wg,
+                    const float* swg, int64_t k, int64_t n, double* yr, double* sr) {
+    int64_t kb = (k + 127) / 128;
+    for (int64_t j = 0; j < n; ++j) {
+        double acc = 0.0, sabs = 0.0;
+        const uint8_t* wr = wg + j * k;
+        const float* swr = swg + j * kb;
+        for (int64_t kk = 0; kk < k; ++kk) {
+            double a = e4m3_decode(xr[kk]) * (double)sxr[kk / 128];
+            double p = a * (e4m3_decode(wr[kk]) * (double)swr[kk / 128]);
+            acc += p;
+            sabs += fabs(p);
+        }
+        yr[j] = acc;
+        sr[j] = sabs;
+    }
+}
+
+/* Ragged layout: x [m, k], sx [m, kb], w [E, n, k], sw [E, n, kb] with
+ * kb = ceil(k / 128); the offsets as in oracle_forward. */
+int oracle_fp8_forward(const uint8_t* x, const float* sx, const uint8_t* w,
+                       const float* sw, const int32_t* offs, int64_t m, int64_t k,
+                       int64_t n, int32_t num_groups, const int64_t* rows,
+                       int64_t nrows, double* y, double* s, int32_t* status) {
+    if (num_groups < 1 || num_groups > ORACLE_MAX_GROUPS) return -1;
+    int64_t* ends = (int64_t*)malloc(sizeof(int64_t) * (size_t)num_groups);
+    if (!ends) return -2;
+    group_ends(offs, num_groups, m, ends);
+    int64_t kb = (k + 127) / 128;
+    int64_t count = rows ? nrows : m;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < count; ++r) {
+        int64_t i = rows ? rows[r] : r;
+        int32_t g = (i >= 0 && i < m) ? group_of_row(ends, num_groups, i) : -1;
+        status[r] = g >= 0;
+        if (g < 0) continue;
+        fp8_row(x + i * k, sx + i * kb, w + (int64_t)g * n * k, sw + (int64_t)g * n * kb,
+                k, n, y + r * n, s + r * n);
+    }
+    free(ends);
+    return 0;
+}
+
+/* Masked layout: x [E, max_m, k], sx [E, max_m, kb], w [E, n, k],
+ * sw [E, n, kb]; rows r < masked_m[e] are active, the others (values and
+ * scales alike) are never read.  rows: flat indices e*max_m + r. */
+int oracle_fp8_masked_forward(const uint8_t* x, const float* sx, const uint8_t* w,
+                              const float* sw, const int32_t* masked_m, int64_t max_m,
+                              int64_t k, int64_t n, int32_t num_groups,
+                              const int64_t* rows, int64_t nrows, double* y, double* s,
+                              int32_t* status) {
+    if (num_groups < 1) return -1;
+    int64_t kb = (k + 127) / 128;
+    int64_t total = (int64_t)num_groups * max_m;
+    int64_t count = rows ? nrows : total;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < count; ++r) {
+        int64_t flat = rows ? rows[r] : r;
+        int ok = flat >= 0 && flat < total;
+        int64_t e = ok ? flat / max_m : 0, row = ok ? flat % max_m : 0;
+        if (ok) ok = row < masked_active(masked_m, e, max_m);
+        status[r] = ok;
+        if (!ok) continue;
+        fp8_row(x + flat * k, sx + flat * kb, w + e * n * k, sw + e * n * kb, k, n,
+                y + r * n, s + r * n);
     }
     return 0;
 }
