@@ -232,6 +232,98 @@ gg_status gg_masked_wgrad_ex(const void* x, const void* dy,
                              int64_t n, int32_t num_groups, float alpha,
                              float beta, void* stream);
 
+/*
+ * FP8 (e4m3) block-scaled forward
+ * -------------------------------
+ * The fp8 form of the forward and masked forward (sglang PR #32385: the
+ * masked MoE GEMMs of an fp8 rollout, "Evidence" operand table and "Cause"
+ * model table): e4m3 operands (OCP E4M3, one byte each) with one power-of-
+ * two scale per row and 128 reduction values,
+ *
+ *   Y[i, n] = sum_k x[i, k] sx[i, k/128] * w[g, n, k] sw[g, n, k/128]
+ *
+ * over the rows i of expert g.  The weight is [E, n, k] with k contiguous
+ * (the "nt" operand of the page's call), and k must be a multiple of 128
+ * (G = k / 128 scale blocks).  Accumulation is fp32: the matrix cores sum
+ * each run of 64 products with about 13 significant bits and add that into
+ * the fp32 accumulator, so results agree with the exact sum to within
+ * roughly 2^-12 of sum |products| (plus the output rounding).
+ *
+ * Scales are consumed as E8M0 bytes (2^(e-127)) in a packed, tile-major
+ * layout that gg_fp8_pack_scales writes; a caller packs its weight scales
+ * once and its activation scales per call (with the same offsets or
+ * masked_m as the GEMM that reads them).
+ */
+typedef enum {
+    GG_FP8_ACT_RAGGED = 0,  /* activation scales, ragged rows (groups = end offsets, rows = m) */
+    GG_FP8_ACT_MASKED = 1,  /* activation scales, masked layout (groups = masked_m, rows = max_m) */
+    GG_FP8_WEIGHT = 2       /* weight scales, rows = n per expert (groups unused, may be NULL) */
+} gg_fp8_scale_layout;
+
+/* Bytes of packed scales for an operand of `rows` rows (m, max_m or n) and
+ * reduction length k (a multiple of 128): ceil(rows/256) * num_groups tiles
+ * (ragged activations: ceil(rows/256) + num_groups, an upper bound), each
+ * (k / 128) * 256 bytes.  Returns -1 for invalid arguments. */
+int64_t gg_fp8_scale_bytes(gg_fp8_scale_layout layout, int64_t rows, int64_t k,
+                           int32_t num_groups);
+
+/*
+ * gg_fp8_pack_scales -- write the packed scales of one operand.
+ *   src      scales, one per (row, k-block) at src[row * ld_src + kb]:
+ *            fp32 values (src_is_f32 = 1) or E8M0 bytes (src_is_f32 = 0;
+ *            the page's packed int32 scales are 4 such bytes per word).
+ *            Rows run over [m] (ragged), [E, max_m] or [E, n] flattened.
+ *   ld_src   elements per source row, >= k / 128
+ *   groups   the end offsets (ragged) or masked_m (masked), device memory;
+ *            ignored for weights
+ *   dst      gg_fp8_scale_bytes(...) bytes, device memory, 16-byte aligned
+ *   bad_count  optional device int32: incremented by the number of ACTIVE
+ *            scales that are not UE8M0 (an fp32 with its sign or mantissa
+ *            bits set -- the page's "Problem" check -- or the byte 0xFF).
+ *            Inactive rows (past an expert's end, at or past masked_m) are
+ *            neither read nor validated, so garbage there is harmless (the
+ *            fix the page names as the more correct one, "Rejected
+ *            alternatives").  A non-UE8M0 active scale is packed as its
+ *            exponent field (the mantissa dropped).
+ * Cited passage: sglang PR #32385, "Problem", "Cause" and "Rejected
+ * alternatives".
+ */
+gg_status gg_fp8_pack_scales(gg_fp8_scale_layout layout, const void* src,
+                             int src_is_f32, int64_t ld_src,
+                             const int32_t* groups, int64_t rows, int64_t k,
+                             int32_t num_groups, void* dst,
+                             int32_t* bad_count, void* stream);
+
+/*
+ * gg_fp8_forward -- the ragged fp8 forward.
+ *   x         [m, k]     e4m3 bytes
+ *   x_scales  packed (GG_FP8_ACT_RAGGED, same offs)
+ *   w         [E, n, k]  e4m3 bytes
+ *   w_scales  packed (GG_FP8_WEIGHT)
+ *   offs      [E] int32 end offsets, device memory
+ *   y         [m, n] y_dtype; rows past end(E-1) untouched
+ * Requirements: those of gg_forward, and k % 128 == 0.
+ * Cited passage: sglang PR #32385, "Evidence" (fp8 operands with per-128
+ * scales) and "Cause" (G = k / 128).
+ */
+gg_status gg_fp8_forward(const void* x, const void* x_scales, const void* w,
+                         const void* w_scales, const int32_t* offs, void* y,
+                         gg_dtype y_dtype, int64_t m, int64_t k, int64_t n,
+                         int32_t num_groups, void* stream);
+
+/*
+ * gg_fp8_masked_forward -- the same on the masked layout: x [E, max_m, k],
+ * x_scales packed with GG_FP8_ACT_MASKED and the same masked_m, y
+ * [E, max_m, n]; only active rows are read or written.
+ * Cited passage: sglang PR #32385, "Evidence" (the masked fp8 call and its
+ * operand table).
+ */
+gg_status gg_fp8_masked_forward(const void* x, const void* x_scales,
+                                const void* w, const void* w_scales,
+                                const int32_t* masked_m, void* y,
+                                gg_dtype y_dtype, int64_t max_m, int64_t k,
+                                int64_t n, int32_t num_groups, void* stream);
+
 /* Static description of a status code. */
 const char* gg_status_str(gg_status s);
 

@@ -73,6 +73,14 @@ def load():
         f = getattr(lib, name)
         f.argtypes = sig_ex
         f.restype = ctypes.c_int
+    lib.gg_fp8_scale_bytes.argtypes = [ctypes.c_int, I64, I64, I32]
+    lib.gg_fp8_scale_bytes.restype = ctypes.c_int64
+    lib.gg_fp8_pack_scales.argtypes = [ctypes.c_int, P, ctypes.c_int, I64, P, I64, I64, I32, P, P, P]
+    lib.gg_fp8_pack_scales.restype = ctypes.c_int
+    for name in ("gg_fp8_forward", "gg_fp8_masked_forward"):
+        f = getattr(lib, name)
+        f.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, I32, P]
+        f.restype = ctypes.c_int
     lib.gg_status_str.argtypes = [ctypes.c_int]
     lib.gg_status_str.restype = ctypes.c_char_p
     lib.gg_last_error.argtypes = []
@@ -340,4 +348,117 @@ def masked_forward_silu_mul(x, w13, masked_m, out=None, out_dtype=None):
         raise ValueError(f"out must be [{e}, {max_m}, {n // 2}]")
     _invoke("gg_masked_forward_silu_mul", x, w13, masked_m, out, _dtype_code(out.dtype), max_m, k, n,
             e, dev)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# fp8 (e4m3) block-scaled forward
+# ---------------------------------------------------------------------------
+
+GG_FP8_ACT_RAGGED = 0
+GG_FP8_ACT_MASKED = 1
+GG_FP8_WEIGHT = 2
+
+
+def fp8_scale_bytes(layout: int, rows: int, k: int, num_groups: int) -> int:
+    """Bytes of packed scales (gg_fp8_scale_bytes)."""
+    v = int(load().gg_fp8_scale_bytes(int(layout), int(rows), int(k), int(num_groups)))
+    if v < 0:
+        raise ValueError("invalid arguments for gg_fp8_scale_bytes")
+    return v
+
+
+def fp8_pack_scales(layout: int, scales, groups, rows: int, k: int, num_groups: int,
+                    out=None, bad_count=None):
+    """Packed E8M0 scales of one operand (gg_fp8_pack_scales).  scales: fp32
+    or uint8 (E8M0 bytes) with one scale per (row, k-block) in its last dim
+    (rows flattened: [m, G], [E, max_m, G] or [E, n, G]; G may be padded);
+    groups: the int32 end offsets / masked_m (ignored for weights);
+    bad_count: optional int32 [1] device tensor the kernel adds the number of
+    active non-UE8M0 scales to.  Returns the packed uint8 tensor."""
+    torch = _torch()
+    dev = scales.device
+    if scales.dtype not in (torch.float32, torch.uint8):
+        raise TypeError("scales must be float32 or uint8 (E8M0 bytes)")
+    if not scales.is_contiguous():
+        raise ValueError("scales must be contiguous")
+    if groups is not None:
+        _check(groups, "groups", torch.int32, 1, dev)
+    nbytes = fp8_scale_bytes(layout, rows, k, num_groups)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _check(out, "out", torch.uint8, 1, dev)
+    if out.numel() < nbytes:
+        raise ValueError(f"out must hold {nbytes} bytes")
+    if bad_count is not None:
+        _check(bad_count, "bad_count", torch.int32, 1, dev)
+    rc = call_raw("gg_fp8_pack_scales", int(layout), scales.data_ptr(),
+                  1 if scales.dtype == torch.float32 else 0, int(scales.shape[-1]),
+                  None if groups is None else groups.data_ptr(), int(rows), int(k), int(num_groups),
+                  out.data_ptr(), None if bad_count is None else bad_count.data_ptr(),
+                  _stream_handle(dev))
+    if rc != 0:
+        raise GGError("gg_fp8_pack_scales", rc, last_error())
+    return out
+
+
+def _fp8_call(name, x, xs, w, ws, groups, out, m, k, n, e, dev):
+    rc = call_raw(name, x.data_ptr(), xs.data_ptr(), w.data_ptr(), ws.data_ptr(), groups.data_ptr(),
+                  out.data_ptr(), _dtype_code(out.dtype), int(m), int(k), int(n), int(e),
+                  _stream_handle(dev))
+    if rc != 0:
+        raise GGError(name, rc, last_error())
+
+
+def fp8_forward(x, x_scales, w, w_scales, offs, out=None, out_dtype=None):
+    """Y[rows of g] = sum_k x sx w[g] sw over 128-value scale blocks
+    (gg_fp8_forward).  x: uint8 e4m3 [m, k]; w: uint8 e4m3 [E, n, k];
+    x_scales / w_scales: packed by fp8_pack_scales (GG_FP8_ACT_RAGGED with
+    the same offs / GG_FP8_WEIGHT); offs: int32 [E] end offsets."""
+    torch = _torch()
+    dev = x.device
+    _check(x, "x", torch.uint8, 2, dev)
+    _check(w, "w", torch.uint8, 3, dev)
+    _check(offs, "offs", torch.int32, 1, dev)
+    _check(x_scales, "x_scales", torch.uint8, 1, dev)
+    _check(w_scales, "w_scales", torch.uint8, 1, dev)
+    m, k = x.shape
+    e, n, k2 = w.shape
+    if k2 != k or offs.shape[0] != e:
+        raise ValueError("shape mismatch between x, w and offs")
+    if x_scales.numel() < fp8_scale_bytes(GG_FP8_ACT_RAGGED, m, k, e) or \
+            w_scales.numel() < fp8_scale_bytes(GG_FP8_WEIGHT, n, k, e):
+        raise ValueError("packed scales are smaller than fp8_scale_bytes requires")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check(out, "out", out.dtype, 2, dev)
+    if tuple(out.shape) != (m, n):
+        raise ValueError(f"out must be [{m}, {n}]")
+    _fp8_call("gg_fp8_forward", x, x_scales, w, w_scales, offs, out, m, k, n, e, dev)
+    return out
+
+
+def fp8_masked_forward(x, x_scales, w, w_scales, masked_m, out=None, out_dtype=None):
+    """The masked fp8 forward (gg_fp8_masked_forward): x uint8 [E, max_m, k],
+    x_scales packed with GG_FP8_ACT_MASKED and the same masked_m."""
+    torch = _torch()
+    dev = x.device
+    _check(x, "x", torch.uint8, 3, dev)
+    _check(w, "w", torch.uint8, 3, dev)
+    _check(masked_m, "masked_m", torch.int32, 1, dev)
+    _check(x_scales, "x_scales", torch.uint8, 1, dev)
+    _check(w_scales, "w_scales", torch.uint8, 1, dev)
+    e, max_m, k = x.shape
+    e2, n, k2 = w.shape
+    if e2 != e or k2 != k or masked_m.shape[0] != e:
+        raise ValueError("shape mismatch between x, w and masked_m")
+    if x_scales.numel() < fp8_scale_bytes(GG_FP8_ACT_MASKED, max_m, k, e) or \
+            w_scales.numel() < fp8_scale_bytes(GG_FP8_WEIGHT, n, k, e):
+        raise ValueError("packed scales are smaller than fp8_scale_bytes requires")
+    if out is None:
+        out = torch.empty((e, max_m, n), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check(out, "out", out.dtype, 3, dev)
+    if tuple(out.shape) != (e, max_m, n):
+        raise ValueError(f"out must be [{e}, {max_m}, {n}]")
+    _fp8_call("gg_fp8_masked_forward", x, x_scales, w, w_scales, masked_m, out, max_m, k, n, e, dev)
     return out

@@ -207,6 +207,81 @@ gg_status gg_masked_forward(const void* x, const void* w, const int32_t* masked_
                               stream);
 }
 
+int64_t gg_fp8_scale_bytes(gg_fp8_scale_layout layout, int64_t rows, int64_t k, int32_t num_groups) {
+  if (layout < GG_FP8_ACT_RAGGED || layout > GG_FP8_WEIGHT) return -1;
+  if (rows < 0 || k < 128 || k % 128 != 0 || k > GG_MAX_KN) return -1;
+  if (num_groups < 1 || num_groups > GG_MAX_GROUPS) return -1;
+  if (rows > (int64_t(1) << 31) - 1) return -1;
+  return gg::fp8_scale_tiles((int)layout, rows, num_groups) * (k / 128) * 256;
+}
+
+gg_status gg_fp8_pack_scales(gg_fp8_scale_layout layout, const void* src, int src_is_f32, int64_t ld_src,
+                             const int32_t* groups, int64_t rows, int64_t k, int32_t num_groups,
+                             void* dst, int32_t* bad_count, void* stream) {
+  if (layout < GG_FP8_ACT_RAGGED || layout > GG_FP8_WEIGHT) return fail(GG_ERR_BAD_DIM, "unknown scale layout");
+  if (!src || !dst || (layout != GG_FP8_WEIGHT && !groups))
+    return fail(GG_ERR_NULL_PTR, "a required pointer is NULL");
+  if (num_groups < 1 || num_groups > GG_MAX_GROUPS) return fail(GG_ERR_LIMIT, "num_groups must be in [1, GG_MAX_GROUPS]");
+  if (rows < 0 || k < 128 || k % 128 != 0 || k > GG_MAX_KN)
+    return fail(GG_ERR_BAD_DIM, "need rows >= 0 and k a positive multiple of 128 up to GG_MAX_KN");
+  const int64_t kb = k / 128;
+  if (ld_src < kb) return fail(GG_ERR_BAD_DIM, "ld_src must be at least k / 128");
+  const double src_rows = layout == GG_FP8_ACT_RAGGED ? (double)rows : (double)rows * num_groups;
+  if (src_rows > 2147483647.0) return fail(GG_ERR_BAD_DIM, "row count exceeds 2^31 - 1");
+  if (src_rows * (double)ld_src * 4.0 > 4.0e18) return fail(GG_ERR_BAD_DIM, "problem too large");
+  if (!aligned16(dst) || (groups && !aligned16(groups)) || (src_is_f32 && (reinterpret_cast<uintptr_t>(src) & 3u)))
+    return fail(GG_ERR_ALIGNMENT, "dst and groups must be 16-byte aligned, fp32 src 4-byte aligned");
+  int cus = 0;
+  gg_status s = device_cus(&cus);
+  if (s != GG_OK) return s;
+  hipError_t e = gg::launch_pack_scales((int)layout, src_is_f32 != 0, src, ld_src, groups, rows, (int32_t)kb,
+                                        num_groups, static_cast<uint8_t*>(dst), bad_count, cus,
+                                        static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_error = std::string("kernel launch: ") + hipGetErrorString(e);
+    return GG_ERR_HIP;
+  }
+  g_last_error.clear();
+  return GG_OK;
+}
+
+static gg_status fp8_run(bool masked, const void* x, const void* xs, const void* w, const void* ws,
+                         const int32_t* groups, void* y, gg_dtype y_dtype, int64_t rows, int64_t k,
+                         int64_t n, int32_t num_groups, void* stream) {
+  gg_status s = check(x, w, groups, y, y_dtype, rows, k, n, num_groups);
+  if (s != GG_OK) return s;
+  if (!xs || !ws) return fail(GG_ERR_NULL_PTR, "a required pointer is NULL");
+  if (k % 128 != 0) return fail(GG_ERR_BAD_DIM, "k must be a multiple of 128 (one scale per 128 values)");
+  if (!aligned16(xs) || !aligned16(ws)) return fail(GG_ERR_ALIGNMENT, "pointers must be 16-byte aligned");
+  if (masked) {
+    s = masked_rows(rows, num_groups);
+    if (s != GG_OK) return s;
+  }
+  int cus = 0;
+  s = device_cus(&cus);
+  if (s != GG_OK) return s;
+  hipError_t e = gg::launch_fp8(masked, x, xs, w, ws, groups, y, y_dtype == GG_F32, rows, k, n, num_groups,
+                                cus, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_error = std::string("kernel launch: ") + hipGetErrorString(e);
+    return GG_ERR_HIP;
+  }
+  g_last_error.clear();
+  return GG_OK;
+}
+
+gg_status gg_fp8_forward(const void* x, const void* x_scales, const void* w, const void* w_scales,
+                         const int32_t* offs, void* y, gg_dtype y_dtype, int64_t m, int64_t k, int64_t n,
+                         int32_t num_groups, void* stream) {
+  return fp8_run(false, x, x_scales, w, w_scales, offs, y, y_dtype, m, k, n, num_groups, stream);
+}
+
+gg_status gg_fp8_masked_forward(const void* x, const void* x_scales, const void* w, const void* w_scales,
+                                const int32_t* masked_m, void* y, gg_dtype y_dtype, int64_t max_m, int64_t k,
+                                int64_t n, int32_t num_groups, void* stream) {
+  return fp8_run(true, x, x_scales, w, w_scales, masked_m, y, y_dtype, max_m, k, n, num_groups, stream);
+}
+
 const char* gg_status_str(gg_status s) {
   switch (s) {
     case GG_OK: return "GG_OK";

@@ -1,0 +1,196 @@
+// gg_fp8_scales.hip -- the scale-layout step of the fp8 block-scaled forward.
+//
+// The fp8 kernels read their power-of-two scales as E8M0 bytes (2^(e - 127))
+// in a packed, tile-major layout (stated with the fp8 main loop in
+// gg_kernels.hip): for every 256-row tile of an operand and every k-block of
+// 128 reduction values, 256 bytes, tile row r at 128 (r / 128) + 4 (r mod 32)
+// + (r / 32) mod 4.  This kernel writes that layout from the scales as a
+// quantizer emits them -- fp32 values [rows, k-blocks] (sglang PR #32385,
+// "Cause": the fp32 fallback branch) or one E8M0 byte each (the packed int32
+// branch of the same table is four such bytes per word) -- and counts the
+// scales that are not UE8M0.
+//
+// Only active rows are read or validated: rows past an expert's end offset,
+// or at or past masked_m in the masked layout, are written as zero bytes and
+// never looked at, whatever the caller left there (the page's "Cause" and
+// "Rejected alternatives": validating the padding is what failed).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gg_internal.h"
+
+namespace gg {
+namespace {
+
+constexpr int kRows = 256;     // rows per packed tile
+constexpr int kThreads = 256;
+
+// E8M0 byte of one scale, and whether the scale is UE8M0: an fp32 with
+// sign and mantissa bits clear (+0.0 or a positive power of two; +0.0 maps
+// to the smallest E8M0 value, 2^-127), or any byte but 0xFF (E8M0's NaN).
+template <bool SRC_F32>
+__device__ __forceinline__ uint32_t e8m0(const void* src, int64_t idx, int& bad) {
+  if constexpr (SRC_F32) {
+    const uint32_t bits = reinterpret_cast<const uint32_t*>(src)[idx];
+    bad += (bits & 0x807FFFFFu) != 0u;
+    return (bits >> 23) & 0xFFu;
+  } else {
+    const uint32_t b = reinterpret_cast<const uint8_t*>(src)[idx];
+    bad += b == 0xFFu;
+    return b;
+  }
+}
+
+// LAYOUT 0: ragged activations (groups = end offsets, rows = M);
+// 1: masked activations (groups = masked_m, rows = max_m per expert);
+// 2: weights (rows = N per expert, groups unused).
+template <int LAYOUT, bool SRC_F32>
+__global__ __launch_bounds__(kThreads) void pack_scales_kernel(const void* src, int64_t ld_src,
+                                                               const int32_t* groups, int64_t rows,
+                                                               int32_t kblocks, int32_t num_groups,
+                                                               int64_t tiles, uint8_t* dst,
+                                                               int32_t* bad_count) {
+  __shared__ int32_t s_end[GG_MAX_GROUPS_DEV];
+  __shared__ int32_t s_pref[GG_MAX_GROUPS_DEV + 1];
+  __shared__ int32_t s_scan[kThreads];
+  __shared__ int32_t s_bad;
+  const int tid = threadIdx.x;
+  const int E = num_groups;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  int64_t total = tiles;
+  if constexpr (LAYOUT == 0) {
+    // clamped monotone ends (prefix max of the offsets, capped at rows) and
+    // the prefix of per-expert 256-row tile counts, as the GEMM decodes them
+    const int per = (E + kThreads - 1) / kThreads;
+    const int g0 = tid * per;
+    const int g1 = g0 + per < E ? g0 + per : E;
+    int run = 0;
+    for (int g = g0; g < g1; ++g) {
+      const int o = groups[g];
+      run = o > run ? o : run;
+      s_end[g] = run;
+    }
+    s_scan[tid] = run;
+    __syncthreads();
+    for (int d = 1; d < kThreads; d <<= 1) {
+      const int o = tid >= d ? s_scan[tid - d] : 0;
+      __syncthreads();
+      if (tid >= d && o > s_scan[tid]) s_scan[tid] = o;
+      __syncthreads();
+    }
+    const int before = tid > 0 ? s_scan[tid - 1] : 0;
+    __syncthreads();
+    int local = 0;
+    for (int g = g0; g < g1; ++g) {
+      int e = s_end[g] > before ? s_end[g] : before;
+      e = e < rows ? e : (int)rows;
+      s_end[g] = e;
+    }
+    __syncthreads();
+    for (int g = g0; g < g1; ++g) {
+      const int start = g == 0 ? 0 : s_end[g - 1];
+      local += (s_end[g] - start + kRows - 1) / kRows;
+    }
+    s_scan[tid] = local;
+    __syncthreads();
+    for (int d = 1; d < kThreads; d <<= 1) {
+      const int o = tid >= d ? s_scan[tid - d] : 0;
+      __syncthreads();
+      if (tid >= d) s_scan[tid] += o;
+      __syncthreads();
+    }
+    int acc = s_scan[tid] - local;
+    for (int g = g0; g < g1; ++g) {
+      s_pref[g] = acc;
+      const int start = g == 0 ? 0 : s_end[g - 1];
+      acc += (s_end[g] - start + kRows - 1) / kRows;
+    }
+    if (tid == kThreads - 1) s_pref[E] = s_scan[tid];
+    __syncthreads();
+    total = s_pref[E];
+  }
+  const int64_t tpe = (rows + kRows - 1) / kRows;   // layouts 1, 2: tiles per expert
+  int bad = 0;
+  // thread t builds dword d = t mod 64 of k-blocks t / 64, t / 64 + 4, ...:
+  // the bytes of tile rows 128 (d / 32) + d mod 32 + 32 b, b = 0..3
+  const int d = tid & 63;
+  const int kb0 = tid >> 6;
+  for (int64_t T = blockIdx.x; T < total; T += gridDim.x) {
+    int64_t first;     // source row of tile row 0
+    int64_t valid;     // rows of the tile that are active
+    if constexpr (LAYOUT == 0) {
+      int lo = 0, hi = E;                 // largest g with s_pref[g] <= T
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= T) lo = mid; else hi = mid;
+      }
+      const int start = lo == 0 ? 0 : s_end[lo - 1];
+      first = start + (T - s_pref[lo]) * kRows;
+      valid = s_end[lo] - first;
+    } else {
+      const int64_t e = T / tpe;
+      const int64_t r0 = (T - e * tpe) * kRows;
+      first = e * rows + r0;
+      int64_t active = rows;
+      if constexpr (LAYOUT == 1) {
+        int64_t a = groups[e];
+        a = a < 0 ? 0 : a;
+        active = a < rows ? a : rows;
+      }
+      valid = active - r0;
+    }
+    for (int kb = kb0; kb < kblocks; kb += 4) {
+      uint32_t word = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int r = 128 * (d >> 5) + (d & 31) + 32 * b;
+        if (r < valid) word |= e8m0<SRC_F32>(src, (first + r) * ld_src + kb, bad) << (8 * b);
+      }
+      reinterpret_cast<uint32_t*>(dst + (T * kblocks + kb) * kRows)[d] = word;
+    }
+  }
+  if (bad_count) {
+    if (bad) atomicAdd(&s_bad, bad);
+    __syncthreads();
+    if (tid == 0 && s_bad) atomicAdd(bad_count, s_bad);
+  }
+}
+
+template <int LAYOUT>
+hipError_t launch_layout(bool src_f32, const void* src, int64_t ld_src, const int32_t* groups,
+                         int64_t rows, int32_t kblocks, int32_t E, int64_t tiles, uint8_t* dst,
+                         int32_t* bad, int num_cus, hipStream_t stream) {
+  const int64_t want = tiles < 4 * (int64_t)num_cus ? tiles : 4 * (int64_t)num_cus;
+  const int grid = (int)(want > 0 ? want : 1);
+  if (src_f32)
+    hipLaunchKernelGGL((pack_scales_kernel<LAYOUT, true>), dim3(grid), dim3(kThreads), 0, stream, src,
+                       ld_src, groups, rows, kblocks, E, tiles, dst, bad);
+  else
+    hipLaunchKernelGGL((pack_scales_kernel<LAYOUT, false>), dim3(grid), dim3(kThreads), 0, stream, src,
+                       ld_src, groups, rows, kblocks, E, tiles, dst, bad);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t fp8_scale_tiles(int layout, int64_t rows, int32_t num_groups) {
+  const int64_t t = (rows + kRows - 1) / kRows;
+  return layout == 0 ? t + num_groups : t * num_groups;
+}
+
+hipError_t launch_pack_scales(int layout, bool src_f32, const void* src, int64_t ld_src,
+                              const int32_t* groups, int64_t rows, int32_t kblocks, int32_t num_groups,
+                              uint8_t* dst, int32_t* bad, int num_cus, hipStream_t stream) {
+  const int64_t tiles = fp8_scale_tiles(layout, rows, num_groups);
+  switch (layout) {
+    case 0: return launch_layout<0>(src_f32, src, ld_src, groups, rows, kblocks, num_groups, tiles, dst,
+                                    bad, num_cus, stream);
+    case 1: return launch_layout<1>(src_f32, src, ld_src, groups, rows, kblocks, num_groups, tiles, dst,
+                                    bad, num_cus, stream);
+    default: return launch_layout<2>(src_f32, src, ld_src, groups, rows, kblocks, num_groups, tiles, dst,
+                                     bad, num_cus, stream);
+  }
+}
+
+}  // namespace gg

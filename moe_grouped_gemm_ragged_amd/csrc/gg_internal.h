@@ -17,4 +17,26 @@ namespace gg {
 hipError_t launch(int mode, const void* a, const void* b, const int32_t* groups, void* c,
                   bool out_f32, int64_t m, int64_t k, int64_t n, int32_t num_groups,
                   float alpha, float beta, int num_cus, hipStream_t stream);
+
+// The fp8 (e4m3) block-scaled forward, ragged (groups = end offsets) or
+// masked (groups = masked_m, m = max_m): x [rows, k] and w [E, n, k] e4m3,
+// sx / sw their scales in the packed layout of gg_fp8_pack_scales, k a
+// multiple of 128.  Arguments were validated by the caller.
+hipError_t launch_fp8(bool masked, const void* x, const void* sx, const void* w, const void* sw,
+                      const int32_t* groups, void* c, bool out_f32, int64_t m, int64_t k, int64_t n,
+                      int32_t num_groups, int num_cus, hipStream_t stream);
+
+// Packed fp8 scale tiles for `rows` rows of an operand: layout 0 ragged
+// activations (an upper bound: ceil(rows / 256) + num_groups), 1 masked
+// activations and 2 weights (num_groups * ceil(rows / 256)).  Each tile
+// takes kblocks * 256 bytes.
+int64_t fp8_scale_tiles(int layout, int64_t rows, int32_t num_groups);
+
+// Writes the packed scales of one operand (gg_fp8_scales.hip).  src holds
+// one scale per (row, k-block) at row * ld_src + kb, fp32 or E8M0 bytes;
+// bad (nullable) is incremented by the number of active scales that are
+// not UE8M0.
+hipError_t launch_pack_scales(int layout, bool src_f32, const void* src, int64_t ld_src,
+                              const int32_t* groups, int64_t rows, int32_t kblocks, int32_t num_groups,
+                              uint8_t* dst, int32_t* bad, int num_cus, hipStream_t stream);
 }  // namespace gg

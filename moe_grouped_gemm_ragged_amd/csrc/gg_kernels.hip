@@ -84,15 +84,19 @@ typedef short shortx4 __attribute__((ext_vector_type(4)));
 
 enum Mode {
   FWD = 0, DGRAD = 1, WGRAD = 2, MASKED = 3, MASKED_DGRAD = 4, MASKED_WGRAD = 5,
-  FWD_SILU = 6, MASKED_SILU = 7
+  FWD_SILU = 6, MASKED_SILU = 7, FP8 = 8, FP8_MASKED = 9
 };
 
 // The masked modes are the ragged passes on the masked layout: expert e's
 // rows start at e * max_m and its active count is masked_m[e].  The SiLU
 // modes are forwards whose epilogue applies the gate/up activation.
 constexpr bool is_masked(int mode) {
-  return mode == MASKED || mode == MASKED_DGRAD || mode == MASKED_WGRAD || mode == MASKED_SILU;
+  return mode == MASKED || mode == MASKED_DGRAD || mode == MASKED_WGRAD || mode == MASKED_SILU ||
+         mode == FP8_MASKED;
 }
+// The fp8 modes: e4m3 operands, X [rows, K] and W [E, N, K] (both
+// reduction-contiguous), one power-of-two scale per 128 reduction values.
+constexpr bool is_fp8(int mode) { return mode == FP8 || mode == FP8_MASKED; }
 constexpr bool is_silu(int mode) { return mode == FWD_SILU || mode == MASKED_SILU; }
 constexpr bool is_wgrad(int mode) { return mode == WGRAD || mode == MASKED_WGRAD; }
 constexpr bool is_dgrad(int mode) { return mode == DGRAD || mode == MASKED_DGRAD; }
@@ -108,6 +112,8 @@ struct Params {
   int32_t num_groups;
   float alpha;              // out = alpha * product + beta * out
   float beta;               // (the output is not read when beta == 0)
+  const uint8_t* sa;        // fp8: X's scales, packed (E8M0 bytes, see the fp8 section)
+  const uint8_t* sb;        // fp8: W's scales, packed
 };
 
 // One operand tile: element (tile row r, reduction index q) of the tile
@@ -167,7 +173,7 @@ struct DmaCtx {
   uint32_t step;      // extra byte offset per load (scalar offset)
 };
 
-template <bool STRIDED>
+template <bool STRIDED, int ESZ = 2>
 __device__ __forceinline__ DmaCtx dma_ctx(const Operand& op, int q0, int tid) {
   DmaCtx c;
   // lane terms recomputed per stage (a few VALU ops) rather than hoisted and
@@ -189,12 +195,13 @@ __device__ __forceinline__ DmaCtx dma_ctx(const Operand& op, int q0, int tid) {
   } else {
     // load j of wave w covers tile rows 32 w + 16 j .. + 15; lane i: row
     // 32 w + 16 j + i / 4, chunk position i mod 4, logical chunk
-    // (i mod 4) ^ ((row / 4) mod 4) = (i mod 4) ^ ((i / 16) mod 4).
-    const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - 2u * (uint32_t)q0 : 0u;
-    c.rs = make_rsrc(op.origin + 2 * (int64_t)q0, nrec);
+    // (i mod 4) ^ ((row / 4) mod 4) = (i mod 4) ^ ((i / 16) mod 4).  ESZ:
+    // bytes per element (2 bf16, 1 e4m3); a chunk is 16 bytes either way.
+    const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - (uint32_t)(ESZ * q0) : 0u;
+    c.rs = make_rsrc(op.origin + (int64_t)ESZ * q0, nrec);
     const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
     uint32_t v = (uint32_t)(32 * w + (lane >> 2)) * op.ld_bytes + 16u * (uint32_t)chunk;
-    if (q0 + 8 * chunk >= op.red) v = kOutOfRange;   // past the reduction end: zero
+    if (q0 + (16 / ESZ) * chunk >= op.red) v = kOutOfRange;   // past the reduction end: zero
     c.voff = v;
     c.step = 16u * op.ld_bytes;
   }
@@ -448,6 +455,200 @@ __device__ __attribute__((always_inline)) inline void mainloop(
     if (kt + 3 < nk) GG_STAGE(s3, s0, s2, kt + 3)
   }
 #undef GG_STAGE
+}
+
+// ---- fp8 (e4m3) block-scaled main loop ----------------------------------------------
+//
+// The same tile engine on bytes: a stage is 64 e4m3 values (64 bytes) of
+// each of the 256 tile rows of X and W, i.e. exactly the bytes of a bf16
+// stage, in the same reduction-contiguous LDS layout; one
+// v_mfma_scale_f32_32x32x64_f8f6f4 per 32 x 32 block consumes a stage in
+// the time two bf16 MFMAs take, so a stage does twice the FLOPs in the same
+// cycles and bytes.  The MFMA applies the block scales itself: each lane
+// hands it one E8M0 byte (2^(e - 127)) for its row of either operand, and a
+// 64-deep MFMA lies inside one 128-value scale block, so the byte is the
+// row's scale for that block.
+//
+// Packed scales.  For every 256-row tile of X (an expert's row tile rt, in
+// the order of the experts; masked: expert e's tiles at e * ceil(max_m /
+// 256)) and every 256-column tile of W (expert e, column tile ct at e *
+// ceil(N / 256) + ct), the scales of k-block kb are 256 bytes at
+// ((tile * kblocks) + kb) * 256, tile row r at byte 128 (r / 128) + 4 (r mod
+// 32) + (r / 32) mod 4.  So the 4 scales a lane needs (its row in each of
+// the wave's four 32-row blocks) are one dword.  Per k-block, wave 0 copies
+// the tile's 256 X-scale bytes and wave 1 its 256 W-scale bytes into a
+// 2-slot LDS ring with one direct-to-LDS dword load each, issued two k-blocks
+// ahead with the stage loads; every lane reads its two dwords once per
+// k-block.
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+constexpr int BK8 = 64;             // e4m3 values per stage
+constexpr int kScaleSlot = 512;     // LDS bytes of one k-block's scales (X, then W)
+
+// Fragment i of a stage: 32 bytes of row 32 i + l % 32 -- the two 16-byte
+// chunks the bf16 sub-steps read (chunks l / 32 and 2 + l / 32).  Which
+// reduction values a lane holds does not matter as long as both operands
+// agree, and they share the layout.
+__device__ __forceinline__ i32x8 read_frag8(const uint8_t* lds, const FragAddr& fa, int i) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(lds + fa.o[0] + (uint32_t)(i * 32 * 64));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(lds + fa.o[1] + (uint32_t)(i * 32 * 64));
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// One scaled MFMA of block (i, j): source A is the W fragment wf (output
+// columns) with scale byte j of sb, source B the X fragment xf (rows) with
+// byte i of sa, so the block holds C^T as in the bf16 loop.  The byte
+// selects are immediates, hence the switch (folded once the callers' loops
+// are unrolled).
+__device__ __forceinline__ floatx16 mfma8(int i, int j, const i32x8& wf, const i32x8& xf, floatx16 c,
+                                          uint32_t sa, uint32_t sb) {
+#define GG_MF8(I, J) \
+  case (I) * 2 + (J): return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(wf, xf, c, 0, 0, J, (int)sb, I, (int)sa);
+  switch (i * 2 + j) {
+    GG_MF8(0, 0) GG_MF8(0, 1) GG_MF8(1, 0) GG_MF8(1, 1)
+    GG_MF8(2, 0) GG_MF8(2, 1) GG_MF8(3, 0) GG_MF8(3, 1)
+  }
+#undef GG_MF8
+  return c;
+}
+
+// Wave 0 copies the X scales, wave 1 the W scales of k-block kb into an LDS
+// slot (out-of-range blocks land as zeros and are never read).
+__device__ __forceinline__ void scale_load(const uint8_t* __restrict__ sa_tile,
+                                           const uint8_t* __restrict__ sb_tile, uint32_t nbytes, int kb,
+                                           uint8_t* slot, int wave, int lane) {
+  if (wave < 2) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(wave == 0 ? sa_tile : sb_tile, nbytes);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, LDS_PTR(slot + (wave == 0 ? 0 : 256)), 4,
+                                             opaque_v((uint32_t)lane * 4u), (uint32_t)kb * 256u, 0, 0);
+  }
+}
+
+// This lane's scale dwords for one k-block from its LDS slot, shifted so
+// that byte i (X) / byte j (W) is the scale of the wave's block i / j.
+template <int TMA>
+__device__ __forceinline__ void scale_read(const uint8_t* slot, int wm, int wn, int lane, uint32_t& sa,
+                                           uint32_t& sb) {
+  const int wa = TMA == 2 ? 0 : wm;
+  sa = *reinterpret_cast<const uint32_t*>(slot + 4 * (32 * wa + (lane & 31)));
+  sb = *reinterpret_cast<const uint32_t*>(slot + 256 + 4 * (32 * (wn >> 1) + (lane & 31)));
+  if (TMA == 2) sa >>= 16 * wm;
+  sb >>= 16 * (wn & 1);
+}
+
+template <int TMA>
+__device__ __forceinline__ void load_stage8(const Operand& A, const Operand& B, int st, uint8_t* buf,
+                                            int tid, int wave) {
+  const DmaCtx ca = dma_ctx<false, 1>(A, st * BK8, tid);
+  const DmaCtx cb = dma_ctx<false, 1>(B, st * BK8, tid);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) dma_load(ca, buf, wave, j);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) dma_load(cb, buf + OP_BYTES, wave, j);
+}
+
+// The fp8 tile's loads in flight when its main loop starts: stages 0..2,
+// the A half of stage 3, and the scales of k-blocks 0 and 1 (waves 0 and 1
+// only, issued before stages 0 and 2 so that every wait below finds them
+// complete when it finds the stage complete).
+__device__ __attribute__((always_inline)) inline void prologue_loads8(
+    uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
+    uint8_t* __restrict__ s3, uint8_t* __restrict__ sc, const uint8_t* __restrict__ a_origin,
+    const uint8_t* __restrict__ b_origin, const uint8_t* __restrict__ sa_tile,
+    const uint8_t* __restrict__ sb_tile, uint32_t sc_bytes, Operand A, Operand B, int tid, int wave) {
+  A.origin = a_origin;
+  B.origin = b_origin;
+  const int lane = tid & 63;
+  scale_load(sa_tile, sb_tile, sc_bytes, 0, sc, wave, lane);
+  load_stage8<TM>(A, B, 0, s0, tid, wave);
+  load_stage8<TM>(A, B, 1, s1, tid, wave);
+  scale_load(sa_tile, sb_tile, sc_bytes, 1, sc + kScaleSlot, wave, lane);
+  load_stage8<TM>(A, B, 2, s2, tid, wave);
+  const DmaCtx ca = dma_ctx<false, 1>(A, 3 * BK8, tid);
+  dma_load(ca, s3, wave, 0);
+  dma_load(ca, s3, wave, 1);
+}
+
+// The fp8 reduction loop: the bf16 loop's stage schedule (loads of the B
+// half of stage kt+3 in the first half-stage, wait and barrier, loads of the
+// A half of stage kt+4 in the second), with the MFMAs of a stage split by
+// row blocks instead of reduction halves (first half: blocks i < TMA/2).
+// The W fragments of a stage serve both halves, so they are double-buffered
+// across stages (FB, NB); the X fragments of the first half of stage kt+1
+// are read during the second half of stage kt, the rest after it.  Even
+// stages also issue (waves 0, 1) the scales of k-block kt/2 + 2, into the
+// slot k-block kt/2 used; odd stages read the next k-block's scales right
+// after their barrier.  Waves 0 and 1 then have one more load in flight at every
+// wait.
+template <int TMA>
+__device__ __attribute__((always_inline)) inline void mainloop8(
+    uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
+    uint8_t* __restrict__ s3, uint8_t* __restrict__ sc, const uint8_t* __restrict__ a_origin,
+    const uint8_t* __restrict__ b_origin, const uint8_t* __restrict__ sa_tile,
+    const uint8_t* __restrict__ sb_tile, uint32_t sc_bytes, Operand A, Operand B, int tid, int wave,
+    int wm, int wn, const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[TM][TN]) {
+  constexpr int kSub = TMA / 2 * TN;                 // MFMAs per half-stage
+  constexpr int kGap = kSub / 2 > 0 ? kSub / 2 : 1;
+  constexpr int kAt = kGap - 1;
+  constexpr int kItems = TMA / 2 + TN;              // fragments read during the second half
+  A.origin = a_origin;
+  B.origin = b_origin;
+  const int lane = tid & 63;
+  const int nk = (A.red + BK8 - 1) / BK8;           // even: K is a multiple of 128
+  if (nk <= 0) return;
+  i32x8 fa[TMA], fb0[TN], fb1[TN];
+  uint32_t sa0, sb0, sa1 = 0, sb1 = 0;
+  if (wave < 2) stage_barrier_vm<kPrologueLoads + 1>();
+  else stage_barrier_vm<kPrologueLoads>();
+  scale_read<TMA>(sc, wm, wn, lane, sa0, sb0);
+#pragma unroll
+  for (int i = 0; i < TMA; ++i) fa[i] = read_frag8(s0, faa, i);
+#pragma unroll
+  for (int j = 0; j < TN; ++j) fb0[j] = read_frag8(s0 + OP_BYTES, fab, j);
+
+#define GG8_STAGE(BC, BN, BP, KT, FB, NB, SA, SB, ODD, SLOT, SA_N, SB_N)                   \
+  {                                                                                       \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    const DmaCtx cb = dma_ctx<false, 1>(B, ((KT) + 3) * BK8, tid);                        \
+    _Pragma("unroll") for (int q = 0; q < kSub; ++q) {                                    \
+      const int i = q / TN, j = q % TN;                                                   \
+      acc[i][j] = mfma8(i, j, FB[j], fa[i], acc[i][j], SA, SB);                           \
+      if (q % kGap == kAt && q / kGap < 2) dma_load(cb, (BP) + OP_BYTES, wave, q / kGap); \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+    }                                                                                     \
+    mfma_fence(acc);                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    if (wave < 2) stage_barrier_vm<9>(); else stage_barrier_vm<8>();                      \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    if (!(ODD)) scale_load(sa_tile, sb_tile, sc_bytes, (KT) / 2 + 2, sc + (SLOT) * kScaleSlot, wave, lane); \
+    if (ODD) scale_read<TMA>(sc + (SLOT) * kScaleSlot, wm, wn, lane, SA_N, SB_N);        \
+    const DmaCtx ca = dma_ctx<false, 1>(A, ((KT) + 4) * BK8, tid);                        \
+    _Pragma("unroll") for (int q = 0; q < kSub; ++q) {                                    \
+      const int i = TMA / 2 + q / TN, j = q % TN;                                         \
+      acc[i][j] = mfma8(i, j, FB[j], fa[i], acc[i][j], SA, SB);                           \
+      if (q % kGap == kAt && q / kGap < 2) dma_load(ca, BC, wave, q / kGap);              \
+      if (q < TMA / 2) fa[q] = read_frag8(BN, faa, q);                                    \
+      else if (q < kItems) NB[q - TMA / 2] = read_frag8((BN) + OP_BYTES, fab, q - TMA / 2); \
+      __builtin_amdgcn_sched_barrier(0);                                                  \
+    }                                                                                     \
+    mfma_fence(acc);                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+    _Pragma("unroll") for (int q = kSub; q < kItems; ++q) {                               \
+      if (q < TMA / 2) fa[q] = read_frag8(BN, faa, q);                                    \
+      else NB[q - TMA / 2] = read_frag8((BN) + OP_BYTES, fab, q - TMA / 2);               \
+    }                                                                                     \
+    _Pragma("unroll") for (int i = TMA / 2; i < TMA; ++i) fa[i] = read_frag8(BN, faa, i); \
+    __builtin_amdgcn_sched_barrier(0);                                                    \
+  }
+
+  for (int kt = 0; kt < nk; kt += 4) {
+    GG8_STAGE(s0, s1, s3, kt, fb0, fb1, sa0, sb0, false, 0, sa1, sb1)
+    GG8_STAGE(s1, s2, s0, kt + 1, fb1, fb0, sa0, sb0, true, 1, sa1, sb1)
+    if (kt + 2 < nk) {
+      GG8_STAGE(s2, s3, s1, kt + 2, fb0, fb1, sa1, sb1, false, 1, sa0, sb0)
+      GG8_STAGE(s3, s0, s2, kt + 3, fb1, fb0, sa1, sb1, true, 0, sa0, sb0)
+    }
+  }
+#undef GG8_STAGE
 }
 
 // ---- epilogue --------------------------------------------------------------------
@@ -809,16 +1010,20 @@ struct Tile {
   uint8_t* cbase;       // output element (first row, first column) of the tile
   uint32_t ldc_bytes;   // output row pitch
   int rows, cols;       // valid output rows / columns of the tile
+  const uint8_t* sa;    // fp8: the tile's packed X scales (k-block 0)
+  const uint8_t* sb;    // fp8: the tile's packed W scales
 };
 
 
 template <int MODE, bool OUT_F32>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   constexpr bool A_STRIDED = is_wgrad(MODE);
-  constexpr bool B_STRIDED = !is_dgrad(MODE);
+  constexpr bool B_STRIDED = !is_dgrad(MODE) && !is_fp8(MODE);
 
-  // LDS: NSTAGE stage buffers of 32 KB (A tile, then B tile).
+  // LDS: NSTAGE stage buffers of 32 KB (A tile, then B tile); fp8: two
+  // k-blocks of scales.
   __shared__ __attribute__((aligned(16))) uint8_t smem[NSTAGE * STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sc[is_fp8(MODE) ? 2 * kScaleSlot : 16];
   __shared__ int32_t s_end[GG_MAX_GROUPS_DEV];
   __shared__ int32_t s_pref[GG_MAX_GROUPS_DEV + 1];
   __shared__ int32_t s_half[GG_MAX_GROUPS_DEV + 1];
@@ -884,6 +1089,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     Operand& B = T.B;
     A.split = 0;
     B.split = 0;
+    T.sa = nullptr;
+    T.sb = nullptr;
     if constexpr (is_wgrad(MODE)) {
       const int g = (int)(rt_all / row_tiles_w);
       const int rt = (int)(rt_all % row_tiles_w);
@@ -917,7 +1124,28 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
       const int row0 = s + rt * BM;             // first expert row of the tile
       const int rows = (e - row0) < BM ? (e - row0) : BM;
       const int64_t arow = is_masked(MODE) ? (int64_t)g * p.m + row0 : (int64_t)row0;
-      if constexpr (is_dgrad(MODE)) {
+      if constexpr (is_fp8(MODE)) {
+        // A(row i, red kk) = X[arow + i, kk];  B(row n, red kk) = W[g, col0 + n, kk]
+        // (one byte per value)
+        A.origin = pa + arow * p.k;
+        A.ld_bytes = (uint32_t)p.k;
+        A.rows = rows;
+        A.red = (int)p.k;
+        A.row_tail = 0;
+        B.origin = pb + ((int64_t)g * p.n + col0) * p.k;
+        B.ld_bytes = (uint32_t)p.k;
+        B.rows = (int)(p.n - col0 < BN ? p.n - col0 : BN);
+        B.red = (int)p.k;
+        B.row_tail = 0;
+        T.ldc_bytes = (uint32_t)(esz * p.n);
+        T.cbase = pc + esz * (arow * p.n + col0);
+        // packed scale tiles: X row tile (experts in order), W column tile
+        const int64_t kblocks = p.k / 128;
+        const int64_t xtile = is_masked(MODE) ? (int64_t)g * ((p.m + BM - 1) / BM) + rt
+                                              : (int64_t)uniform(s_pref[g]) + uniform(s_half[g]) + rt;
+        T.sa = p.sa + xtile * kblocks * 256;
+        T.sb = p.sb + ((int64_t)g * ((p.n + BN - 1) / BN) + ct) * kblocks * 256;
+      } else if constexpr (is_dgrad(MODE)) {
         // A(row i, red j) = dY[arow + i, j];  B(row kk, red j) = W[g, col0 + kk, j]
         A.origin = pa + 2 * (arow * p.n);
         A.ld_bytes = (uint32_t)(2 * p.n);
@@ -960,10 +1188,16 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     }
   };
   auto issue_prologue = [&](const Tile& T) __attribute__((always_inline)) {
-    if (T.A.red > 0)
-      prologue_loads<A_STRIDED, B_STRIDED>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
-                                           smem + 3 * STAGE_BYTES, T.A.origin, T.B.origin, T.A,
-                                           T.B, tid, wave);
+    if (T.A.red > 0) {
+      if constexpr (is_fp8(MODE))
+        prologue_loads8(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES, smem + 3 * STAGE_BYTES, s_sc,
+                        T.A.origin, T.B.origin, T.sa, T.sb, (uint32_t)(p.k / 128 * 256), T.A, T.B, tid,
+                        wave);
+      else
+        prologue_loads<A_STRIDED, B_STRIDED>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
+                                             smem + 3 * STAGE_BYTES, T.A.origin, T.B.origin, T.A,
+                                             T.B, tid, wave);
+    }
   };
 
   if ((int64_t)blockIdx.x >= total) return;
@@ -991,16 +1225,28 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     const bool half = !is_wgrad(MODE) && cur.rows <= BM / 2;
     // fp32 tiles after the first start with the previous tile's stores
     // still in flight behind their prologue loads
-    if (half)
-      mainloop<A_STRIDED, B_STRIDED, 2>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
-                                        smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
-                                        cur.B, tid, wave, faa_half, fab, acc, prev_stores);
-    else
-      mainloop<A_STRIDED, B_STRIDED, TM>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
-                                         smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
-                                         cur.B, tid, wave, faa, fab, acc, prev_stores);
+    if constexpr (is_fp8(MODE)) {
+      const uint32_t sc_bytes = (uint32_t)(p.k / 128 * 256);
+      if (half)
+        mainloop8<2>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES, smem + 3 * STAGE_BYTES, s_sc,
+                     cur.A.origin, cur.B.origin, cur.sa, cur.sb, sc_bytes, cur.A, cur.B, tid, wave, wm,
+                     wn, faa_half, fab, acc);
+      else
+        mainloop8<TM>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES, smem + 3 * STAGE_BYTES, s_sc,
+                      cur.A.origin, cur.B.origin, cur.sa, cur.sb, sc_bytes, cur.A, cur.B, tid, wave, wm,
+                      wn, faa, fab, acc);
+    } else {
+      if (half)
+        mainloop<A_STRIDED, B_STRIDED, 2>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
+                                          smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
+                                          cur.B, tid, wave, faa_half, fab, acc, prev_stores);
+      else
+        mainloop<A_STRIDED, B_STRIDED, TM>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
+                                           smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
+                                           cur.B, tid, wave, faa, fab, acc, prev_stores);
+    }
     const int64_t tn = t + gridDim.x;
-    if (OUT_F32 && !scaled && !is_silu(MODE)) {
+    if (OUT_F32 && !scaled && !is_silu(MODE) && !is_fp8(MODE)) {
       // Every wave is done reading this tile's stages: issue the next
       // tile's prologue loads first, then this tile's stores, so the
       // stores drain while those loads are in flight.  (Loads of stages
@@ -1039,13 +1285,13 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
         else
           store_tile_lds<TM, OUT_F32, true>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane,
                                             acc, slab, p.alpha, p.beta);
-      } else if constexpr (!OUT_F32) {
+      } else if constexpr (!OUT_F32 || is_fp8(MODE)) {
         if (half)
-          store_tile_lds<2, false, false>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane,
-                                          acc, slab, 1.0f, 0.0f);
+          store_tile_lds<2, OUT_F32, false>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane,
+                                            acc, slab, 1.0f, 0.0f);
         else
-          store_tile_lds<TM, false, false>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane,
-                                           acc, slab, 1.0f, 0.0f);
+          store_tile_lds<TM, OUT_F32, false>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane,
+                                             acc, slab, 1.0f, 0.0f);
       }
       prev_stores = 0;
       // the next tile's first loads overwrite these arrays
@@ -1114,6 +1360,31 @@ hipError_t launch(int mode, const void* a, const void* b, const int32_t* groups,
     case MASKED_SILU: return launch_mode<MASKED_SILU>(p, out_f32, grid, stream);
   }
   return hipErrorInvalidValue;
+}
+
+
+hipError_t launch_fp8(bool masked, const void* x, const void* sx, const void* w, const void* sw,
+                      const int32_t* groups, void* c, bool out_f32, int64_t m, int64_t k, int64_t n,
+                      int32_t num_groups, int num_cus, hipStream_t stream) {
+  Params p;
+  p.a = static_cast<const uint16_t*>(x);
+  p.b = static_cast<const uint16_t*>(w);
+  p.groups = groups;
+  p.c = c;
+  p.m = m;
+  p.k = k;
+  p.n = n;
+  p.num_groups = num_groups;
+  p.alpha = 1.0f;
+  p.beta = 0.0f;
+  p.sa = static_cast<const uint8_t*>(sx);
+  p.sb = static_cast<const uint8_t*>(sw);
+  const int mode = masked ? FP8_MASKED : FP8;
+  const int64_t tiles = max_tiles(mode, m, k, n, num_groups);
+  if (tiles <= 0) return hipSuccess;
+  const int grid = (int)(tiles < num_cus ? tiles : num_cus);
+  return masked ? launch_mode<FP8_MASKED>(p, out_f32, grid, stream)
+                : launch_mode<FP8>(p, out_f32, grid, stream);
 }
 
 }  // namespace gg

@@ -12,6 +12,15 @@ Tolerance (written here, used by every GPU parity test):
   bf16 ulp of r is smaller than what any fp32 accumulation can promise.
 * fp32 outputs: |g - r| <= 1e-2 max(1, |r|) and, tighter,
   |g - r| <= 2 L 2^-24 S + ulp_f32(r).
+* the fp8 (e4m3) block-scaled forward (check_fp8): |g - r| <= ulp_out(r) +
+  (2^-12 + K 2^-26) S, for either output type (bf16 also passes within 1
+  ulp).  The scaled fp8 MFMA sums each run of 64 products with about 13
+  significant bits before adding it into the fp32 accumulator: measured on
+  MI355X over 32768 random dot products, |err| <= 2^-12.2 S_run for
+  wide-range codes and <= 2^-14.5 S_run for Gaussian-quantized data, plus
+  about 2^-21 of the accumulator per addition.  Summed over the K / 64 runs
+  that gives the bound above (2^-12 S, and K / 64 * 2^-20 S for the
+  accumulator term).
 """
 from __future__ import annotations
 
@@ -115,3 +124,40 @@ def check(got, ref, sabs, L, what="", report=None):
     if got.dtype == np.uint16:
         return check_bf16(got, ref, sabs, L, what, report)
     return check_f32(got, ref, sabs, L, what, report)
+
+
+FP8_RUN_REL = 2.0 ** -12     # per-MFMA error of the fp8 dot product, relative to its S
+
+
+def check_fp8(got, ref, sabs, K, what="", report: Report | None = None):
+    """The fp8 forward's tolerance: ulp_out(r) + (2^-12 + K 2^-26) S."""
+    ref = np.asarray(ref, dtype=np.float64)
+    sabs = np.asarray(sabs, dtype=np.float64)
+    tau = FP8_RUN_REL + K * 2.0 ** -26
+    if got.dtype == np.uint16:
+        ref_bits = oracle.round_bf16(ref)
+        dist = np.abs(ordered_bf16(got) - ordered_bf16(ref_bits))
+        g = dec_bf16(got)
+        bound = ulp_bf16(ref) + tau * sabs
+        ok = (dist <= 1) | (np.abs(g - ref) <= bound)
+    else:
+        g = np.asarray(got, dtype=np.float32).astype(np.float64)
+        dist = None
+        bound = ulp_f32(ref) + tau * sabs
+        ok = np.abs(g - ref) <= bound
+    if not np.all(ok):
+        idx = np.argwhere(~ok)
+        first = tuple(idx[0])
+        raise AssertionError(
+            f"{what}: {len(idx)} of {ok.size} elements out of the fp8 tolerance; first at {first}: "
+            f"got {g[first]!r} want {ref[first]!r}, S={sabs[first]!r}, K={K}")
+    if report is not None:
+        report.n += ok.size
+        with np.errstate(divide="ignore", invalid="ignore"):
+            ratio = np.where(bound > 0, np.abs(g - ref) / bound, 0.0)
+        report.max_ratio = max(report.max_ratio, float(np.max(ratio)) if ratio.size else 0.0)
+        if dist is not None:
+            report.exact += int(np.sum(dist == 0))
+            report.within1 += int(np.sum(dist <= 1))
+            report.max_ulp = max(report.max_ulp, int(dist.max()) if dist.size else 0)
+    return ok

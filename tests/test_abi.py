@@ -119,3 +119,70 @@ def test_binding_needs_out_to_accumulate():
     offs = torch.zeros(1, dtype=torch.int32)
     with pytest.raises(ValueError):
         gg.wgrad(x, dy, offs, beta=1.0)
+
+
+# --------------------------------------------------------------------------
+# fp8 entry points: host-side checks only
+# --------------------------------------------------------------------------
+
+FP8_OK = dict(x=A, xs=A + 0x100, w=A + 0x200, ws=A + 0x300, g=A + 0x400, c=A + 0x500, dt=0,
+              m=64, k=256, n=64, e=4, s=0)
+
+
+def call_fp8(name, **kw):
+    v = dict(FP8_OK, **kw)
+    return gg.call_raw(name, v["x"], v["xs"], v["w"], v["ws"], v["g"], v["c"], v["dt"], v["m"],
+                       v["k"], v["n"], v["e"], v["s"])
+
+
+@pytest.mark.parametrize("name", ["gg_fp8_forward", "gg_fp8_masked_forward"])
+@pytest.mark.parametrize("case,status", [
+    (dict(x=0), 1), (dict(xs=0), 1), (dict(w=0), 1), (dict(ws=0), 1), (dict(g=0), 1), (dict(c=0), 1),
+    (dict(k=192), 2), (dict(k=64), 2), (dict(n=20), 2), (dict(m=-1), 2),
+    (dict(xs=A + 8), 3), (dict(ws=A + 4), 3), (dict(x=A + 8), 3),
+    (dict(dt=3), 4), (dict(e=0), 5), (dict(e=2049), 5),
+])
+def test_fp8_entry_points_check_arguments(lib, name, case, status):
+    rc = call_fp8(name, **case)
+    assert rc == status, (name, case, rc, gg.last_error())
+    assert gg.last_error() != ""
+
+
+def test_fp8_masked_row_limit(lib):
+    rc = call_fp8("gg_fp8_masked_forward", m=1 << 24, e=256)
+    assert rc == 2 and "max_m" in gg.last_error()
+
+
+@pytest.mark.parametrize("layout,rows,k,e,expect", [
+    (0, 1000, 768, 8, (4 + 8) * 6 * 256),       # ragged: ceil(1000/256) + E tiles
+    (1, 256, 768, 64, 64 * 1 * 6 * 256),         # masked: E * ceil(max_m/256)
+    (2, 2048, 768, 64, 64 * 8 * 6 * 256),        # weights: E * ceil(n/256)
+    (2, 300, 128, 2, 2 * 2 * 1 * 256),
+])
+def test_fp8_scale_bytes(lib, layout, rows, k, e, expect):
+    assert gg.fp8_scale_bytes(layout, rows, k, e) == expect
+
+
+@pytest.mark.parametrize("args", [(3, 64, 128, 1), (0, 64, 100, 1), (0, -1, 128, 1), (0, 64, 128, 0)])
+def test_fp8_scale_bytes_rejects(lib, args):
+    assert lib.gg_fp8_scale_bytes(*args) == -1
+
+
+PACK_OK = dict(layout=0, src=A, f32=1, ld=2, g=A + 0x100, rows=64, k=256, e=4, dst=A + 0x200, bad=0, s=0)
+
+
+def call_pack(**kw):
+    v = dict(PACK_OK, **kw)
+    return gg.call_raw("gg_fp8_pack_scales", v["layout"], v["src"], v["f32"], v["ld"], v["g"], v["rows"],
+                       v["k"], v["e"], v["dst"], v["bad"] or None, v["s"])
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(src=0), 1), (dict(dst=0), 1), (dict(g=0), 1), (dict(layout=1, g=0), 1),
+    (dict(layout=5), 2), (dict(k=200), 2), (dict(ld=1), 2), (dict(rows=-1), 2),
+    (dict(dst=A + 8), 3), (dict(src=A + 2), 3),
+    (dict(e=0), 5),
+])
+def test_fp8_pack_scales_checks_arguments(lib, case, status):
+    rc = call_pack(**case)
+    assert rc == status, (case, rc, gg.last_error())
