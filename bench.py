@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 bf16 FLOP/clk/CU (dense)
+PEAK_FP8_TFLOPS = 5033.2       # the same with e4m3 operands (8192 FLOP/clk/CU, dense)
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_ragged_amd", "csrc", "gg_kernels.hip")
 
@@ -44,8 +45,8 @@ KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_ragged_amd", "csrc", "gg_kerne
 # Valid only for the kernel source they were taken on (sha256 below); for any
 # other source the roofline reports traffic as null.
 MEASURED_TRAFFIC = {
-    "kernel_sha256": "e2e276d1b0e0e7995acc324d75c230bec6f190613ee3e46f7c365051a848ad42",
-    "bytes": {"fwd": 23849564670, "dgrad": 28337767415, "wgrad": 25028869737},
+    "kernel_sha256": "a77f2aa3c1efb2c777ea4886e7b7db296d9ddd1d51836c2fc3b2e2b880d6b3df",
+    "bytes": {"fwd": 24341179580, "dgrad": 28055306697, "wgrad": 36988943343},
 }
 
 
@@ -324,6 +325,48 @@ def main():
             "unfused": "gg_forward to a bf16 [M, 2I] buffer, then torch silu(G) * U"}
         del tq, aq, hq
         torch.cuda.empty_cache()
+
+        # fp8 (e4m3) block-scaled forward: the GLM-up and Qwen3 gate/up
+        # recipes in fp8, and the masked down and gate/up projections of the
+        # fp8 rollout (weights rotated over 3 copies as above).  The X-scale
+        # packing, which a caller runs once per call, is timed on its own.
+        for name in ("fp8_glm_up", "fp8_qwen3_gateup", "fp8_masked_down", "fp8_masked_gateup"):
+            w8 = synth.by_name(name)
+            t8 = synth.make_fp8_inputs(w8, dev)
+            e8 = w8.num_groups
+            masked = w8.layout == "masked"
+            wsc = gg.fp8_pack_scales(gg.GG_FP8_WEIGHT, t8["sw"], None, w8.n, w8.k, e8)
+            copies = 3 if masked else 1
+            wq8 = [t8["w8"]] + [t8["w8"].clone() for _ in range(copies - 1)]
+            grp = t8["masked_m"] if masked else t8["offs"]
+            lay = gg.GG_FP8_ACT_MASKED if masked else gg.GG_FP8_ACT_RAGGED
+            xsc = gg.fp8_pack_scales(lay, t8["sx"], grp, w8.m, w8.k, e8)
+            y8 = torch.empty(((e8, w8.m, w8.n) if masked else (w8.m, w8.n)), dtype=torch.bfloat16, device=dev)
+            r8 = {"i": 0}
+
+            def wpick():
+                r8["i"] = (r8["i"] + 1) % copies
+                return wq8[r8["i"]]
+            if masked:
+                fwd8 = lambda: gg.fp8_masked_forward(t8["x8"], xsc, wpick(), wsc, grp, out=y8)
+            else:
+                fwd8 = lambda: gg.fp8_forward(t8["x8"], xsc, wpick(), wsc, grp, out=y8)
+            pack8 = lambda: gg.fp8_pack_scales(lay, t8["sx"], grp, w8.m, w8.k, e8, out=xsc)
+            reps = 10 if name == "fp8_glm_up" else 30
+            _, ms8 = time_passes([("fwd", fwd8), ("pack", pack8)], reps, 3, torch)
+            f8 = {k: sorted(v)[len(v) // 2] for k, v in ms8.items()}
+            act = w8.active_rows()
+            live8 = int((w8.group_sizes() > 0).sum())
+            ab8 = act * w8.k + live8 * w8.n * w8.k + 2 * act * w8.n
+            tf8 = w8.flops() / (f8["fwd"] * 1e-3) / 1e12
+            context[name] = {"fwd": {"ms": round(f8["fwd"], 4), "TFLOP/s": round(tf8, 2),
+                                     "frac_of_fp8_mfma_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
+                                     "algorithmic_GB/s": round(ab8 / (f8["fwd"] * 1e-3) / 1e9, 1)},
+                             "pack_x_scales_ms": round(f8["pack"], 4)}
+            if masked:
+                context[name]["weights"] = "rotated over 3 copies (HBM-resident per call)"
+            del t8, wq8, wsc, xsc, y8
+            torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
