@@ -233,6 +233,54 @@ gg_status gg_masked_wgrad_ex(const void* x, const void* dy,
                              float beta, void* stream);
 
 /*
+ * [E, N, K] weight layout
+ * -----------------------
+ * The same passes with each expert's weight stored transposed, W[g] as
+ * [n, k] (k contiguous) and dW as [E, n, k]: the "NT" / "TN" forms the
+ * grouped GEMM dispatches besides "NN" (TransformerEngine PR #3542,
+ * "Summary": TN, NN and NT dispatch), and the layout of the fp8 call's
+ * weight (sglang PR #32385, "Evidence": the "nt" grouped GEMM).
+ *
+ *   gg_forward_nk         y[i, :]  = x[i, :] . W[g]^T        x [m, k], y [m, n]
+ *   gg_dgrad_nk           dx[i, :] = dy[i, :] . W[g]         dy [m, n], dx [m, k]
+ *   gg_wgrad_nk           dW[g]    = dy[rows of g]^T . x[rows of g]   dW [E, n, k]
+ *   gg_masked_forward_nk  y[e, r, :] = x[e, r, :] . W[e]^T, r < masked_m[e]
+ *
+ * Arguments, requirements, ownership and errors are those of the [E, k, n]
+ * entry point of the same pass; the _ex forms add alpha and beta as above.
+ */
+gg_status gg_forward_nk(const void* x, const void* w, const int32_t* offs,
+                        void* y, gg_dtype y_dtype, int64_t m, int64_t k,
+                        int64_t n, int32_t num_groups, void* stream);
+gg_status gg_dgrad_nk(const void* dy, const void* w, const int32_t* offs,
+                      void* dx, gg_dtype dx_dtype, int64_t m, int64_t k,
+                      int64_t n, int32_t num_groups, void* stream);
+gg_status gg_wgrad_nk(const void* x, const void* dy, const int32_t* offs,
+                      void* dw, gg_dtype dw_dtype, int64_t m, int64_t k,
+                      int64_t n, int32_t num_groups, void* stream);
+gg_status gg_masked_forward_nk(const void* x, const void* w,
+                               const int32_t* masked_m, void* y,
+                               gg_dtype y_dtype, int64_t max_m, int64_t k,
+                               int64_t n, int32_t num_groups, void* stream);
+gg_status gg_forward_nk_ex(const void* x, const void* w, const int32_t* offs,
+                           void* y, gg_dtype y_dtype, int64_t m, int64_t k,
+                           int64_t n, int32_t num_groups, float alpha,
+                           float beta, void* stream);
+gg_status gg_dgrad_nk_ex(const void* dy, const void* w, const int32_t* offs,
+                         void* dx, gg_dtype dx_dtype, int64_t m, int64_t k,
+                         int64_t n, int32_t num_groups, float alpha,
+                         float beta, void* stream);
+gg_status gg_wgrad_nk_ex(const void* x, const void* dy, const int32_t* offs,
+                         void* dw, gg_dtype dw_dtype, int64_t m, int64_t k,
+                         int64_t n, int32_t num_groups, float alpha,
+                         float beta, void* stream);
+gg_status gg_masked_forward_nk_ex(const void* x, const void* w,
+                                  const int32_t* masked_m, void* y,
+                                  gg_dtype y_dtype, int64_t max_m, int64_t k,
+                                  int64_t n, int32_t num_groups, float alpha,
+                                  float beta, void* stream);
+
+/*
  * FP8 (e4m3) block-scaled forward
  * -------------------------------
  * The fp8 form of the forward and masked forward (sglang PR #32385: the

@@ -63,13 +63,15 @@ def load():
     I32 = ctypes.c_int32
     sig = [P, P, P, P, ctypes.c_int, I64, I64, I64, I32, P]
     for name in ("gg_forward", "gg_dgrad", "gg_wgrad", "gg_masked_forward", "gg_masked_dgrad",
-                 "gg_masked_wgrad", "gg_forward_silu_mul", "gg_masked_forward_silu_mul"):
+                 "gg_masked_wgrad", "gg_forward_silu_mul", "gg_masked_forward_silu_mul",
+                 "gg_forward_nk", "gg_dgrad_nk", "gg_wgrad_nk", "gg_masked_forward_nk"):
         f = getattr(lib, name)
         f.argtypes = sig
         f.restype = ctypes.c_int
     sig_ex = sig[:-1] + [ctypes.c_float, ctypes.c_float, P]
     for name in ("gg_forward_ex", "gg_dgrad_ex", "gg_wgrad_ex", "gg_masked_forward_ex",
-                 "gg_masked_dgrad_ex", "gg_masked_wgrad_ex"):
+                 "gg_masked_dgrad_ex", "gg_masked_wgrad_ex", "gg_forward_nk_ex", "gg_dgrad_nk_ex",
+                 "gg_wgrad_nk_ex", "gg_masked_forward_nk_ex"):
         f = getattr(lib, name)
         f.argtypes = sig_ex
         f.restype = ctypes.c_int
@@ -348,6 +350,96 @@ def masked_forward_silu_mul(x, w13, masked_m, out=None, out_dtype=None):
         raise ValueError(f"out must be [{e}, {max_m}, {n // 2}]")
     _invoke("gg_masked_forward_silu_mul", x, w13, masked_m, out, _dtype_code(out.dtype), max_m, k, n,
             e, dev)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# [E, N, K] weight layout
+# ---------------------------------------------------------------------------
+
+def forward_nk(x, w, offs, out=None, out_dtype=None, alpha=1.0, beta=0.0):
+    """Y = X W[g]^T with W [E, n, k] (gg_forward_nk).  x: bf16 [m, k]."""
+    torch = _torch()
+    _need_out(out, beta)
+    dev = x.device
+    _check(x, "x", torch.bfloat16, 2, dev)
+    _check(w, "w", torch.bfloat16, 3, dev)
+    _check(offs, "offs", torch.int32, 1, dev)
+    m, k = x.shape
+    e, n, k2 = w.shape
+    if k2 != k or offs.shape[0] != e:
+        raise ValueError("shape mismatch between x, w and offs")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check(out, "out", out.dtype, 2, dev)
+    if tuple(out.shape) != (m, n):
+        raise ValueError(f"out must be [{m}, {n}]")
+    _invoke("gg_forward_nk", x, w, offs, out, _dtype_code(out.dtype), m, k, n, e, dev, alpha, beta)
+    return out
+
+
+def dgrad_nk(dy, w, offs, out=None, out_dtype=None, alpha=1.0, beta=0.0):
+    """dX = dY W[g] with W [E, n, k] (gg_dgrad_nk).  dy: bf16 [m, n]."""
+    torch = _torch()
+    _need_out(out, beta)
+    dev = dy.device
+    _check(dy, "dy", torch.bfloat16, 2, dev)
+    _check(w, "w", torch.bfloat16, 3, dev)
+    _check(offs, "offs", torch.int32, 1, dev)
+    m, n = dy.shape
+    e, n2, k = w.shape
+    if n2 != n or offs.shape[0] != e:
+        raise ValueError("shape mismatch between dy, w and offs")
+    if out is None:
+        out = torch.empty((m, k), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check(out, "out", out.dtype, 2, dev)
+    if tuple(out.shape) != (m, k):
+        raise ValueError(f"out must be [{m}, {k}]")
+    _invoke("gg_dgrad_nk", dy, w, offs, out, _dtype_code(out.dtype), m, k, n, e, dev, alpha, beta)
+    return out
+
+
+def wgrad_nk(x, dy, offs, out=None, out_dtype=None, alpha=1.0, beta=0.0):
+    """dW[g] = dY[rows of g]^T X[rows of g], dW as [E, n, k] (gg_wgrad_nk)."""
+    torch = _torch()
+    _need_out(out, beta)
+    dev = x.device
+    _check(x, "x", torch.bfloat16, 2, dev)
+    _check(dy, "dy", torch.bfloat16, 2, dev)
+    _check(offs, "offs", torch.int32, 1, dev)
+    m, k = x.shape
+    m2, n = dy.shape
+    e = offs.shape[0]
+    if m2 != m:
+        raise ValueError("x and dy must have the same rows")
+    if out is None:
+        out = torch.empty((e, n, k), dtype=out_dtype or torch.float32, device=dev)
+    _check(out, "out", out.dtype, 3, dev)
+    if tuple(out.shape) != (e, n, k):
+        raise ValueError(f"out must be [{e}, {n}, {k}]")
+    _invoke("gg_wgrad_nk", x, dy, offs, out, _dtype_code(out.dtype), m, k, n, e, dev, alpha, beta)
+    return out
+
+
+def masked_forward_nk(x, w, masked_m, out=None, out_dtype=None, alpha=1.0, beta=0.0):
+    """The masked forward with W [E, n, k] (gg_masked_forward_nk)."""
+    torch = _torch()
+    _need_out(out, beta)
+    dev = x.device
+    _check(x, "x", torch.bfloat16, 3, dev)
+    _check(w, "w", torch.bfloat16, 3, dev)
+    _check(masked_m, "masked_m", torch.int32, 1, dev)
+    e, max_m, k = x.shape
+    e2, n, k2 = w.shape
+    if e2 != e or k2 != k or masked_m.shape[0] != e:
+        raise ValueError("shape mismatch between x, w and masked_m")
+    if out is None:
+        out = torch.empty((e, max_m, n), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check(out, "out", out.dtype, 3, dev)
+    if tuple(out.shape) != (e, max_m, n):
+        raise ValueError(f"out must be [{e}, {max_m}, {n}]")
+    _invoke("gg_masked_forward_nk", x, w, masked_m, out, _dtype_code(out.dtype), max_m, k, n, e, dev,
+            alpha, beta)
     return out
 
 

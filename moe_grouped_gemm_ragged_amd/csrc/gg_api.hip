@@ -207,6 +207,66 @@ gg_status gg_masked_forward(const void* x, const void* w, const int32_t* masked_
                               stream);
 }
 
+// The [E, N, K] weight layout runs the [E, K, N] kernels with the roles of
+// the dimensions exchanged: y = x W[g]^T is the dgrad form (x as its "dy",
+// k as its n), dx = dy W[g] with W[g] [n, k] the forward form, dW[g]^T =
+// dy^T x the wgrad form with its operands swapped, and the masked forward
+// the masked dgrad form.
+gg_status gg_forward_nk_ex(const void* x, const void* w, const int32_t* offs, void* y, gg_dtype y_dtype,
+                           int64_t m, int64_t k, int64_t n, int32_t num_groups, float alpha, float beta,
+                           void* stream) {
+  gg_status s = check(x, w, offs, y, y_dtype, m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  return run(1, x, w, offs, y, y_dtype, m, n, k, num_groups, alpha, beta, stream);
+}
+
+gg_status gg_dgrad_nk_ex(const void* dy, const void* w, const int32_t* offs, void* dx, gg_dtype dx_dtype,
+                         int64_t m, int64_t k, int64_t n, int32_t num_groups, float alpha, float beta,
+                         void* stream) {
+  gg_status s = check(dy, w, offs, dx, dx_dtype, m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  return run(0, dy, w, offs, dx, dx_dtype, m, n, k, num_groups, alpha, beta, stream);
+}
+
+gg_status gg_wgrad_nk_ex(const void* x, const void* dy, const int32_t* offs, void* dw, gg_dtype dw_dtype,
+                         int64_t m, int64_t k, int64_t n, int32_t num_groups, float alpha, float beta,
+                         void* stream) {
+  gg_status s = check(x, dy, offs, dw, dw_dtype, m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  return run(2, dy, x, offs, dw, dw_dtype, m, n, k, num_groups, alpha, beta, stream);
+}
+
+gg_status gg_masked_forward_nk_ex(const void* x, const void* w, const int32_t* masked_m, void* y,
+                                  gg_dtype y_dtype, int64_t max_m, int64_t k, int64_t n,
+                                  int32_t num_groups, float alpha, float beta, void* stream) {
+  gg_status s = check(x, w, masked_m, y, y_dtype, max_m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  s = masked_rows(max_m, num_groups);
+  if (s != GG_OK) return s;
+  return run(4, x, w, masked_m, y, y_dtype, max_m, n, k, num_groups, alpha, beta, stream);
+}
+
+gg_status gg_forward_nk(const void* x, const void* w, const int32_t* offs, void* y, gg_dtype y_dtype,
+                        int64_t m, int64_t k, int64_t n, int32_t num_groups, void* stream) {
+  return gg_forward_nk_ex(x, w, offs, y, y_dtype, m, k, n, num_groups, 1.0f, 0.0f, stream);
+}
+
+gg_status gg_dgrad_nk(const void* dy, const void* w, const int32_t* offs, void* dx, gg_dtype dx_dtype,
+                      int64_t m, int64_t k, int64_t n, int32_t num_groups, void* stream) {
+  return gg_dgrad_nk_ex(dy, w, offs, dx, dx_dtype, m, k, n, num_groups, 1.0f, 0.0f, stream);
+}
+
+gg_status gg_wgrad_nk(const void* x, const void* dy, const int32_t* offs, void* dw, gg_dtype dw_dtype,
+                      int64_t m, int64_t k, int64_t n, int32_t num_groups, void* stream) {
+  return gg_wgrad_nk_ex(x, dy, offs, dw, dw_dtype, m, k, n, num_groups, 1.0f, 0.0f, stream);
+}
+
+gg_status gg_masked_forward_nk(const void* x, const void* w, const int32_t* masked_m, void* y,
+                               gg_dtype y_dtype, int64_t max_m, int64_t k, int64_t n, int32_t num_groups,
+                               void* stream) {
+  return gg_masked_forward_nk_ex(x, w, masked_m, y, y_dtype, max_m, k, n, num_groups, 1.0f, 0.0f, stream);
+}
+
 int64_t gg_fp8_scale_bytes(gg_fp8_scale_layout layout, int64_t rows, int64_t k, int32_t num_groups) {
   if (layout < GG_FP8_ACT_RAGGED || layout > GG_FP8_WEIGHT) return -1;
   if (rows < 0 || k < 128 || k % 128 != 0 || k > GG_MAX_KN) return -1;

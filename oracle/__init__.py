@@ -419,3 +419,40 @@ def ue8m0_violations(scales, active=None) -> int:
     if active is not None:
         bad = bad & np.asarray(active, dtype=bool)
     return int(bad.sum())
+
+
+# ---- [E, N, K] weight layout --------------------------------------------------
+# The same passes with W[g] stored as its transpose [n, k] and dW as
+# [E, n, k] (TransformerEngine PR #3542, "Summary": TN / NN / NT forms).  A
+# layout only: the weight is transposed (a copy, no arithmetic) and the
+# [E, K, N] function computes.
+
+def _t(w):
+    return np.ascontiguousarray(np.swapaxes(_u16(w), 1, 2))
+
+
+def forward_nk(x, w_nk, offs, rows=None) -> Result:
+    """Y = X W[g]^T with w_nk uint16 [E, N, K]."""
+    return forward(x, _t(w_nk), offs, rows=rows)
+
+
+def dgrad_nk(dy, w_nk, offs, rows=None) -> Result:
+    """dX = dY W[g] with w_nk uint16 [E, N, K] (dX rows are K wide)."""
+    return dgrad(dy, _t(w_nk), offs, rows=rows)
+
+
+def wgrad_nk(x, dy, offs, num_groups=None) -> Result:
+    """dW[g] as [N, K]: the rows of the result are (g, n) pairs in order."""
+    res = wgrad(x, dy, offs, num_groups=num_groups)
+    e = len(offs) if num_groups is None else num_groups
+    k = x.shape[1]
+    n = dy.shape[1]
+    v = np.ascontiguousarray(np.swapaxes(res.value.reshape(e, k, n), 1, 2)).reshape(e * n, k)
+    sa = np.ascontiguousarray(np.swapaxes(res.sabs.reshape(e, k, n), 1, 2)).reshape(e * n, k)
+    st = np.ones(e * n, dtype=np.int32)
+    idx = np.stack([np.repeat(np.arange(e), n), np.tile(np.arange(n), e)], axis=1)
+    return Result(v, sa, st, idx)
+
+
+def masked_forward_nk(x, w_nk, masked_m, rows=None) -> Result:
+    return masked_forward(x, _t(w_nk), masked_m, rows=rows)

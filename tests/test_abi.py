@@ -186,3 +186,18 @@ def call_pack(**kw):
 def test_fp8_pack_scales_checks_arguments(lib, case, status):
     rc = call_pack(**case)
     assert rc == status, (case, rc, gg.last_error())
+
+
+NK_ENTRY = ["gg_forward_nk", "gg_dgrad_nk", "gg_wgrad_nk", "gg_masked_forward_nk"]
+
+
+@pytest.mark.parametrize("name", NK_ENTRY)
+@pytest.mark.parametrize("case,status", [
+    (dict(a=0), 1), (dict(g=0), 1), (dict(k=12), 2), (dict(n=20), 2), (dict(m=-1), 2),
+    (dict(b=A + 2), 3), (dict(dt=2), 4), (dict(e=0), 5),
+])
+def test_nk_entry_points_check_arguments(lib, name, case, status):
+    rc = call(name, **case)
+    assert rc == status, (name, case, rc, gg.last_error())
+    rc = call_ex(name + "_ex", 0.5, 1.0, **case)
+    assert rc == status, (name + "_ex", case, rc, gg.last_error())
