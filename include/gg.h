@@ -281,6 +281,38 @@ gg_status gg_masked_forward_nk_ex(const void* x, const void* w,
                                   float beta, void* stream);
 
 /*
+ * Grouped bias with a per-token factor
+ * ------------------------------------
+ *   y[i, :] = alpha * (x[i, :] . W[g]) + beta * y[i, :] + s[i] * bias[g, :]
+ * over the rows i of each expert g, combined in fp32 and rounded once.
+ *   bias        bf16 [E, n], device memory, 16-byte aligned
+ *   bias_scale  fp32 per-token factors s, device memory, or NULL for s = 1.
+ *               Indexed by output row (masked: e * max_m + r); only rows
+ *               an expert owns are read, so for the ragged layout it needs
+ *               just end(E-1) entries -- the logical tokens -- however much
+ *               unused capacity x and y carry (TransformerEngine PR #3542,
+ *               review finding "Bias scaling breaks capacity": the scale
+ *               vector covers the logical rows only and the capacity rows
+ *               must be preserved).
+ * Rows past end(E-1) (masked: at or past masked_m[e]) are neither read nor
+ * written.  Otherwise as gg_forward_ex / gg_masked_forward_ex.
+ * Cited passage: TransformerEngine PR #3542, "Summary" (grouped bias applied
+ * to the grouped GEMM's output, optionally scaled per token) and the review
+ * finding above.
+ */
+gg_status gg_forward_bias(const void* x, const void* w, const int32_t* offs,
+                          const void* bias, const float* bias_scale, void* y,
+                          gg_dtype y_dtype, int64_t m, int64_t k, int64_t n,
+                          int32_t num_groups, float alpha, float beta,
+                          void* stream);
+gg_status gg_masked_forward_bias(const void* x, const void* w,
+                                 const int32_t* masked_m, const void* bias,
+                                 const float* bias_scale, void* y,
+                                 gg_dtype y_dtype, int64_t max_m, int64_t k,
+                                 int64_t n, int32_t num_groups, float alpha,
+                                 float beta, void* stream);
+
+/*
  * FP8 (e4m3) block-scaled forward
  * -------------------------------
  * The fp8 form of the forward and masked forward (sglang PR #32385: the

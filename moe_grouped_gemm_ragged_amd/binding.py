@@ -75,6 +75,11 @@ def load():
         f = getattr(lib, name)
         f.argtypes = sig_ex
         f.restype = ctypes.c_int
+    for name in ("gg_forward_bias", "gg_masked_forward_bias"):
+        f = getattr(lib, name)
+        f.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, I32, ctypes.c_float,
+                      ctypes.c_float, P]
+        f.restype = ctypes.c_int
     lib.gg_fp8_scale_bytes.argtypes = [ctypes.c_int, I64, I64, I32]
     lib.gg_fp8_scale_bytes.restype = ctypes.c_int64
     lib.gg_fp8_pack_scales.argtypes = [ctypes.c_int, P, ctypes.c_int, I64, P, I64, I64, I32, P, P, P]
@@ -350,6 +355,73 @@ def masked_forward_silu_mul(x, w13, masked_m, out=None, out_dtype=None):
         raise ValueError(f"out must be [{e}, {max_m}, {n // 2}]")
     _invoke("gg_masked_forward_silu_mul", x, w13, masked_m, out, _dtype_code(out.dtype), max_m, k, n,
             e, dev)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# grouped bias with a per-token factor
+# ---------------------------------------------------------------------------
+
+def _bias_call(name, x, w, groups, bias, bias_scale, out, m, k, n, e, dev, alpha, beta):
+    torch = _torch()
+    _check(bias, "bias", torch.bfloat16, 2, dev)
+    if tuple(bias.shape) != (e, n):
+        raise ValueError(f"bias must be [{e}, {n}]")
+    if bias_scale is not None:
+        if bias_scale.dtype != torch.float32 or bias_scale.device != dev or not bias_scale.is_contiguous():
+            raise TypeError("bias_scale must be a contiguous float32 tensor on the device")
+    rc = call_raw(name, x.data_ptr(), w.data_ptr(), groups.data_ptr(), bias.data_ptr(),
+                  None if bias_scale is None else bias_scale.data_ptr(), out.data_ptr(),
+                  _dtype_code(out.dtype), int(m), int(k), int(n), int(e), float(alpha), float(beta),
+                  _stream_handle(dev))
+    if rc != 0:
+        raise GGError(name, rc, last_error())
+
+
+def forward_bias(x, w, offs, bias, bias_scale=None, out=None, out_dtype=None, alpha=1.0, beta=0.0):
+    """Y[i] = alpha X[i] W[g] + beta Y[i] + s[i] bias[g] on the rows of each
+    expert (gg_forward_bias).  bias: bf16 [E, n]; bias_scale: fp32 with at
+    least offs[-1] entries (the logical tokens), or None for 1."""
+    torch = _torch()
+    _need_out(out, beta)
+    dev = x.device
+    _check(x, "x", torch.bfloat16, 2, dev)
+    _check(w, "w", torch.bfloat16, 3, dev)
+    _check(offs, "offs", torch.int32, 1, dev)
+    m, k = x.shape
+    e, k2, n = w.shape
+    if k2 != k or offs.shape[0] != e:
+        raise ValueError("shape mismatch between x, w and offs")
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check(out, "out", out.dtype, 2, dev)
+    if tuple(out.shape) != (m, n):
+        raise ValueError(f"out must be [{m}, {n}]")
+    _bias_call("gg_forward_bias", x, w, offs, bias, bias_scale, out, m, k, n, e, dev, alpha, beta)
+    return out
+
+
+def masked_forward_bias(x, w, masked_m, bias, bias_scale=None, out=None, out_dtype=None, alpha=1.0,
+                        beta=0.0):
+    """The masked forward plus s[e, r] bias[e] on active rows
+    (gg_masked_forward_bias); bias_scale: fp32 [E, max_m] or None."""
+    torch = _torch()
+    _need_out(out, beta)
+    dev = x.device
+    _check(x, "x", torch.bfloat16, 3, dev)
+    _check(w, "w", torch.bfloat16, 3, dev)
+    _check(masked_m, "masked_m", torch.int32, 1, dev)
+    e, max_m, k = x.shape
+    e2, k2, n = w.shape
+    if e2 != e or k2 != k or masked_m.shape[0] != e:
+        raise ValueError("shape mismatch between x, w and masked_m")
+    if out is None:
+        out = torch.empty((e, max_m, n), dtype=out_dtype or torch.bfloat16, device=dev)
+    _check(out, "out", out.dtype, 3, dev)
+    if tuple(out.shape) != (e, max_m, n):
+        raise ValueError(f"out must be [{e}, {max_m}, {n}]")
+    _bias_call("gg_masked_forward_bias", x, w, masked_m, bias, bias_scale, out, max_m, k, n, e, dev,
+               alpha, beta)
     return out
 
 

@@ -73,11 +73,12 @@ gg_status check(const void* p0, const void* p1, const void* groups, const void* 
 }
 
 gg_status run(int mode, const void* a, const void* b, const int32_t* groups, void* c, gg_dtype dt,
-              int64_t m, int64_t k, int64_t n, int32_t E, float alpha, float beta, void* stream) {
+              int64_t m, int64_t k, int64_t n, int32_t E, float alpha, float beta, void* stream,
+              const void* bias = nullptr, const float* bias_scale = nullptr) {
   int cus = 0;
   gg_status s = device_cus(&cus);
   if (s != GG_OK) return s;
-  hipError_t e = gg::launch(mode, a, b, groups, c, dt == GG_F32, m, k, n, E, alpha, beta, cus,
+  hipError_t e = gg::launch(mode, a, b, groups, c, dt == GG_F32, m, k, n, E, alpha, beta, bias, bias_scale, cus,
                             static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_error = std::string("kernel launch: ") + hipGetErrorString(e);
@@ -265,6 +266,35 @@ gg_status gg_masked_forward_nk(const void* x, const void* w, const int32_t* mask
                                gg_dtype y_dtype, int64_t max_m, int64_t k, int64_t n, int32_t num_groups,
                                void* stream) {
   return gg_masked_forward_nk_ex(x, w, masked_m, y, y_dtype, max_m, k, n, num_groups, 1.0f, 0.0f, stream);
+}
+
+static gg_status bias_args(const void* bias, const float* bias_scale) {
+  if (!bias) return fail(GG_ERR_NULL_PTR, "bias is NULL");
+  if (!aligned16(bias) || (reinterpret_cast<uintptr_t>(bias_scale) & 3u))
+    return fail(GG_ERR_ALIGNMENT, "bias must be 16-byte aligned and bias_scale 4-byte aligned");
+  return GG_OK;
+}
+
+gg_status gg_forward_bias(const void* x, const void* w, const int32_t* offs, const void* bias,
+                          const float* bias_scale, void* y, gg_dtype y_dtype, int64_t m, int64_t k, int64_t n,
+                          int32_t num_groups, float alpha, float beta, void* stream) {
+  gg_status s = check(x, w, offs, y, y_dtype, m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  s = bias_args(bias, bias_scale);
+  if (s != GG_OK) return s;
+  return run(0, x, w, offs, y, y_dtype, m, k, n, num_groups, alpha, beta, stream, bias, bias_scale);
+}
+
+gg_status gg_masked_forward_bias(const void* x, const void* w, const int32_t* masked_m, const void* bias,
+                                 const float* bias_scale, void* y, gg_dtype y_dtype, int64_t max_m, int64_t k,
+                                 int64_t n, int32_t num_groups, float alpha, float beta, void* stream) {
+  gg_status s = check(x, w, masked_m, y, y_dtype, max_m, k, n, num_groups);
+  if (s != GG_OK) return s;
+  s = masked_rows(max_m, num_groups);
+  if (s != GG_OK) return s;
+  s = bias_args(bias, bias_scale);
+  if (s != GG_OK) return s;
+  return run(3, x, w, masked_m, y, y_dtype, max_m, k, n, num_groups, alpha, beta, stream, bias, bias_scale);
 }
 
 int64_t gg_fp8_scale_bytes(gg_fp8_scale_layout layout, int64_t rows, int64_t k, int32_t num_groups) {

@@ -12,11 +12,14 @@ namespace gg {
 // 5 masked wgrad, 6 forward with the SiLU-mul activation, 7 masked forward
 // with the SiLU-mul activation.  Arguments were
 // validated by the caller.  Writes alpha * product + beta * (prior output)
-// (the prior output is not read when beta == 0).  Launches one persistent
-// grid of at most num_cus workgroups on `stream`.
+// (the prior output is not read when beta == 0), plus bias_scale[row] *
+// bias[expert, col] when bias is non-null (modes 0 and 3 only; bias is
+// bf16 [E, output cols], bias_scale fp32 indexed by the output row, null for
+// 1).  Launches one persistent grid of at most num_cus workgroups on `stream`.
 hipError_t launch(int mode, const void* a, const void* b, const int32_t* groups, void* c,
                   bool out_f32, int64_t m, int64_t k, int64_t n, int32_t num_groups,
-                  float alpha, float beta, int num_cus, hipStream_t stream);
+                  float alpha, float beta, const void* bias, const float* bias_scale, int num_cus,
+                  hipStream_t stream);
 
 // The fp8 (e4m3) block-scaled forward, ragged (groups = end offsets) or
 // masked (groups = masked_m, m = max_m): x [rows, k] and w [E, n, k] e4m3,

@@ -114,7 +114,13 @@ struct Params {
   float beta;               // (the output is not read when beta == 0)
   const uint8_t* sa;        // fp8: X's scales, packed (E8M0 bytes, see the fp8 section)
   const uint8_t* sb;        // fp8: W's scales, packed
+  const uint16_t* bias;     // row passes: bf16 [E, output cols] added to each row, or null
+  const float* bias_scale;  // its per-row factor (absolute row index), or null for 1
 };
+
+// Passes whose epilogue can add the grouped bias: the forward, ragged and
+// masked.
+constexpr bool has_bias(int mode) { return mode == FWD || mode == MASKED; }
 
 // One operand tile: element (tile row r, reduction index q) of the tile
 // lives at byte origin + 2 (r * ld + q) (red-contig) or origin + 2 (q * ld +
@@ -721,7 +727,9 @@ constexpr int kSlabPitch = 64 * 4 + 16;
 template <int TMA, bool OUT_F32, bool SCALED>
 __device__ __forceinline__ void store_tile_lds(uint8_t* cbase, uint32_t ldc_bytes, int rows, int cols,
                                                int wm, int wn, int lane, const floatx16 (&acc)[TM][TN],
-                                               uint8_t* slab, float alpha, float beta) {
+                                               uint8_t* slab, float alpha, float beta,
+                                               const uint16_t* bias = nullptr,
+                                               const float* bscale = nullptr) {
   constexpr uint32_t esz = OUT_F32 ? 4 : 2;
   const uint32_t nrec = (uint32_t)(rows - 1) * ldc_bytes + (uint32_t)cols * esz;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(cbase, nrec);
@@ -770,6 +778,26 @@ __device__ __forceinline__ void store_tile_lds(uint8_t* cbase, uint32_t ldc_byte
           }
           lo = lo + clo * beta;
           hi = hi + chi * beta;
+        }
+        if (bias) {
+          // + s[row] * bias[col]: the tile's bias row (its 8 columns of this
+          // lane) and the row's factor, both through range-checked
+          // resources (columns past cols and rows past rows read as zero)
+          const uint32_t boff = col_ok ? opaque_v((uint32_t)gcol * 2u) : kOutOfRange;
+          const u32x4 b = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(bias, (uint32_t)cols * 2u), boff, 0, 0));
+          const floatx4 blo = {__builtin_bit_cast(float, b[0] << 16), __builtin_bit_cast(float, b[0] & 0xFFFF0000u),
+                               __builtin_bit_cast(float, b[1] << 16), __builtin_bit_cast(float, b[1] & 0xFFFF0000u)};
+          const floatx4 bhi = {__builtin_bit_cast(float, b[2] << 16), __builtin_bit_cast(float, b[2] & 0xFFFF0000u),
+                               __builtin_bit_cast(float, b[3] << 16), __builtin_bit_cast(float, b[3] & 0xFFFF0000u)};
+          float sc = 1.0f;
+          if (bscale) {
+            const uint32_t r = (uint32_t)(32 * TMA * wm + 32 * i + 8 * q) + opaque_v((uint32_t)(lane >> 3));
+            sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                               make_rsrc(bscale, (uint32_t)rows * 4u), r * 4u, 0, 0));
+          }
+          lo = lo + blo * sc;
+          hi = hi + bhi * sc;
         }
       }
       if constexpr (OUT_F32) {
@@ -1012,6 +1040,8 @@ struct Tile {
   int rows, cols;       // valid output rows / columns of the tile
   const uint8_t* sa;    // fp8: the tile's packed X scales (k-block 0)
   const uint8_t* sb;    // fp8: the tile's packed W scales
+  const uint16_t* bias;   // the expert's bias at the tile's first column, or null
+  const float* bscale;    // the bias factor of the tile's first row, or null
 };
 
 
@@ -1091,6 +1121,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     B.split = 0;
     T.sa = nullptr;
     T.sb = nullptr;
+    T.bias = nullptr;
+    T.bscale = nullptr;
     if constexpr (is_wgrad(MODE)) {
       const int g = (int)(rt_all / row_tiles_w);
       const int rt = (int)(rt_all % row_tiles_w);
@@ -1185,6 +1217,12 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
       }
       T.rows = rows;
       T.cols = B.rows;
+      if constexpr (has_bias(MODE)) {
+        if (p.bias) {
+          T.bias = p.bias + (int64_t)g * p.n + col0;
+          T.bscale = p.bias_scale ? p.bias_scale + arow : nullptr;
+        }
+      }
     }
   };
   auto issue_prologue = [&](const Tile& T) __attribute__((always_inline)) {
@@ -1210,7 +1248,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   int prev_stores = 0;    // fp32 stores issued after the current tile's prologue loads
   // The scaled form (alpha != 1 or beta != 0) goes through the LDS epilogue
   // for both output types.
-  const bool scaled = p.alpha != 1.0f || p.beta != 0.0f;
+  const bool scaled = p.alpha != 1.0f || p.beta != 0.0f || p.bias != nullptr;
   for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
     floatx16 acc[TM][TN];
 #pragma unroll
@@ -1281,10 +1319,10 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
       } else if (scaled) {
         if (half)
           store_tile_lds<2, OUT_F32, true>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane,
-                                           acc, slab, p.alpha, p.beta);
+                                           acc, slab, p.alpha, p.beta, cur.bias, cur.bscale);
         else
           store_tile_lds<TM, OUT_F32, true>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane,
-                                            acc, slab, p.alpha, p.beta);
+                                            acc, slab, p.alpha, p.beta, cur.bias, cur.bscale);
       } else if constexpr (!OUT_F32 || is_fp8(MODE)) {
         if (half)
           store_tile_lds<2, OUT_F32, false>(cur.cbase, cur.ldc_bytes, cur.rows, cur.cols, wm, wn, lane,
@@ -1334,7 +1372,8 @@ static int64_t max_tiles(int mode, int64_t m, int64_t k, int64_t n, int64_t E) {
 
 hipError_t launch(int mode, const void* a, const void* b, const int32_t* groups, void* c,
                   bool out_f32, int64_t m, int64_t k, int64_t n, int32_t num_groups,
-                  float alpha, float beta, int num_cus, hipStream_t stream) {
+                  float alpha, float beta, const void* bias, const float* bias_scale, int num_cus,
+                  hipStream_t stream) {
   Params p;
   p.a = static_cast<const uint16_t*>(a);
   p.b = static_cast<const uint16_t*>(b);
@@ -1346,6 +1385,10 @@ hipError_t launch(int mode, const void* a, const void* b, const int32_t* groups,
   p.num_groups = num_groups;
   p.alpha = alpha;
   p.beta = beta;
+  p.sa = nullptr;
+  p.sb = nullptr;
+  p.bias = static_cast<const uint16_t*>(bias);
+  p.bias_scale = bias_scale;
   const int64_t tiles = max_tiles(mode, m, k, n, num_groups);
   if (tiles <= 0) return hipSuccess;
   const int grid = (int)(tiles < num_cus ? tiles : num_cus);
@@ -1379,6 +1422,8 @@ hipError_t launch_fp8(bool masked, const void* x, const void* sx, const void* w,
   p.beta = 0.0f;
   p.sa = static_cast<const uint8_t*>(sx);
   p.sb = static_cast<const uint8_t*>(sw);
+  p.bias = nullptr;
+  p.bias_scale = nullptr;
   const int mode = masked ? FP8_MASKED : FP8;
   const int64_t tiles = max_tiles(mode, m, k, n, num_groups);
   if (tiles <= 0) return hipSuccess;

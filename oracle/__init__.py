@@ -456,3 +456,63 @@ def wgrad_nk(x, dy, offs, num_groups=None) -> Result:
 
 def masked_forward_nk(x, w_nk, masked_m, rows=None) -> Result:
     return masked_forward(x, _t(w_nk), masked_m, rows=rows)
+
+
+# ---- grouped bias with a per-token factor ---------------------------------------
+# y[i, :] = alpha P[i, :] + beta C[i, :] + s[i] bias[g, :] over the rows i of
+# each expert g (TransformerEngine PR #3542, "Summary": grouped bias applied
+# to the grouped GEMM's output; review finding "Bias scaling breaks
+# capacity": s covers the logical rows only and capacity rows are kept), in
+# fp64 before the one rounding.
+
+def _clamped_ends(offs, m):
+    ends = np.zeros(len(offs), dtype=np.int64)
+    prev = 0
+    for g, o in enumerate(np.asarray(offs, dtype=np.int64)):
+        e = min(max(int(o), prev), m)
+        ends[g] = e
+        prev = e
+    return ends
+
+
+def _add_bias(res: Result, groups_of_rows, bias, scale_of_rows) -> Result:
+    b = decode_bf16(np.asarray(bias, dtype=np.uint16))
+    ok = res.status == 1
+    add = np.zeros_like(res.value)
+    add[ok] = scale_of_rows[ok, None] * b[groups_of_rows[ok]]
+    value = np.where(ok[:, None], res.value + add, res.value)
+    sabs = np.where(ok[:, None], res.sabs + np.abs(add), res.sabs)
+    return Result(value, sabs, res.status, res.index)
+
+
+def forward_bias(x, w, offs, bias, bias_scale=None, rows=None, alpha=1.0, beta=0.0, c_in=None) -> Result:
+    """Rows of the ragged forward plus s[i] bias[g]: bias uint16 bf16 [E, N];
+    bias_scale fp32 indexed by row (at least end(E-1) entries) or None for
+    1.  Rows no expert owns keep status 0."""
+    res = forward(x, w, offs, rows=rows, alpha=alpha, beta=beta, c_in=c_in)
+    m = x.shape[0]
+    ends = _clamped_ends(offs, m)
+    idx = np.asarray(res.index, dtype=np.int64)
+    grp = np.minimum(np.searchsorted(ends, idx, side="right"), len(ends) - 1)
+    sc = np.ones(len(idx)) if bias_scale is None else np.zeros(len(idx))
+    if bias_scale is not None:
+        bs = np.asarray(bias_scale, dtype=np.float32).astype(np.float64)
+        live = res.status == 1
+        sc[live] = bs[idx[live]]
+    return _add_bias(res, grp, bias, sc)
+
+
+def masked_forward_bias(x, w, masked_m, bias, bias_scale=None, rows=None, alpha=1.0, beta=0.0,
+                        c_in=None) -> Result:
+    """The masked forward plus s[e * max_m + r] bias[e] on active rows."""
+    res = masked_forward(x, w, masked_m, rows=rows, alpha=alpha, beta=beta, c_in=c_in)
+    max_m = x.shape[1]
+    idx = np.asarray(res.index, dtype=np.int64)
+    grp = idx // max_m
+    sc = np.ones(len(idx))
+    if bias_scale is not None:
+        bs = np.asarray(bias_scale, dtype=np.float32).astype(np.float64).reshape(-1)
+        live = res.status == 1
+        sc = np.zeros(len(idx))
+        sc[live] = bs[idx[live]]
+    return _add_bias(res, grp, bias, sc)

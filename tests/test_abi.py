@@ -201,3 +201,23 @@ def test_nk_entry_points_check_arguments(lib, name, case, status):
     assert rc == status, (name, case, rc, gg.last_error())
     rc = call_ex(name + "_ex", 0.5, 1.0, **case)
     assert rc == status, (name + "_ex", case, rc, gg.last_error())
+
+
+BIAS_OK = dict(a=A, b=A + 0x100, g=A + 0x200, bias=A + 0x300, bs=A + 0x400, c=A + 0x500, dt=0,
+               m=64, k=64, n=64, e=4, s=0)
+
+
+def call_bias(name, **kw):
+    v = dict(BIAS_OK, **kw)
+    return gg.call_raw(name, v["a"], v["b"], v["g"], v["bias"], v["bs"] or None, v["c"], v["dt"], v["m"],
+                       v["k"], v["n"], v["e"], 1.0, 0.0, v["s"])
+
+
+@pytest.mark.parametrize("name", ["gg_forward_bias", "gg_masked_forward_bias"])
+@pytest.mark.parametrize("case,status", [
+    (dict(a=0), 1), (dict(bias=0), 1), (dict(c=0), 1), (dict(k=12), 2), (dict(m=-1), 2),
+    (dict(bias=A + 8), 3), (dict(bs=A + 2), 3), (dict(dt=2), 4), (dict(e=0), 5),
+])
+def test_bias_entry_points_check_arguments(lib, name, case, status):
+    rc = call_bias(name, **case)
+    assert rc == status, (name, case, rc, gg.last_error())
