@@ -313,6 +313,71 @@ gg_status gg_masked_forward_bias(const void* x, const void* w,
                                  float beta, void* stream);
 
 /*
+ * Producing the grouped layout
+ * ----------------------------
+ * The steps upstream and downstream of the grouped GEMM: offsets from
+ * per-expert row counts, the permutation of token slots into expert-grouped
+ * rows padded to min_alignment_m, the row gather, and the weighted combine
+ * back to tokens.  All run on the device; none reads anything back to the
+ * host (PyTorch issue #152668, "Describe the bug": offsets are created by a
+ * permute-indices kernel with min_alignment_m 8 or 16, and padding empty
+ * experts avoids the hang of that page's backend; TransformerEngine PR
+ * #3224, discussion: m_splits live on the device).
+ *
+ * pad(c) = c rounded up to a multiple of min_alignment (>= 1), and at least
+ * min_alignment when pad_empty != 0.
+ *
+ * gg_offsets_from_splits -- offs[g] = sum_{g' <= g} pad(m_splits[g']).
+ *   m_splits  int64 [num_groups] device (negative counts count as 0)
+ *   offs      int32 [num_groups] device, written
+ *
+ * gg_route -- token-slot -> expert assignment to the grouped layout.
+ *   expert_of_slot  int32 [slots] device: the expert of each (token, k)
+ *                   slot, slot = token * topk + k; values outside
+ *                   [0, num_groups) drop the slot
+ *   offs            int32 [num_groups]: padded end offsets, written
+ *   row_slot        int32 [rows_cap]: for each row below offs[E-1] the slot
+ *                   it holds, or -1 for a padding row; rows past it untouched.
+ *                   Within an expert the slots keep their order.
+ *   rows_cap        >= gg_route_rows_bound(slots, num_groups, min_alignment)
+ *   slot_row        int32 [slots]: the row each slot went to, -1 if dropped
+ *   workspace       gg_route_workspace_bytes(slots, num_groups) bytes of
+ *                   device memory, 16-byte aligned, the caller's; contents
+ *                   on entry do not matter
+ *
+ * gg_gather_rows -- dst[r] = src[row_slot[r] / topk] for r below the last
+ *   end offset, zeros for a padding row; rows past it untouched.  src has
+ *   `tokens` rows and dst rows_cap rows of row_bytes (a multiple of 16) each:
+ *   bf16 or e4m3 activations alike.
+ *
+ * gg_combine_rows -- out[t, :] = sum_k w[t, k] y[slot_row[t * topk + k], :]
+ *   over the slots that were not dropped, in fp32, rounded once to out_dtype.
+ *   y bf16 [rows_cap, n] (n % 8 == 0); weights fp32 [tokens, topk] or NULL
+ *   for 1; out [tokens, n].
+ * Cited passages: PyTorch issue #152668, "Describe the bug" (permute indices
+ * with min_alignment_m; padding empty experts) and "Probably two
+ * resolutions" (a); TransformerEngine PR #3224, discussion (device m_splits).
+ */
+gg_status gg_offsets_from_splits(const int64_t* m_splits, int32_t num_groups,
+                                 int32_t min_alignment, int pad_empty,
+                                 int32_t* offs, void* stream);
+int64_t gg_route_rows_bound(int64_t slots, int32_t num_groups,
+                            int32_t min_alignment);
+int64_t gg_route_workspace_bytes(int64_t slots, int32_t num_groups);
+gg_status gg_route(const int32_t* expert_of_slot, int64_t slots,
+                   int32_t num_groups, int32_t min_alignment, int pad_empty,
+                   int32_t* offs, int32_t* row_slot, int64_t rows_cap,
+                   int32_t* slot_row, void* workspace, void* stream);
+gg_status gg_gather_rows(const void* src, int64_t tokens, int64_t row_bytes,
+                         const int32_t* row_slot, int32_t topk,
+                         const int32_t* offs, int32_t num_groups,
+                         int64_t rows_cap, void* dst, void* stream);
+gg_status gg_combine_rows(const void* y, int64_t n, const int32_t* slot_row,
+                          const float* weights, int32_t topk, int64_t tokens,
+                          int64_t rows_cap, void* out, gg_dtype out_dtype,
+                          void* stream);
+
+/*
  * FP8 (e4m3) block-scaled forward
  * -------------------------------
  * The fp8 form of the forward and masked forward (sglang PR #32385: the

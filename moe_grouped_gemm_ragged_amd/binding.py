@@ -80,6 +80,18 @@ def load():
         f.argtypes = [P, P, P, P, P, P, ctypes.c_int, I64, I64, I64, I32, ctypes.c_float,
                       ctypes.c_float, P]
         f.restype = ctypes.c_int
+    lib.gg_offsets_from_splits.argtypes = [P, I32, I32, ctypes.c_int, P, P]
+    lib.gg_offsets_from_splits.restype = ctypes.c_int
+    lib.gg_route_rows_bound.argtypes = [I64, I32, I32]
+    lib.gg_route_rows_bound.restype = ctypes.c_int64
+    lib.gg_route_workspace_bytes.argtypes = [I64, I32]
+    lib.gg_route_workspace_bytes.restype = ctypes.c_int64
+    lib.gg_route.argtypes = [P, I64, I32, I32, ctypes.c_int, P, P, I64, P, P, P]
+    lib.gg_route.restype = ctypes.c_int
+    lib.gg_gather_rows.argtypes = [P, I64, I64, P, I32, P, I32, I64, P, P]
+    lib.gg_gather_rows.restype = ctypes.c_int
+    lib.gg_combine_rows.argtypes = [P, I64, P, P, I32, I64, I64, P, ctypes.c_int, P]
+    lib.gg_combine_rows.restype = ctypes.c_int
     lib.gg_fp8_scale_bytes.argtypes = [ctypes.c_int, I64, I64, I32]
     lib.gg_fp8_scale_bytes.restype = ctypes.c_int64
     lib.gg_fp8_pack_scales.argtypes = [ctypes.c_int, P, ctypes.c_int, I64, P, I64, I64, I32, P, P, P]
@@ -355,6 +367,96 @@ def masked_forward_silu_mul(x, w13, masked_m, out=None, out_dtype=None):
         raise ValueError(f"out must be [{e}, {max_m}, {n // 2}]")
     _invoke("gg_masked_forward_silu_mul", x, w13, masked_m, out, _dtype_code(out.dtype), max_m, k, n,
             e, dev)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# producing the grouped layout
+# ---------------------------------------------------------------------------
+
+def _raise(name, rc):
+    if rc != 0:
+        raise GGError(name, rc, last_error())
+
+
+def offsets_from_splits(m_splits, min_alignment=1, pad_empty=False, out=None):
+    """int32 end offsets from int64 per-expert row counts on the device
+    (gg_offsets_from_splits), each count padded to min_alignment."""
+    torch = _torch()
+    dev = m_splits.device
+    _check(m_splits, "m_splits", torch.int64, 1, dev)
+    e = m_splits.shape[0]
+    if out is None:
+        out = torch.empty(e, dtype=torch.int32, device=dev)
+    _check(out, "out", torch.int32, 1, dev)
+    _raise("gg_offsets_from_splits", call_raw("gg_offsets_from_splits", m_splits.data_ptr(), int(e),
+                                              int(min_alignment), 1 if pad_empty else 0, out.data_ptr(),
+                                              _stream_handle(dev)))
+    return out
+
+
+def route_rows_bound(slots, num_groups, min_alignment=1) -> int:
+    v = int(load().gg_route_rows_bound(int(slots), int(num_groups), int(min_alignment)))
+    if v < 0:
+        raise ValueError("invalid arguments for gg_route_rows_bound")
+    return v
+
+
+def route(expert_of_slot, num_groups, min_alignment=1, pad_empty=False, rows_cap=None):
+    """Token slots -> grouped layout (gg_route).  expert_of_slot: int32
+    [tokens, topk] (or flat) expert ids.  Returns (offs int32 [E], row_slot
+    int32 [rows_cap], slot_row int32 [slots]); row_slot past offs[-1] is
+    uninitialised."""
+    torch = _torch()
+    dev = expert_of_slot.device
+    if expert_of_slot.dtype != torch.int32 or not expert_of_slot.is_contiguous():
+        raise TypeError("expert_of_slot must be a contiguous int32 tensor")
+    slots = expert_of_slot.numel()
+    cap = route_rows_bound(slots, num_groups, min_alignment) if rows_cap is None else int(rows_cap)
+    offs = torch.empty(num_groups, dtype=torch.int32, device=dev)
+    row_slot = torch.empty(max(cap, 1), dtype=torch.int32, device=dev)
+    slot_row = torch.empty(max(slots, 1), dtype=torch.int32, device=dev)
+    ws = torch.empty(int(load().gg_route_workspace_bytes(slots, num_groups)), dtype=torch.uint8, device=dev)
+    _raise("gg_route", call_raw("gg_route", expert_of_slot.data_ptr(), int(slots), int(num_groups),
+                                int(min_alignment), 1 if pad_empty else 0, offs.data_ptr(),
+                                row_slot.data_ptr(), int(cap), slot_row.data_ptr(), ws.data_ptr(),
+                                _stream_handle(dev)))
+    return offs, row_slot[:cap], slot_row[:slots]
+
+
+def gather_rows(src, row_slot, topk, offs, out=None):
+    """Grouped rows from token rows (gg_gather_rows): src [tokens, ...]
+    (any dtype, rows a multiple of 16 bytes); returns [len(row_slot), ...]."""
+    torch = _torch()
+    dev = src.device
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    tokens = src.shape[0]
+    row_bytes = src[0].numel() * src.element_size() if tokens else src.shape[1:].numel() * src.element_size()
+    rows_cap = row_slot.shape[0]
+    if out is None:
+        out = torch.empty((rows_cap, *src.shape[1:]), dtype=src.dtype, device=dev)
+    _raise("gg_gather_rows", call_raw("gg_gather_rows", src.data_ptr(), int(tokens), int(row_bytes),
+                                      row_slot.data_ptr(), int(topk), offs.data_ptr(), int(offs.shape[0]),
+                                      int(rows_cap), out.data_ptr(), _stream_handle(dev)))
+    return out
+
+
+def combine_rows(y, slot_row, topk, weights=None, out=None, out_dtype=None):
+    """out[t] = sum_k w[t, k] y[slot_row[t topk + k]] (gg_combine_rows): y
+    bf16 [rows, n]; weights fp32 [tokens, topk] or None."""
+    torch = _torch()
+    dev = y.device
+    _check(y, "y", torch.bfloat16, 2, dev)
+    rows_cap, n = y.shape
+    slots = slot_row.numel()
+    tokens = slots // topk
+    if out is None:
+        out = torch.empty((tokens, n), dtype=out_dtype or torch.bfloat16, device=dev)
+    _raise("gg_combine_rows", call_raw("gg_combine_rows", y.data_ptr(), int(n), slot_row.data_ptr(),
+                                       None if weights is None else weights.data_ptr(), int(topk),
+                                       int(tokens), int(rows_cap), out.data_ptr(), _dtype_code(out.dtype),
+                                       _stream_handle(dev)))
     return out
 
 

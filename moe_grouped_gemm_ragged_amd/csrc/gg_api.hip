@@ -297,6 +297,98 @@ gg_status gg_masked_forward_bias(const void* x, const void* w, const int32_t* ma
   return run(3, x, w, masked_m, y, y_dtype, max_m, k, n, num_groups, alpha, beta, stream, bias, bias_scale);
 }
 
+static gg_status hip_result(hipError_t e) {
+  if (e != hipSuccess) {
+    g_last_error = std::string("kernel launch: ") + hipGetErrorString(e);
+    return GG_ERR_HIP;
+  }
+  g_last_error.clear();
+  return GG_OK;
+}
+
+static bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+constexpr int32_t kMaxAlignment = 4096;
+
+gg_status gg_offsets_from_splits(const int64_t* m_splits, int32_t num_groups, int32_t min_alignment,
+                                 int pad_empty, int32_t* offs, void* stream) {
+  if (!m_splits || !offs) return fail(GG_ERR_NULL_PTR, "a required pointer is NULL");
+  if (num_groups < 1 || num_groups > GG_MAX_GROUPS) return fail(GG_ERR_LIMIT, "num_groups must be in [1, GG_MAX_GROUPS]");
+  if (min_alignment < 1 || min_alignment > kMaxAlignment)
+    return fail(GG_ERR_BAD_DIM, "min_alignment must be in [1, 4096]");
+  if ((reinterpret_cast<uintptr_t>(m_splits) & 7u) || !aligned4(offs))
+    return fail(GG_ERR_ALIGNMENT, "m_splits must be 8-byte and offs 4-byte aligned");
+  return hip_result(gg::launch_offsets_from_splits(m_splits, num_groups, min_alignment, pad_empty != 0, offs,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+int64_t gg_route_rows_bound(int64_t slots, int32_t num_groups, int32_t min_alignment) {
+  if (slots < 0 || num_groups < 1 || num_groups > GG_MAX_GROUPS || min_alignment < 1 ||
+      min_alignment > kMaxAlignment)
+    return -1;
+  return slots + (int64_t)num_groups * min_alignment;
+}
+
+int64_t gg_route_workspace_bytes(int64_t slots, int32_t num_groups) {
+  if (slots < 0 || num_groups < 1 || num_groups > GG_MAX_GROUPS) return -1;
+  const int64_t b = gg::route_blocks(slots);
+  return (b > 0 ? b : 1) * (int64_t)num_groups * 4;
+}
+
+gg_status gg_route(const int32_t* expert_of_slot, int64_t slots, int32_t num_groups, int32_t min_alignment,
+                   int pad_empty, int32_t* offs, int32_t* row_slot, int64_t rows_cap, int32_t* slot_row,
+                   void* workspace, void* stream) {
+  if (!offs || !row_slot || !workspace || (slots > 0 && (!expert_of_slot || !slot_row)))
+    return fail(GG_ERR_NULL_PTR, "a required pointer is NULL");
+  if (num_groups < 1 || num_groups > GG_MAX_GROUPS) return fail(GG_ERR_LIMIT, "num_groups must be in [1, GG_MAX_GROUPS]");
+  if (min_alignment < 1 || min_alignment > kMaxAlignment)
+    return fail(GG_ERR_BAD_DIM, "min_alignment must be in [1, 4096]");
+  if (slots < 0) return fail(GG_ERR_BAD_DIM, "slots must be >= 0");
+  const int64_t bound = gg_route_rows_bound(slots, num_groups, min_alignment);
+  if (bound > (int64_t(1) << 31) - 1) return fail(GG_ERR_BAD_DIM, "slots + num_groups * min_alignment exceeds 2^31 - 1");
+  if (rows_cap < bound) return fail(GG_ERR_BAD_DIM, "rows_cap is below gg_route_rows_bound");
+  if (!aligned4(expert_of_slot) || !aligned4(offs) || !aligned4(row_slot) || !aligned4(slot_row) ||
+      !aligned16(workspace))
+    return fail(GG_ERR_ALIGNMENT, "int32 arrays must be 4-byte aligned, workspace 16-byte aligned");
+  return hip_result(gg::launch_route(expert_of_slot, slots, num_groups, min_alignment, pad_empty != 0, offs,
+                                     row_slot, slot_row, static_cast<int32_t*>(workspace),
+                                     static_cast<hipStream_t>(stream)));
+}
+
+gg_status gg_gather_rows(const void* src, int64_t tokens, int64_t row_bytes, const int32_t* row_slot,
+                         int32_t topk, const int32_t* offs, int32_t num_groups, int64_t rows_cap, void* dst,
+                         void* stream) {
+  if (!src || !row_slot || !offs || !dst) return fail(GG_ERR_NULL_PTR, "a required pointer is NULL");
+  if (num_groups < 1 || num_groups > GG_MAX_GROUPS) return fail(GG_ERR_LIMIT, "num_groups must be in [1, GG_MAX_GROUPS]");
+  if (tokens < 0 || rows_cap < 0 || topk < 1 || row_bytes < 16 || row_bytes % 16 != 0)
+    return fail(GG_ERR_BAD_DIM, "need tokens, rows_cap >= 0, topk >= 1, row_bytes a positive multiple of 16");
+  if (rows_cap > (int64_t(1) << 31) - 1 || tokens * (int64_t)topk > (int64_t(1) << 31) - 1)
+    return fail(GG_ERR_BAD_DIM, "row or slot count exceeds 2^31 - 1");
+  if (!aligned16(src) || !aligned16(dst) || !aligned4(row_slot) || !aligned4(offs))
+    return fail(GG_ERR_ALIGNMENT, "src and dst must be 16-byte aligned");
+  int cus = 0;
+  gg_status s = device_cus(&cus);
+  if (s != GG_OK) return s;
+  return hip_result(gg::launch_gather_rows(src, row_bytes, row_slot, topk, offs, num_groups, rows_cap, tokens,
+                                           dst, cus, static_cast<hipStream_t>(stream)));
+}
+
+gg_status gg_combine_rows(const void* y, int64_t n, const int32_t* slot_row, const float* weights, int32_t topk,
+                          int64_t tokens, int64_t rows_cap, void* out, gg_dtype out_dtype, void* stream) {
+  if (!y || !slot_row || !out) return fail(GG_ERR_NULL_PTR, "a required pointer is NULL");
+  if (out_dtype != GG_BF16 && out_dtype != GG_F32) return fail(GG_ERR_BAD_DTYPE, "output dtype must be GG_BF16 or GG_F32");
+  if (n < 8 || n % 8 != 0 || tokens < 0 || topk < 1 || rows_cap < 0)
+    return fail(GG_ERR_BAD_DIM, "need n a positive multiple of 8, tokens, rows_cap >= 0, topk >= 1");
+  if (tokens * (int64_t)topk > (int64_t(1) << 31) - 1) return fail(GG_ERR_BAD_DIM, "slot count exceeds 2^31 - 1");
+  if (!aligned16(y) || !aligned16(out) || !aligned4(slot_row) || !aligned4(weights))
+    return fail(GG_ERR_ALIGNMENT, "y and out must be 16-byte aligned");
+  int cus = 0;
+  gg_status s = device_cus(&cus);
+  if (s != GG_OK) return s;
+  return hip_result(gg::launch_combine_rows(y, n, slot_row, weights, topk, tokens, rows_cap, out,
+                                            out_dtype == GG_F32, cus, static_cast<hipStream_t>(stream)));
+}
+
 int64_t gg_fp8_scale_bytes(gg_fp8_scale_layout layout, int64_t rows, int64_t k, int32_t num_groups) {
   if (layout < GG_FP8_ACT_RAGGED || layout > GG_FP8_WEIGHT) return -1;
   if (rows < 0 || k < 128 || k % 128 != 0 || k > GG_MAX_KN) return -1;

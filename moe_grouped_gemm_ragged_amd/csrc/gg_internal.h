@@ -42,4 +42,18 @@ int64_t fp8_scale_tiles(int layout, int64_t rows, int32_t num_groups);
 hipError_t launch_pack_scales(int layout, bool src_f32, const void* src, int64_t ld_src,
                               const int32_t* groups, int64_t rows, int32_t kblocks, int32_t num_groups,
                               uint8_t* dst, int32_t* bad, int num_cus, hipStream_t stream);
+
+// Routing and layout steps (gg_route.hip).
+int64_t route_blocks(int64_t slots);   // blocks of the route passes; hist holds E * this many ints
+hipError_t launch_offsets_from_splits(const int64_t* splits, int32_t E, int32_t align, bool pad_empty,
+                                      int32_t* offs, hipStream_t stream);
+hipError_t launch_route(const int32_t* expert, int64_t slots, int32_t E, int32_t align, bool pad_empty,
+                        int32_t* offs, int32_t* row_slot, int32_t* slot_row, int32_t* hist,
+                        hipStream_t stream);
+hipError_t launch_gather_rows(const void* src, int64_t row_bytes, const int32_t* row_slot, int32_t topk,
+                              const int32_t* offs, int32_t E, int64_t rows_cap, int64_t tokens, void* dst,
+                              int num_cus, hipStream_t stream);
+hipError_t launch_combine_rows(const void* y, int64_t n, const int32_t* slot_row, const float* w, int32_t topk,
+                               int64_t tokens, int64_t rows_cap, void* out, bool out_f32, int num_cus,
+                               hipStream_t stream);
 }  // namespace gg

@@ -516,3 +516,73 @@ def masked_forward_bias(x, w, masked_m, bias, bias_scale=None, rows=None, alpha=
         sc = np.zeros(len(idx))
         sc[live] = bs[idx[live]]
     return _add_bias(res, grp, bias, sc)
+
+
+# ---- producing the grouped layout ------------------------------------------------
+# PyTorch issue #152668, "Describe the bug": end offsets come from a
+# permute-indices step that rounds each expert's token count up to
+# min_alignment_m and (its fix) pads empty experts; TransformerEngine PR
+# #3224: per-expert counts (m_splits) on the device.  Integer work, written
+# out from those definitions: pad(c) = c rounded up to a multiple of align,
+# at least align when pad_empty.
+
+def pad_count(c: int, align: int, pad_empty: bool) -> int:
+    c = max(int(c), 0)
+    p = -(-c // align) * align
+    if pad_empty and p < align:
+        p = align
+    return p
+
+
+def offsets_from_splits(splits, align=1, pad_empty=False) -> np.ndarray:
+    out, run = [], 0
+    for c in splits:
+        run += pad_count(c, align, pad_empty)
+        out.append(run)
+    return np.array(out, dtype=np.int64)
+
+
+def route(expert_of_slot, num_groups, align=1, pad_empty=False):
+    """Slots (token * topk + k) grouped by expert, each expert's slots in
+    ascending order, followed by its padding rows (-1).  Returns offs,
+    row_slot (length offs[-1]) and slot_row (-1 for a slot whose expert is
+    outside [0, num_groups))."""
+    ids = np.asarray(expert_of_slot, dtype=np.int64).reshape(-1)
+    row_slot, slot_row = [], np.full(len(ids), -1, dtype=np.int64)
+    offs = []
+    for e in range(num_groups):
+        mine = np.flatnonzero(ids == e).tolist()
+        for s in mine:
+            slot_row[s] = len(row_slot)
+            row_slot.append(s)
+        row_slot += [-1] * (pad_count(len(mine), align, pad_empty) - len(mine))
+        offs.append(len(row_slot))
+    return np.array(offs, dtype=np.int64), np.array(row_slot, dtype=np.int64), slot_row
+
+
+def gather_rows(src, row_slot, topk):
+    """Row r of the grouped layout: src[row_slot[r] // topk], zeros for -1."""
+    src = np.asarray(src)
+    out = np.zeros((len(row_slot),) + src.shape[1:], dtype=src.dtype)
+    for r, s in enumerate(row_slot):
+        if s >= 0:
+            out[r] = src[s // topk]
+    return out
+
+
+def combine_rows(y_bits, slot_row, topk, weights=None) -> Result:
+    """out[t] = sum_k w[t, k] y[slot_row[t topk + k]] in fp64 over the slots
+    that were not dropped; y as bf16 bits.  S = sum |w y|."""
+    y = decode_bf16(np.asarray(y_bits, dtype=np.uint16))
+    slot_row = np.asarray(slot_row, dtype=np.int64).reshape(-1)
+    tokens = len(slot_row) // topk
+    w = np.ones((tokens, topk)) if weights is None else np.asarray(weights, dtype=np.float32).astype(np.float64)
+    value = np.zeros((tokens, y.shape[1]))
+    sabs = np.zeros((tokens, y.shape[1]))
+    for t in range(tokens):
+        for k in range(topk):
+            r = slot_row[t * topk + k]
+            if r >= 0:
+                value[t] += w[t, k] * y[r]
+                sabs[t] += np.abs(w[t, k] * y[r])
+    return Result(value, sabs, np.ones(tokens, dtype=np.int32), np.arange(tokens))

@@ -221,3 +221,44 @@ def call_bias(name, **kw):
 def test_bias_entry_points_check_arguments(lib, name, case, status):
     rc = call_bias(name, **case)
     assert rc == status, (name, case, rc, gg.last_error())
+
+
+def test_route_sizes(lib):
+    assert gg.route_rows_bound(100, 8, 16) == 100 + 8 * 16
+    assert lib.gg_route_rows_bound(-1, 8, 1) == -1
+    assert lib.gg_route_rows_bound(10, 8, 0) == -1
+    assert lib.gg_route_workspace_bytes(4096, 16) == 2 * 16 * 4
+    assert lib.gg_route_workspace_bytes(0, 16) == 16 * 4
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(ids=0), 1), (dict(offs=0), 1), (dict(ws=0), 1), (dict(e=0), 5), (dict(align=0), 2),
+    (dict(align=5000), 2), (dict(cap=90), 2), (dict(slots=-1), 2), (dict(ws=A + 8), 3), (dict(offs=A + 2), 3),
+])
+def test_route_checks_arguments(lib, case, status):
+    v = dict(ids=A, slots=64, e=4, align=8, pad=1, offs=A + 0x100, rs=A + 0x200, cap=64 + 32, sr=A + 0x300,
+             ws=A + 0x400, s=0)
+    v.update(case)
+    rc = gg.call_raw("gg_route", v["ids"] or None, v["slots"], v["e"], v["align"], v["pad"], v["offs"] or None,
+                     v["rs"], v["cap"], v["sr"], v["ws"] or None, v["s"])
+    assert rc == status, (case, rc, gg.last_error())
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(src=0), 1), (dict(rb=24), 2), (dict(topk=0), 2), (dict(src=A + 8), 3), (dict(e=0), 5)])
+def test_gather_checks_arguments(lib, case, status):
+    v = dict(src=A, tokens=10, rb=32, rs=A + 0x100, topk=2, offs=A + 0x200, e=4, cap=40, dst=A + 0x300, s=0)
+    v.update(case)
+    rc = gg.call_raw("gg_gather_rows", v["src"] or None, v["tokens"], v["rb"], v["rs"], v["topk"], v["offs"],
+                     v["e"], v["cap"], v["dst"], v["s"])
+    assert rc == status, (case, rc, gg.last_error())
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(y=0), 1), (dict(n=12), 2), (dict(topk=0), 2), (dict(out=A + 4), 3), (dict(dt=3), 4)])
+def test_combine_checks_arguments(lib, case, status):
+    v = dict(y=A, n=64, sr=A + 0x100, w=A + 0x200, topk=2, tokens=10, cap=40, out=A + 0x300, dt=0, s=0)
+    v.update(case)
+    rc = gg.call_raw("gg_combine_rows", v["y"] or None, v["n"], v["sr"], v["w"], v["topk"], v["tokens"], v["cap"],
+                     v["out"], v["dt"], v["s"])
+    assert rc == status, (case, rc, gg.last_error())
