@@ -326,6 +326,61 @@ def main():
         del tq, aq, hq
         torch.cuda.empty_cache()
 
+        # The grouped layout's production and its consumers on a Qwen3
+        # gate/up layer (8192 tokens, top-8 of 128 experts, min_alignment_m
+        # 16 with empty experts padded): routing, the row gather, the
+        # forward on the padded layout, the weighted combine; and the
+        # forward with the grouped bias scaled per token against the plain
+        # forward.
+        w4 = synth.qwen3_gateup()
+        tokens4, topk4 = w4.m // 8, 8
+        g4 = torch.Generator(device=dev)
+        g4.manual_seed(404)
+        scores = torch.randn((tokens4, w4.num_groups), generator=g4, device=dev)
+        probs4, ids4 = torch.topk(torch.softmax(scores, -1), topk4, dim=-1)
+        ids4 = ids4.to(torch.int32).contiguous()
+        probs4 = probs4.float().contiguous()
+        x4 = torch.randn((tokens4, w4.k), generator=g4, device=dev).to(torch.bfloat16)
+        wt4 = (torch.randn((w4.num_groups, w4.k, w4.n), generator=g4, device=dev) * 0.02).to(torch.bfloat16)
+        cap4 = gg.route_rows_bound(tokens4 * topk4, w4.num_groups, 16)
+        ws4 = torch.empty(int(gg.load().gg_route_workspace_bytes(tokens4 * topk4, w4.num_groups)),
+                          dtype=torch.uint8, device=dev)
+        offs4 = torch.empty(w4.num_groups, dtype=torch.int32, device=dev)
+        rs4 = torch.empty(cap4, dtype=torch.int32, device=dev)
+        sr4 = torch.empty(tokens4 * topk4, dtype=torch.int32, device=dev)
+        xg4 = torch.empty((cap4, w4.k), dtype=torch.bfloat16, device=dev)
+        y4 = torch.empty((cap4, w4.n), dtype=torch.bfloat16, device=dev)
+        o4 = torch.empty((tokens4, w4.n), dtype=torch.bfloat16, device=dev)
+        bias4 = (torch.randn((w4.num_groups, w4.n), generator=g4, device=dev) * 0.1).to(torch.bfloat16)
+        bscale4 = torch.rand((cap4,), generator=g4, device=dev)
+        st4 = torch.cuda.current_stream(dev).cuda_stream
+
+        def route4():
+            rc = gg.call_raw("gg_route", ids4.data_ptr(), tokens4 * topk4, w4.num_groups, 16, 1,
+                             offs4.data_ptr(), rs4.data_ptr(), cap4, sr4.data_ptr(), ws4.data_ptr(), st4)
+            assert rc == 0
+        route4()
+        _, ms4 = time_passes([("route", route4),
+                              ("gather", lambda: gg.gather_rows(x4, rs4, topk4, offs4, out=xg4)),
+                              ("forward", lambda: gg.forward(xg4, wt4, offs4, out=y4)),
+                              ("forward_bias", lambda: gg.forward_bias(xg4, wt4, offs4, bias4, bscale4, out=y4)),
+                              ("combine", lambda: gg.combine_rows(y4, sr4, topk4, probs4, out=o4))],
+                             20, 3, torch)
+        f4 = {k: sorted(v)[len(v) // 2] for k, v in ms4.items()}
+        rows4 = int(offs4[-1].item())
+        context["qwen3_routed_layer"] = {
+            "tokens": tokens4, "topk": topk4, "experts": w4.num_groups, "min_alignment_m": 16,
+            "padded_rows": rows4,
+            "route_ms": round(f4["route"], 4),
+            "gather_ms": round(f4["gather"], 4),
+            "gather_GB/s": round(2 * rows4 * w4.k * 2 / (f4["gather"] * 1e-3) / 1e9, 1),
+            "forward_ms": round(f4["forward"], 4),
+            "forward_bias_scaled_ms": round(f4["forward_bias"], 4),
+            "combine_ms": round(f4["combine"], 4),
+            "combine_GB/s": round((tokens4 * topk4 * w4.n * 2 + tokens4 * w4.n * 2) / (f4["combine"] * 1e-3) / 1e9, 1)}
+        del x4, wt4, xg4, y4, o4, ws4, rs4, sr4
+        torch.cuda.empty_cache()
+
         # fp8 (e4m3) block-scaled forward: the GLM-up and Qwen3 gate/up
         # recipes in fp8, and the masked down and gate/up projections of the
         # fp8 rollout (weights rotated over 3 copies as above).  The X-scale
