@@ -594,7 +594,7 @@ __device__ __attribute__((always_inline)) inline void mainloop8(
     int wm, int wn, const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[TM][TN]) {
   constexpr int kSub = TMA / 2 * TN;                 // MFMAs per half-stage
   constexpr int kGap = kSub / 2 > 0 ? kSub / 2 : 1;
-  constexpr int kAt = kGap - 1;
+  constexpr int kAt = 0;                            // loads with MFMAs 0 and kGap (measured best)
   constexpr int kItems = TMA / 2 + TN;              // fragments read during the second half
   A.origin = a_origin;
   B.origin = b_origin;

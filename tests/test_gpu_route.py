@@ -131,5 +131,5 @@ def test_routed_layer_end_to_end():
     ref = oracle.forward(xg_ref, synth.bf16_bits(w), ro.astype(np.int32))
     yb = synth.bf16_bits(y)[:used]
     check(yb, ref.value, ref.sabs, k, "routed forward")
-    cref = oracle.combine_rows(synth.bf16_bits(y), rs, topk, probs.cpu().numpy())
+    cref = oracle.combine_rows(yb, rs, topk, probs.cpu().numpy())
     check(synth.bf16_bits(out), cref.value, cref.sabs, topk, "routed combine")
