@@ -233,6 +233,36 @@ gg_status gg_masked_wgrad_ex(const void* x, const void* dy,
                              float beta, void* stream);
 
 /*
+ * Backward of the grouped bias: with y[i, :] += s[i] * bias[g, :] over the
+ * rows i of each expert g,
+ *   gg_bias_grad        dbias[g, :] = sum_{i in g} s[i] dY[i, :]   (s = 1
+ *                       when bias_scale is NULL); an expert with no rows
+ *                       gets +0.0.  dbias fp32 [E, n], written entirely.
+ *   gg_bias_scale_grad  ds[i] = sum_n bias[g, n] dY[i, n] for the rows an
+ *                       expert owns; ds fp32 [m] (masked: [E * max_m]);
+ *                       other entries untouched.
+ * dY bf16 [m, n] (masked: [E, max_m, n]); sums in fp32 in a fixed order
+ * (deterministic).  Errors as the GEMM entry points.
+ * Cited passage: TransformerEngine PR #3542, "Validation" (the grouped
+ * GEMM's tests cover bias in forward, dgrad and wgrad) and "Summary"
+ * (grouped bias, scaled per token).
+ */
+gg_status gg_bias_grad(const void* dy, const int32_t* offs,
+                       const float* bias_scale, float* dbias, int64_t m,
+                       int64_t n, int32_t num_groups, void* stream);
+gg_status gg_masked_bias_grad(const void* dy, const int32_t* masked_m,
+                              const float* bias_scale, float* dbias,
+                              int64_t max_m, int64_t n, int32_t num_groups,
+                              void* stream);
+gg_status gg_bias_scale_grad(const void* dy, const int32_t* offs,
+                             const void* bias, float* ds, int64_t m,
+                             int64_t n, int32_t num_groups, void* stream);
+gg_status gg_masked_bias_scale_grad(const void* dy, const int32_t* masked_m,
+                                    const void* bias, float* ds,
+                                    int64_t max_m, int64_t n,
+                                    int32_t num_groups, void* stream);
+
+/*
  * [E, N, K] weight layout
  * -----------------------
  * The same passes with each expert's weight stored transposed, W[g] as

@@ -92,6 +92,10 @@ def load():
     lib.gg_gather_rows.restype = ctypes.c_int
     lib.gg_combine_rows.argtypes = [P, I64, P, P, I32, I64, I64, P, ctypes.c_int, P]
     lib.gg_combine_rows.restype = ctypes.c_int
+    for name in ("gg_bias_grad", "gg_masked_bias_grad", "gg_bias_scale_grad", "gg_masked_bias_scale_grad"):
+        f = getattr(lib, name)
+        f.argtypes = [P, P, P, P, I64, I64, I32, P]
+        f.restype = ctypes.c_int
     lib.gg_fp8_scale_bytes.argtypes = [ctypes.c_int, I64, I64, I32]
     lib.gg_fp8_scale_bytes.restype = ctypes.c_int64
     lib.gg_fp8_pack_scales.argtypes = [ctypes.c_int, P, ctypes.c_int, I64, P, I64, I64, I32, P, P, P]
@@ -524,6 +528,46 @@ def masked_forward_bias(x, w, masked_m, bias, bias_scale=None, out=None, out_dty
         raise ValueError(f"out must be [{e}, {max_m}, {n}]")
     _bias_call("gg_masked_forward_bias", x, w, masked_m, bias, bias_scale, out, max_m, k, n, e, dev,
                alpha, beta)
+    return out
+
+
+def bias_grad(dy, groups, bias_scale=None, masked=False, out=None):
+    """dbias[g] = sum_{i in g} s[i] dY[i] (gg_bias_grad / gg_masked_bias_grad):
+    dy bf16 [m, n] or [E, max_m, n]; returns fp32 [E, n]."""
+    torch = _torch()
+    dev = dy.device
+    _check(dy, "dy", torch.bfloat16, 3 if masked else 2, dev)
+    _check(groups, "groups", torch.int32, 1, dev)
+    e = groups.shape[0]
+    rows, n = (dy.shape[1], dy.shape[2]) if masked else (dy.shape[0], dy.shape[1])
+    if out is None:
+        out = torch.empty((e, n), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.float32, 2, dev)
+    name = "gg_masked_bias_grad" if masked else "gg_bias_grad"
+    _raise(name, call_raw(name, dy.data_ptr(), groups.data_ptr(),
+                          None if bias_scale is None else bias_scale.data_ptr(), out.data_ptr(), int(rows),
+                          int(n), int(e), _stream_handle(dev)))
+    return out
+
+
+def bias_scale_grad(dy, groups, bias, masked=False, out=None):
+    """ds[i] = <bias[g], dY[i]> on the rows an expert owns
+    (gg_bias_scale_grad / gg_masked_bias_scale_grad); returns fp32 [rows]
+    (other entries as ``out`` held them; NaN when allocated here)."""
+    torch = _torch()
+    dev = dy.device
+    _check(dy, "dy", torch.bfloat16, 3 if masked else 2, dev)
+    _check(groups, "groups", torch.int32, 1, dev)
+    _check(bias, "bias", torch.bfloat16, 2, dev)
+    e = groups.shape[0]
+    rows, n = (dy.shape[1], dy.shape[2]) if masked else (dy.shape[0], dy.shape[1])
+    total = e * rows if masked else rows
+    if out is None:
+        out = torch.full((total,), float("nan"), dtype=torch.float32, device=dev)
+    _check(out, "out", torch.float32, 1, dev)
+    name = "gg_masked_bias_scale_grad" if masked else "gg_bias_scale_grad"
+    _raise(name, call_raw(name, dy.data_ptr(), groups.data_ptr(), bias.data_ptr(), out.data_ptr(), int(rows),
+                          int(n), int(e), _stream_handle(dev)))
     return out
 
 

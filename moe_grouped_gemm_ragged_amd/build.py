@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgg.so")
-SOURCES = ["gg_kernels.hip", "gg_fp8_scales.hip", "gg_route.hip", "gg_api.hip"]
+SOURCES = ["gg_kernels.hip", "gg_fp8_scales.hip", "gg_route.hip", "gg_bias_grad.hip", "gg_api.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -389,6 +389,60 @@ gg_status gg_combine_rows(const void* y, int64_t n, const int32_t* slot_row, con
                                             out_dtype == GG_F32, cus, static_cast<hipStream_t>(stream)));
 }
 
+static gg_status bias_grad_check(const void* dy, const int32_t* groups, const void* out, int64_t rows, int64_t n,
+                                 int32_t E, bool masked) {
+  if (!dy || !groups || !out) return fail(GG_ERR_NULL_PTR, "a required pointer is NULL");
+  if (E < 1 || E > GG_MAX_GROUPS) return fail(GG_ERR_LIMIT, "num_groups must be in [1, GG_MAX_GROUPS]");
+  if (rows < 0 || n < 8 || n % 8 != 0 || n > GG_MAX_KN)
+    return fail(GG_ERR_BAD_DIM, "need rows >= 0 and n a positive multiple of 8 up to GG_MAX_KN");
+  const double total = masked ? (double)rows * E : (double)rows;
+  if (total > 2147483647.0) return fail(GG_ERR_BAD_DIM, "row count exceeds 2^31 - 1");
+  if (!aligned16(dy) || !aligned4(groups) || !aligned4(out))
+    return fail(GG_ERR_ALIGNMENT, "dy must be 16-byte aligned");
+  return GG_OK;
+}
+
+gg_status gg_bias_grad(const void* dy, const int32_t* offs, const float* bias_scale, float* dbias, int64_t m,
+                       int64_t n, int32_t num_groups, void* stream) {
+  gg_status s = bias_grad_check(dy, offs, dbias, m, n, num_groups, false);
+  if (s != GG_OK) return s;
+  if (!aligned4(bias_scale)) return fail(GG_ERR_ALIGNMENT, "bias_scale must be 4-byte aligned");
+  return hip_result(gg::launch_dbias(false, dy, offs, bias_scale, m, n, num_groups, dbias,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+gg_status gg_masked_bias_grad(const void* dy, const int32_t* masked_m, const float* bias_scale, float* dbias,
+                              int64_t max_m, int64_t n, int32_t num_groups, void* stream) {
+  gg_status s = bias_grad_check(dy, masked_m, dbias, max_m, n, num_groups, true);
+  if (s != GG_OK) return s;
+  if (!aligned4(bias_scale)) return fail(GG_ERR_ALIGNMENT, "bias_scale must be 4-byte aligned");
+  return hip_result(gg::launch_dbias(true, dy, masked_m, bias_scale, max_m, n, num_groups, dbias,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+static gg_status dscale_run(bool masked, const void* dy, const int32_t* groups, const void* bias, float* ds,
+                            int64_t rows, int64_t n, int32_t E, void* stream) {
+  gg_status s = bias_grad_check(dy, groups, ds, rows, n, E, masked);
+  if (s != GG_OK) return s;
+  if (!bias) return fail(GG_ERR_NULL_PTR, "bias is NULL");
+  if (!aligned16(bias)) return fail(GG_ERR_ALIGNMENT, "bias must be 16-byte aligned");
+  int cus = 0;
+  s = device_cus(&cus);
+  if (s != GG_OK) return s;
+  return hip_result(gg::launch_dscale(masked, dy, groups, bias, rows, n, E, ds, cus,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+gg_status gg_bias_scale_grad(const void* dy, const int32_t* offs, const void* bias, float* ds, int64_t m,
+                             int64_t n, int32_t num_groups, void* stream) {
+  return dscale_run(false, dy, offs, bias, ds, m, n, num_groups, stream);
+}
+
+gg_status gg_masked_bias_scale_grad(const void* dy, const int32_t* masked_m, const void* bias, float* ds,
+                                    int64_t max_m, int64_t n, int32_t num_groups, void* stream) {
+  return dscale_run(true, dy, masked_m, bias, ds, max_m, n, num_groups, stream);
+}
+
 int64_t gg_fp8_scale_bytes(gg_fp8_scale_layout layout, int64_t rows, int64_t k, int32_t num_groups) {
   if (layout < GG_FP8_ACT_RAGGED || layout > GG_FP8_WEIGHT) return -1;
   if (rows < 0 || k < 128 || k % 128 != 0 || k > GG_MAX_KN) return -1;

@@ -56,4 +56,11 @@ hipError_t launch_gather_rows(const void* src, int64_t row_bytes, const int32_t*
 hipError_t launch_combine_rows(const void* y, int64_t n, const int32_t* slot_row, const float* w, int32_t topk,
                                int64_t tokens, int64_t rows_cap, void* out, bool out_f32, int num_cus,
                                hipStream_t stream);
+
+// Backward of the grouped bias (gg_bias_grad.hip): dbias fp32 [E, n] and
+// the per-row factor's gradient ds fp32 [rows], both from bf16 dY.
+hipError_t launch_dbias(bool masked, const void* dy, const int32_t* groups, const float* scale, int64_t m,
+                        int64_t n, int32_t E, float* dbias, hipStream_t stream);
+hipError_t launch_dscale(bool masked, const void* dy, const int32_t* groups, const void* bias, int64_t m,
+                         int64_t n, int32_t E, float* ds, int num_cus, hipStream_t stream);
 }  // namespace gg

@@ -586,3 +586,53 @@ def combine_rows(y_bits, slot_row, topk, weights=None) -> Result:
                 value[t] += w[t, k] * y[r]
                 sabs[t] += np.abs(w[t, k] * y[r])
     return Result(value, sabs, np.ones(tokens, dtype=np.int32), np.arange(tokens))
+
+
+
+def bias_grad(dy_bits, groups, bias_scale=None, masked=False) -> Result:
+    """dbias[g, :] = sum_{i in g} s[i] dY[i, :] in fp64 (+0.0 for an empty
+    expert); the backward of forward_bias's bias term.  Rows of the result
+    are experts."""
+    dy = decode_bf16(np.asarray(dy_bits, dtype=np.uint16))
+    e = len(groups)
+    if masked:
+        max_m = dy.shape[1]
+        dy = dy.reshape(-1, dy.shape[-1])
+        spans = [(g * max_m, g * max_m + min(max(int(groups[g]), 0), max_m)) for g in range(e)]
+    else:
+        ends = _clamped_ends(groups, dy.shape[0])
+        spans = [(0 if g == 0 else int(ends[g - 1]), int(ends[g])) for g in range(e)]
+    s = None if bias_scale is None else np.asarray(bias_scale, dtype=np.float32).astype(np.float64).reshape(-1)
+    value = np.zeros((e, dy.shape[1]))
+    sabs = np.zeros((e, dy.shape[1]))
+    for g, (a, b) in enumerate(spans):
+        w = np.ones(b - a) if s is None else s[a:b]
+        value[g] = (w[:, None] * dy[a:b]).sum(axis=0)
+        sabs[g] = np.abs(w[:, None] * dy[a:b]).sum(axis=0)
+    return Result(value, sabs, np.ones(e, dtype=np.int32), np.arange(e))
+
+
+def bias_scale_grad(dy_bits, groups, bias_bits, masked=False) -> Result:
+    """ds[i] = sum_n bias[g, n] dY[i, n] in fp64 for the rows an expert owns
+    (status 1), rows of the result = flat rows."""
+    dy = decode_bf16(np.asarray(dy_bits, dtype=np.uint16))
+    b = decode_bf16(np.asarray(bias_bits, dtype=np.uint16))
+    e = len(groups)
+    if masked:
+        max_m = dy.shape[1]
+        dy = dy.reshape(-1, dy.shape[-1])
+        owner = np.full(dy.shape[0], -1)
+        for g in range(e):
+            a = min(max(int(groups[g]), 0), max_m)
+            owner[g * max_m: g * max_m + a] = g
+    else:
+        ends = _clamped_ends(groups, dy.shape[0])
+        owner = np.full(dy.shape[0], -1)
+        for g in range(e):
+            owner[(0 if g == 0 else int(ends[g - 1])): int(ends[g])] = g
+    ok = owner >= 0
+    value = np.full((dy.shape[0], 1), np.nan)
+    sabs = np.full((dy.shape[0], 1), np.nan)
+    value[ok, 0] = (dy[ok] * b[owner[ok]]).sum(axis=1)
+    sabs[ok, 0] = np.abs(dy[ok] * b[owner[ok]]).sum(axis=1)
+    return Result(value, sabs, ok.astype(np.int32), np.arange(dy.shape[0]))

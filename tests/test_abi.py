@@ -262,3 +262,15 @@ def test_combine_checks_arguments(lib, case, status):
     rc = gg.call_raw("gg_combine_rows", v["y"] or None, v["n"], v["sr"], v["w"], v["topk"], v["tokens"], v["cap"],
                      v["out"], v["dt"], v["s"])
     assert rc == status, (case, rc, gg.last_error())
+
+
+@pytest.mark.parametrize("name", ["gg_bias_grad", "gg_masked_bias_grad", "gg_bias_scale_grad",
+                                  "gg_masked_bias_scale_grad"])
+@pytest.mark.parametrize("case,status", [
+    (dict(dy=0), 1), (dict(g=0), 1), (dict(o=0), 1), (dict(n=12), 2), (dict(m=-1), 2), (dict(dy=A + 8), 3),
+    (dict(e=0), 5)])
+def test_bias_grad_entry_points_check_arguments(lib, name, case, status):
+    v = dict(dy=A, g=A + 0x100, x=A + 0x200, o=A + 0x300, m=64, n=64, e=4, s=0)
+    v.update(case)
+    rc = gg.call_raw(name, v["dy"] or None, v["g"] or None, v["x"], v["o"] or None, v["m"], v["n"], v["e"], v["s"])
+    assert rc == status, (name, case, rc, gg.last_error())

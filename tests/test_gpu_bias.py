@@ -111,3 +111,52 @@ def test_zero_bias_equals_plain_forward():
     torch.cuda.synchronize()
     used = int(wl.offs[-1])
     assert np.array_equal(host(y1)[:used], host(y2)[:used])
+
+
+@pytest.mark.parametrize("with_scale", [True, False])
+def test_bias_grad_ragged_with_capacity(with_scale):
+    dev = device()
+    import torch
+    base = synth.by_name("dsv3_small")
+    wl = synth.custom_ragged("dbias", base.group_sizes(), base.k, base.n, seed=3, m=int(base.offs[-1]) + 29)
+    t = synth.make_inputs(wl, dev, need=("dy",))
+    logical = int(wl.offs[-1])
+    scale = torch.rand((logical,), device=dev) if with_scale else None
+    say("bias_grad", with_scale)
+    db = gg.bias_grad(t["dy"], t["offs"], scale)
+    torch.cuda.synchronize()
+    ref = oracle.bias_grad(synth.bf16_bits(t["dy"]), wl.offs, None if scale is None else scale.cpu().numpy())
+    L = int(max(1, wl.group_sizes().max()))
+    check(db.cpu().numpy(), ref.value, ref.sabs, L, "bias_grad")
+    empty = np.flatnonzero(wl.group_sizes() == 0)
+    assert np.all(db.cpu().numpy()[empty] == 0.0)
+
+
+def test_bias_scale_grad_ragged_and_masked():
+    dev = device()
+    import torch
+    wl = synth.by_name("qwen3_gateup_small")
+    t = synth.make_inputs(wl, dev, need=("dy",))
+    bias = (torch.randn((wl.num_groups, wl.n), device=dev) * 0.5).to(torch.bfloat16)
+    say("bias_scale_grad ragged")
+    ds = gg.bias_scale_grad(t["dy"], t["offs"], bias)
+    torch.cuda.synchronize()
+    ref = oracle.bias_scale_grad(synth.bf16_bits(t["dy"]), wl.offs, synth.bf16_bits(bias))
+    ok = ref.status == 1
+    dh = ds.cpu().numpy()
+    check(dh[ok][:, None], ref.value[ok], ref.sabs[ok], wl.n, "bias_scale_grad")
+    assert np.all(np.isnan(dh[~ok])), "rows no expert owns were written"
+    wm = synth.by_name("masked_down_small")
+    tm = synth.make_inputs(wm, dev, need=("dy",))
+    bm = (torch.randn((wm.num_groups, wm.n), device=dev) * 0.5).to(torch.bfloat16)
+    say("bias grads masked")
+    dsm = gg.bias_scale_grad(tm["dy"], tm["masked_m"], bm, masked=True)
+    dbm = gg.bias_grad(tm["dy"], tm["masked_m"], None, masked=True)
+    torch.cuda.synchronize()
+    rm = oracle.bias_scale_grad(synth.bf16_bits(tm["dy"]), wm.masked_m, synth.bf16_bits(bm), masked=True)
+    okm = rm.status == 1
+    dmh = dsm.cpu().numpy()
+    check(dmh[okm][:, None], rm.value[okm], rm.sabs[okm], wm.n, "masked bias_scale_grad")
+    assert np.all(np.isnan(dmh[~okm]))
+    rb = oracle.bias_grad(synth.bf16_bits(tm["dy"]), wm.masked_m, None, masked=True)
+    check(dbm.cpu().numpy(), rb.value, rb.sabs, wm.m, "masked bias_grad")
