@@ -218,3 +218,35 @@ def test_fp8_forward_full_size_sampled(name, count):
     rep = Report()
     check_fp8(yh, ref.value, ref.sabs, wl.k, f"fp8 {name} sampled", rep)
     print(name, len(rows), "rows", rep)
+
+
+@pytest.mark.parametrize("mm,max_m,k,n", [
+    ([0, 300, 257, 1], 300, 128, 8),          # max_m not a multiple of 256: two row tiles per expert
+    ([5, 0, 0, 129], 130, 256, 24),
+])
+def test_fp8_masked_edges(mm, max_m, k, n):
+    dev = device()
+    wl = synth.custom_masked("fp8_masked_edges", mm, max_m, k, n, seed=51 + k)
+    t = synth.make_fp8_inputs(wl, dev)
+    y = sentinel_tensor((wl.num_groups, wl.m, wl.n), _dt("bf16"), dev)
+    say("fp8 masked edges", mm, max_m, k, n)
+    run_fp8(wl, t, y)
+    check_all_rows(wl, t, y, f"fp8 masked edges {mm} {max_m}")
+
+
+def test_fp8_invalid_offsets_are_clamped():
+    """Decreasing and oversize end offsets: the pack step and the GEMM clamp
+    them the same way (end(g) = min(max(offs[0..g]), M)), so the result is
+    the oracle's on the clamped grouping and no row past M is touched."""
+    dev = device()
+    import torch
+    sizes = [40, 300, 9, 200]
+    wl = synth.custom_ragged("fp8_bad_offs", sizes, 256, 136, seed=61, m=560)
+    t = synth.make_fp8_inputs(wl, dev)
+    bad = np.array([40, 20, 349, 10 ** 6], dtype=np.int32)      # decreasing, then past M
+    t["offs"] = torch.from_numpy(bad).to(dev)
+    wl.offs = bad
+    y = sentinel_tensor((wl.m, wl.n), _dt("f32"), dev)
+    say("fp8 invalid offsets")
+    run_fp8(wl, t, y)
+    check_all_rows(wl, t, y, "fp8 clamped offsets")
