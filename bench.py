@@ -45,8 +45,8 @@ KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_ragged_amd", "csrc", "gg_kerne
 # Valid only for the kernel source they were taken on (sha256 below); for any
 # other source the roofline reports traffic as null.
 MEASURED_TRAFFIC = {
-    "kernel_sha256": "a77f2aa3c1efb2c777ea4886e7b7db296d9ddd1d51836c2fc3b2e2b880d6b3df",
-    "bytes": {"fwd": 24341179580, "dgrad": 28055306697, "wgrad": 36988943343},
+    "kernel_sha256": "7638961c02aaad670823617c08022dad311124eefddc793f903817cb79f31a7e",
+    "bytes": {"fwd": 23639475460, "dgrad": 25985065176, "wgrad": 32671123730},
 }
 
 
