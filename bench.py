@@ -28,6 +28,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -45,14 +46,20 @@ KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_ragged_amd", "csrc", "gg_kerne
 # Valid only for the kernel source they were taken on (sha256 below); for any
 # other source the roofline reports traffic as null.
 MEASURED_TRAFFIC = {
-    "kernel_sha256": "7638961c02aaad670823617c08022dad311124eefddc793f903817cb79f31a7e",
+    "kernel_sha256": "d840fab8dcce00ceb7d28e6f8b174593b03e399b33d091112e935b44f15c46da",
     "bytes": {"fwd": 23639475460, "dgrad": 25985065176, "wgrad": 32671123730},
 }
 
 
 def kernel_sha256():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """sha256 of the kernel source's code: comments and blank lines removed,
+    so that a comment edit does not invalidate counter measurements."""
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    src = re.sub(r"//[^\n]*", "", src)
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    code = "\n".join(line.strip() for line in src.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()
 
 
 def log(*a):

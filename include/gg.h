@@ -1,6 +1,10 @@
 /*
- * gg.h -- C ABI of the bf16 grouped (ragged, per-expert) GEMM for MI355X
- * (gfx950).
+ * gg.h -- C ABI of the grouped (ragged, per-expert) GEMM for MI355X
+ * (gfx950): the bf16 passes below, then their scaled and accumulating
+ * forms, the masked backward, the SiLU-mul gate/up forward, the grouped
+ * bias and its backward, the [E, N, K] weight layout, the steps that
+ * produce the grouped layout (offsets, routing, gather, combine), and the
+ * fp8 block-scaled forward.
  *
  * The operation (PyTorch issue #152668, "Easy repro scenario", and its
  * backward): a 2-D activation X[M,K], a packed 3-D weight W[E,K,N] and int32

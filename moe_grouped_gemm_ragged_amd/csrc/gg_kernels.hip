@@ -1,9 +1,8 @@
-// gg_kernels.hip -- persistent bf16 grouped-GEMM kernels for gfx950 (CDNA4).
+// gg_kernels.hip -- persistent grouped-GEMM kernels for gfx950 (CDNA4).
 //
-// One kernel template serves the four passes of the grouped GEMM (forward,
-// dgrad, wgrad and the masked forward; include/gg.h states the operations
-// and the passages that define them).  Each pass is the same tile engine fed
-// by a different operand description:
+// One kernel template serves every pass of the grouped GEMM (include/gg.h
+// states the operations and the passages that define them).  Each pass is
+// the same tile engine fed by a different operand description:
 //
 //   pass           out tile rows x cols   reduction    A operand          B operand
 //   forward        expert rows x n        k            X    (red-contig)  W[g] (red-strided)
@@ -12,6 +11,14 @@
 //   masked fwd     active rows x n        k            X[e] (red-contig)  W[e] (red-strided)
 //   masked dgrad   active rows x k        n            dY[e](red-contig)  W[e] (red-contig)
 //   masked wgrad   k x n                  active rows  X[e] (red-strided) dY[e](red-strided)
+//   SiLU fwd       as forward, 128 activation columns from a gate/up panel
+//   fp8 fwd        expert rows x n        k            X e4m3 (contig)    W[g] [n, k] e4m3 (contig)
+//
+// (The [E, N, K] weight layout of the bf16 passes is these modes with the
+// dimensions exchanged; the host entry points do the mapping.)  Epilogues:
+// fp32 straight from the accumulators, or through LDS for bf16, for
+// alpha * P + beta * C, for the grouped bias s[i] * bias[g], and for the
+// SiLU-mul activation.
 //
 // "red-contig" means the reduction index is the contiguous one in memory;
 // "red-strided" means the tile's row index is.
