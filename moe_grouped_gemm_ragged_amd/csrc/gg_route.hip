@@ -32,7 +32,7 @@ typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 constexpr int kRouteThreads = 512;
-constexpr int kChunk = 2048;          // slots per block in the route passes
+constexpr int kChunk = 1024;          // slots per block in the route passes
 constexpr int kPerThread = kChunk / kRouteThreads;
 
 __device__ __forceinline__ int64_t pad_count(int64_t c, int align, bool pad_empty) {
@@ -111,16 +111,20 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* hist, int32_t
   int64_t local = 0;
   for (int g = g0; g < g1; ++g) {
     int64_t c = 0;
-    for (int b = 0; b < nblocks; ++b) c += hist[(int64_t)g * nblocks + b];
+    const int32_t* hg = hist + (int64_t)g * nblocks;
+#pragma unroll 8
+    for (int b = 0; b < nblocks; ++b) c += hg[b];
     local += pad_count(c, align, pad_empty != 0);
   }
   block_exclusive_scan(local, s, tid, 1024);
   int64_t start = local;
   for (int g = g0; g < g1; ++g) {
     int64_t run = start;
+    int32_t* hg = hist + (int64_t)g * nblocks;
+#pragma unroll 8
     for (int b = 0; b < nblocks; ++b) {
-      const int32_t c = hist[(int64_t)g * nblocks + b];
-      hist[(int64_t)g * nblocks + b] = (int32_t)run;
+      const int32_t c = hg[b];
+      hg[b] = (int32_t)run;
       run += c;
     }
     const int64_t end = start + pad_count(run - start, align, pad_empty != 0);
@@ -142,6 +146,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_place_kernel(const int32_
   const int tid = threadIdx.x;
   const int64_t base = (int64_t)blockIdx.x * kChunk;
   // key = expert (E for dropped or past the end) << 11 | local slot index
+  static_assert(kChunk <= 2048, "the slot index takes 11 bits of the key");
   for (int j = 0; j < kPerThread; ++j) {
     const int i = j * kRouteThreads + tid;
     const int64_t s = base + i;

@@ -227,7 +227,7 @@ def test_route_sizes(lib):
     assert gg.route_rows_bound(100, 8, 16) == 100 + 8 * 16
     assert lib.gg_route_rows_bound(-1, 8, 1) == -1
     assert lib.gg_route_rows_bound(10, 8, 0) == -1
-    assert lib.gg_route_workspace_bytes(4096, 16) == 2 * 16 * 4
+    assert lib.gg_route_workspace_bytes(4096, 16) == 4 * 16 * 4       # 1024 slots per block
     assert lib.gg_route_workspace_bytes(0, 16) == 16 * 4
 
 
