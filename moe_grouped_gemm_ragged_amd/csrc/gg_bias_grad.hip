@@ -7,6 +7,8 @@
 // Both are reductions over bf16 dY in fp32, HBM-bound, in a fixed order per
 // element (deterministic; no atomics).  Groups as everywhere: clamped end
 // offsets (ragged) or masked_m (masked, rows e * max_m + r, r < masked_m[e]).
+// An expert's row range and the per-row expert lookup come from cooperative
+// maxima and scans over the offsets, never a serial walk.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -18,8 +20,14 @@ namespace {
 typedef uint32_t u32x4b __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
-constexpr int kRowLanes = 4;                       // threads along the rows of one column group
-constexpr int kColsPerBlock = 8 * (kThreads / kRowLanes);   // 512 columns per workgroup
+constexpr int kWaves = kThreads / 64;
+// dbias: a workgroup owns 128 columns of one expert -- 16 column groups of 8
+// (a row's 256 bytes per 16 lanes) by 16 row lanes, each with 4 rows in
+// flight.
+constexpr int kDbCols = 128;
+constexpr int kDbGroups = kDbCols / 8;
+constexpr int kDbLanes = kThreads / kDbGroups;
+constexpr int kDbUnroll = 4;
 
 __device__ __forceinline__ void unpack8(const u32x4b q, float (&v)[8]) {
 #pragma unroll
@@ -29,65 +37,112 @@ __device__ __forceinline__ void unpack8(const u32x4b q, float (&v)[8]) {
   }
 }
 
-// Rows [start, end) of expert g in the flat row index space.
+__device__ __forceinline__ int imax(int a, int b) { return a > b ? a : b; }
+
+// Rows [start, end) of expert g in the flat row index space, computed by
+// the whole workgroup.  Ragged: end(g) = min(max(0, offs[0..g]), m) and
+// start = end(g - 1) (0 for g = 0) -- two maxima over the offsets, strided
+// over the threads, then reduced across lanes and waves.  red: kWaves * 2
+// ints of LDS.
 template <bool MASKED>
-__device__ __forceinline__ void group_rows(const int32_t* groups, int g, int64_t m, int64_t& start,
-                                           int64_t& end) {
+__device__ __forceinline__ void group_rows(const int32_t* groups, int g, int64_t m, int tid, int32_t* red,
+                                           int64_t& start, int64_t& end) {
   if constexpr (MASKED) {
     int64_t a = groups[g];
     a = a < 0 ? 0 : (a > m ? m : a);
     start = (int64_t)g * m;
     end = start + a;
   } else {
-    // end(g) = min(max(offs[0..g]), m); start = end(g - 1)
-    int64_t run = 0, prev = 0;
-    for (int h = 0; h <= g; ++h) {
-      prev = run;
-      const int64_t o = groups[h];
-      run = o > run ? o : run;
-      run = run < m ? run : m;
+    int upto = 0, before = 0;          // max over offs[0..g] and offs[0..g-1], floored at 0
+    for (int h = tid; h <= g; h += kThreads) {
+      const int o = groups[h];
+      upto = imax(upto, o);
+      if (h < g) before = imax(before, o);
     }
-    start = prev;
-    end = run;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      upto = imax(upto, __shfl_xor(upto, off, 64));
+      before = imax(before, __shfl_xor(before, off, 64));
+    }
+    if ((tid & 63) == 0) {
+      red[2 * (tid >> 6)] = upto;
+      red[2 * (tid >> 6) + 1] = before;
+    }
+    __syncthreads();
+    upto = 0;
+    before = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      upto = imax(upto, red[2 * w]);
+      before = imax(before, red[2 * w + 1]);
+    }
+    end = upto < m ? upto : m;
+    start = before < m ? before : m;
   }
 }
 
-// One workgroup per (expert, 512-column block): thread (c, l) sums columns
-// 8 c .. 8 c + 7 over rows start + l, start + l + 4, ...; the 4 partial sums
-// of a column are added in LDS in order l = 0..3.
+// One workgroup per (expert, 128-column block).  Thread (c, l) = (tid mod
+// 16, tid / 16) sums columns 8 c .. 8 c + 7 over rows start + l + 16 j:
+// rows 64 q + 16 u + l go to partial sum u (u = 0..3, loads of four rows in
+// flight), the rows past the last whole group of 64 to partial sum 0.  The
+// thread adds its four partials in order u = 0..3, and the 16 row lanes of
+// a column are added in LDS in order l = 0..15: a fixed order per element.
 template <bool MASKED>
 __global__ __launch_bounds__(kThreads) void dbias_kernel(const uint16_t* dy, const int32_t* groups,
                                                          const float* scale, int64_t m, int64_t n,
                                                          int32_t E, float* dbias) {
-  __shared__ float part[kRowLanes][kColsPerBlock];
-  const int col_blocks = (int)((n + kColsPerBlock - 1) / kColsPerBlock);
+  __shared__ float part[kDbLanes][kDbCols];
+  __shared__ int32_t red[2 * kWaves];
+  const int col_blocks = (int)((n + kDbCols - 1) / kDbCols);
   const int g = blockIdx.x / col_blocks;
   const int cb = blockIdx.x - g * col_blocks;
   const int tid = threadIdx.x;
-  const int l = tid % kRowLanes;
-  const int c = tid / kRowLanes;
-  const int64_t col = (int64_t)cb * kColsPerBlock + 8 * c;
+  const int c = tid % kDbGroups;
+  const int l = tid / kDbGroups;
+  const int64_t col = (int64_t)cb * kDbCols + 8 * c;
   int64_t start, end;
-  group_rows<MASKED>(groups, g, m, start, end);
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  group_rows<MASKED>(groups, g, m, tid, red, start, end);
+  float acc[kDbUnroll][8];
+#pragma unroll
+  for (int u = 0; u < kDbUnroll; ++u)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[u][e] = 0.f;
   if (col < n) {
-    for (int64_t i = start + l; i < end; i += kRowLanes) {
+    int64_t i = start + l;
+    for (; i + (kDbUnroll - 1) * kDbLanes < end; i += kDbUnroll * kDbLanes) {
+      u32x4b q[kDbUnroll];
+      float s[kDbUnroll];
+#pragma unroll
+      for (int u = 0; u < kDbUnroll; ++u) {
+        const int64_t r = i + u * kDbLanes;
+        q[u] = *reinterpret_cast<const u32x4b*>(dy + r * n + col);
+        s[u] = scale ? scale[r] : 1.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kDbUnroll; ++u) {
+        float v[8];
+        unpack8(q[u], v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[u][e] += s[u] * v[e];
+      }
+    }
+    for (; i < end; i += kDbLanes) {
       const float s = scale ? scale[i] : 1.0f;
       float v[8];
       unpack8(*reinterpret_cast<const u32x4b*>(dy + i * n + col), v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += s * v[e];
+      for (int e = 0; e < 8; ++e) acc[0][e] += s * v[e];
     }
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) part[l][8 * c + e] = acc[e];
+  for (int e = 0; e < 8; ++e) part[l][8 * c + e] = ((acc[0][e] + acc[1][e]) + acc[2][e]) + acc[3][e];
   __syncthreads();
-  for (int j = tid; j < kColsPerBlock; j += kThreads) {
-    const int64_t cc = (int64_t)cb * kColsPerBlock + j;
+  for (int j = tid; j < kDbCols; j += kThreads) {
+    const int64_t cc = (int64_t)cb * kDbCols + j;
     if (cc < n) {
       float t = part[0][j];
 #pragma unroll
-      for (int q = 1; q < kRowLanes; ++q) t += part[q][j];
+      for (int q = 1; q < kDbLanes; ++q) t += part[q][j];
       dbias[(int64_t)g * n + cc] = t;
     }
   }
@@ -100,17 +155,38 @@ __global__ __launch_bounds__(kThreads) void dscale_kernel(const uint16_t* dy, co
                                                           const uint16_t* bias, int64_t m, int64_t n,
                                                           int32_t E, int64_t rows, float* ds) {
   __shared__ int32_t s_end[GG_MAX_GROUPS_DEV];
+  __shared__ int32_t wave_max[kWaves];
   const int tid = threadIdx.x;
-  // expert ends, so each row finds its expert by binary search
+  // expert ends end(h) = min(max(0, offs[0..h]), m), so each row finds its
+  // expert by binary search: thread t takes a run of consecutive experts,
+  // writes its local prefix maxima, and raises them by the maximum of the
+  // runs before its own (a shuffle scan within the wave, then the totals of
+  // the earlier waves).
   if constexpr (!MASKED) {
-    if (tid == 0) {
-      int64_t run = 0;
-      for (int h = 0; h < E; ++h) {
-        const int64_t o = groups[h];
-        run = o > run ? o : run;
-        run = run < m ? run : m;
-        s_end[h] = (int32_t)run;
-      }
+    const int per = (E + kThreads - 1) / kThreads;
+    const int h0 = tid * per;
+    const int h1 = h0 + per < E ? h0 + per : E;
+    int run = 0;
+    for (int h = h0; h < h1; ++h) {
+      run = imax(run, groups[h]);
+      s_end[h] = run;
+    }
+    const int lane = tid & 63, w = tid >> 6;
+    int incl = run;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, (unsigned)d, 64);
+      if (lane >= d) incl = imax(incl, o);
+    }
+    int before = __shfl_up(incl, 1u, 64);
+    if (lane == 0) before = 0;
+    if (lane == 63) wave_max[w] = incl;
+    __syncthreads();
+    for (int q = 0; q < w; ++q) before = imax(before, wave_max[q]);
+    const int mcap = m < 2147483647 ? (int)m : 2147483647;
+    for (int h = h0; h < h1; ++h) {
+      const int e = imax(s_end[h], before);
+      s_end[h] = e < mcap ? e : mcap;
     }
     __syncthreads();
   }
@@ -152,7 +228,7 @@ __global__ __launch_bounds__(kThreads) void dscale_kernel(const uint16_t* dy, co
 
 hipError_t launch_dbias(bool masked, const void* dy, const int32_t* groups, const float* scale, int64_t m,
                         int64_t n, int32_t E, float* dbias, hipStream_t stream) {
-  const int col_blocks = (int)((n + kColsPerBlock - 1) / kColsPerBlock);
+  const int col_blocks = (int)((n + kDbCols - 1) / kDbCols);
   const dim3 grid((unsigned)(E * col_blocks));
   if (masked)
     hipLaunchKernelGGL(dbias_kernel<true>, grid, dim3(kThreads), 0, stream, static_cast<const uint16_t*>(dy),

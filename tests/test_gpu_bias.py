@@ -160,3 +160,101 @@ def test_bias_scale_grad_ragged_and_masked():
     assert np.all(np.isnan(dmh[~okm]))
     rb = oracle.bias_grad(synth.bf16_bits(tm["dy"]), wm.masked_m, None, masked=True)
     check(dbm.cpu().numpy(), rb.value, rb.sabs, wm.m, "masked bias_grad")
+
+
+def test_bias_grads_clamped_offsets_many_experts_partial_columns():
+    """600 experts (more offsets than a workgroup has threads), N = 200 (a
+    partial 128-column block), empty experts, and offsets that decrease, go
+    negative or pass M (clamped as everywhere).  Both reductions must match
+    the oracle, repeat bit for bit, give +0.0 for every empty expert and
+    leave rows no expert owns untouched."""
+    import torch
+    dev = device()
+    rng = np.random.default_rng(11)
+    e, n = 600, 200
+    sizes = rng.integers(0, 12, size=e)
+    sizes[::7] = 0
+    m = int(sizes.sum()) + 13
+    wl = synth.custom_ragged("dbias_many", sizes, 8, n, seed=5, m=m)
+    t = synth.make_inputs(wl, dev, need=("dy",))
+    offs_h = wl.offs.astype(np.int32).copy()
+    offs_h[5] = offs_h[4] - 3          # decreasing: expert 5 is empty
+    offs_h[9] = -4                     # negative: expert 9 is empty
+    offs_h[e - 2] = m + 50             # past M: expert e-2 runs to M, expert e-1 is empty
+    offs = torch.tensor(offs_h, dtype=torch.int32, device=dev)
+    scale = torch.rand((m,), device=dev)
+    bias = (torch.randn((e, n), device=dev) * 0.5).to(torch.bfloat16)
+    say("bias grads, 600 experts, clamped offsets, n 200")
+    db1 = gg.bias_grad(t["dy"], offs, scale)
+    db2 = gg.bias_grad(t["dy"], offs, scale)
+    ds1 = gg.bias_scale_grad(t["dy"], offs, bias)
+    ds2 = gg.bias_scale_grad(t["dy"], offs, bias)
+    torch.cuda.synchronize()
+    assert torch.equal(db1.view(torch.int32), db2.view(torch.int32)), "dbias not repeatable"
+    assert torch.equal(ds1.view(torch.int32), ds2.view(torch.int32)), "dscale not repeatable"
+    dy_bits = synth.bf16_bits(t["dy"])
+    ref = oracle.bias_grad(dy_bits, offs_h, scale.cpu().numpy())
+    ends = np.minimum(np.maximum.accumulate(np.maximum(offs_h.astype(np.int64), 0)), m)
+    rows = np.diff(np.concatenate([[0], ends]))
+    check(db1.cpu().numpy(), ref.value, ref.sabs, int(max(1, rows.max())), "bias_grad clamped")
+    assert np.all(db1.cpu().numpy()[rows == 0] == 0.0) and not np.any(np.signbit(db1.cpu().numpy()[rows == 0]))
+    rs = oracle.bias_scale_grad(dy_bits, offs_h, synth.bf16_bits(bias))
+    ok = rs.status == 1
+    dh = ds1.cpu().numpy()
+    check(dh[ok][:, None], rs.value[ok], rs.sabs[ok], n, "bias_scale_grad clamped")
+    assert np.all(np.isnan(dh[~ok])), "rows no expert owns were written"
+
+
+def test_masked_bias_grads_out_of_range_counts_partial_columns():
+    """Masked layout with counts below 0 and above max_m (clamped) and
+    N = 136: dbias over the active rows only, ds only on active rows."""
+    import torch
+    dev = device()
+    rng = np.random.default_rng(12)
+    e, max_m, n = 300, 40, 136
+    mm = rng.integers(0, max_m + 1, size=e).astype(np.int32)
+    mm[3], mm[4], mm[5] = -7, max_m + 9, 0
+    wl = synth.custom_masked("dbias_masked", mm, max_m, 8, n, seed=6)
+    t = synth.make_inputs(wl, dev, need=("dy",))
+    counts = torch.tensor(mm, dtype=torch.int32, device=dev)
+    scale = torch.rand((e * max_m,), device=dev)
+    bias = (torch.randn((e, n), device=dev) * 0.5).to(torch.bfloat16)
+    say("masked bias grads, out-of-range counts, n 136")
+    db = gg.bias_grad(t["dy"], counts, scale, masked=True)
+    ds = gg.bias_scale_grad(t["dy"], counts, bias, masked=True)
+    torch.cuda.synchronize()
+    dy_bits = synth.bf16_bits(t["dy"])
+    ref = oracle.bias_grad(dy_bits, mm, scale.cpu().numpy(), masked=True)
+    check(db.cpu().numpy(), ref.value, ref.sabs, max_m, "masked bias_grad clamped")
+    active = np.clip(mm, 0, max_m)
+    assert np.all(db.cpu().numpy()[active == 0] == 0.0)
+    rs = oracle.bias_scale_grad(dy_bits, mm, synth.bf16_bits(bias), masked=True)
+    ok = rs.status == 1
+    dh = ds.cpu().numpy()
+    check(dh[ok][:, None], rs.value[ok], rs.sabs[ok], n, "masked bias_scale_grad clamped")
+    assert np.all(np.isnan(dh[~ok]))
+
+
+def test_bias_grads_full_size_qwen3():
+    """Both reductions at the Qwen3 gate/up size (65536 rows, N 1536, 128
+    experts with empty and 8- / 16-row experts), against the oracle on every
+    element."""
+    import torch
+    dev = device()
+    wl = synth.by_name("qwen3_gateup")
+    t = synth.make_inputs(wl, dev, need=("dy",))
+    logical = int(wl.offs[-1])
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    scale = torch.rand((logical,), generator=g, device=dev)
+    bias = (torch.randn((wl.num_groups, wl.n), generator=g, device=dev) * 0.5).to(torch.bfloat16)
+    say("bias grads, qwen3_gateup full size")
+    db = gg.bias_grad(t["dy"], t["offs"], scale)
+    ds = gg.bias_scale_grad(t["dy"], t["offs"], bias)
+    torch.cuda.synchronize()
+    dy_bits = synth.bf16_bits(t["dy"])
+    ref = oracle.bias_grad(dy_bits, wl.offs, scale.cpu().numpy())
+    check(db.cpu().numpy(), ref.value, ref.sabs, int(wl.group_sizes().max()), "bias_grad qwen3")
+    rs = oracle.bias_scale_grad(dy_bits, wl.offs, synth.bf16_bits(bias))
+    ok = rs.status == 1
+    check(ds.cpu().numpy()[ok][:, None], rs.value[ok], rs.sabs[ok], wl.n, "bias_scale_grad qwen3")
