@@ -21,13 +21,14 @@ typedef uint32_t u32x4b __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-// dbias: a workgroup owns 128 columns of one expert -- 16 column groups of 8
-// (a row's 256 bytes per 16 lanes) by 16 row lanes, each with 4 rows in
-// flight.
-constexpr int kDbCols = 128;
-constexpr int kDbGroups = kDbCols / 8;
-constexpr int kDbLanes = kThreads / kDbGroups;
-constexpr int kDbUnroll = 4;
+// dbias: a workgroup owns COLS (64 or 128) columns of one expert -- COLS / 8
+// column groups of 8 (16 bytes per lane) by the remaining row lanes, each
+// thread with 8 rows in flight.
+constexpr int kDbUnroll = 8;
+// Average rows per expert from which a workgroup takes 128 columns: large
+// experts stream better with 256 bytes of a row per workgroup, many small
+// (and typically skewed) experts balance better over twice the workgroups.
+constexpr int64_t kDbWideRows = 2048;
 
 __device__ __forceinline__ void unpack8(const u32x4b q, float (&v)[8]) {
 #pragma unroll
@@ -81,16 +82,18 @@ __device__ __forceinline__ void group_rows(const int32_t* groups, int g, int64_t
   }
 }
 
-// One workgroup per (expert, 128-column block).  Thread (c, l) = (tid mod
-// 16, tid / 16) sums columns 8 c .. 8 c + 7 over rows start + l + 16 j:
-// rows 64 q + 16 u + l go to partial sum u (u = 0..3, loads of four rows in
-// flight), the rows past the last whole group of 64 to partial sum 0.  The
-// thread adds its four partials in order u = 0..3, and the 16 row lanes of
-// a column are added in LDS in order l = 0..15: a fixed order per element.
-template <bool MASKED>
+// One workgroup per (expert, COLS-column block).  Thread (c, l) = (tid mod
+// G, tid / G), G = COLS / 8, sums columns 8 c .. 8 c + 7 over its rows
+// start + l, start + l + L, ... (L = 256 / G row lanes) in increasing order,
+// loading 8 of them at a time; the L row lanes of a column are then added in
+// LDS in order l = 0..L-1: a fixed order per element.
+template <bool MASKED, int COLS>
 __global__ __launch_bounds__(kThreads) void dbias_kernel(const uint16_t* dy, const int32_t* groups,
                                                          const float* scale, int64_t m, int64_t n,
                                                          int32_t E, float* dbias) {
+  constexpr int kDbCols = COLS;
+  constexpr int kDbGroups = COLS / 8;
+  constexpr int kDbLanes = kThreads / kDbGroups;
   __shared__ float part[kDbLanes][kDbCols];
   __shared__ int32_t red[2 * kWaves];
   const int col_blocks = (int)((n + kDbCols - 1) / kDbCols);
@@ -102,11 +105,9 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(const uint16_t* dy, con
   const int64_t col = (int64_t)cb * kDbCols + 8 * c;
   int64_t start, end;
   group_rows<MASKED>(groups, g, m, tid, red, start, end);
-  float acc[kDbUnroll][8];
+  float acc[8];
 #pragma unroll
-  for (int u = 0; u < kDbUnroll; ++u)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[u][e] = 0.f;
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   if (col < n) {
     int64_t i = start + l;
     for (; i + (kDbUnroll - 1) * kDbLanes < end; i += kDbUnroll * kDbLanes) {
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(const uint16_t* dy, con
         float v[8];
         unpack8(q[u], v);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[u][e] += s[u] * v[e];
+        for (int e = 0; e < 8; ++e) acc[e] += s[u] * v[e];
       }
     }
     for (; i < end; i += kDbLanes) {
@@ -131,11 +132,11 @@ __global__ __launch_bounds__(kThreads) void dbias_kernel(const uint16_t* dy, con
       float v[8];
       unpack8(*reinterpret_cast<const u32x4b*>(dy + i * n + col), v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[0][e] += s * v[e];
+      for (int e = 0; e < 8; ++e) acc[e] += s * v[e];
     }
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) part[l][8 * c + e] = ((acc[0][e] + acc[1][e]) + acc[2][e]) + acc[3][e];
+  for (int e = 0; e < 8; ++e) part[l][8 * c + e] = acc[e];
   __syncthreads();
   for (int j = tid; j < kDbCols; j += kThreads) {
     const int64_t cc = (int64_t)cb * kDbCols + j;
@@ -228,14 +229,19 @@ __global__ __launch_bounds__(kThreads) void dscale_kernel(const uint16_t* dy, co
 
 hipError_t launch_dbias(bool masked, const void* dy, const int32_t* groups, const float* scale, int64_t m,
                         int64_t n, int32_t E, float* dbias, hipStream_t stream) {
-  const int col_blocks = (int)((n + kDbCols - 1) / kDbCols);
-  const dim3 grid((unsigned)(E * col_blocks));
-  if (masked)
-    hipLaunchKernelGGL(dbias_kernel<true>, grid, dim3(kThreads), 0, stream, static_cast<const uint16_t*>(dy),
-                       groups, scale, m, n, E, dbias);
+  // rows per expert: max_m (masked), or the average m / E (ragged)
+  const bool wide = (masked ? m : m / E) >= kDbWideRows;
+  const int cols = wide ? 128 : 64;
+  const dim3 grid((unsigned)(E * ((n + cols - 1) / cols)));
+  const uint16_t* d = static_cast<const uint16_t*>(dy);
+  if (masked && wide)
+    hipLaunchKernelGGL((dbias_kernel<true, 128>), grid, dim3(kThreads), 0, stream, d, groups, scale, m, n, E, dbias);
+  else if (masked)
+    hipLaunchKernelGGL((dbias_kernel<true, 64>), grid, dim3(kThreads), 0, stream, d, groups, scale, m, n, E, dbias);
+  else if (wide)
+    hipLaunchKernelGGL((dbias_kernel<false, 128>), grid, dim3(kThreads), 0, stream, d, groups, scale, m, n, E, dbias);
   else
-    hipLaunchKernelGGL(dbias_kernel<false>, grid, dim3(kThreads), 0, stream, static_cast<const uint16_t*>(dy),
-                       groups, scale, m, n, E, dbias);
+    hipLaunchKernelGGL((dbias_kernel<false, 64>), grid, dim3(kThreads), 0, stream, d, groups, scale, m, n, E, dbias);
   return hipGetLastError();
 }
 

@@ -258,3 +258,26 @@ def test_bias_grads_full_size_qwen3():
     rs = oracle.bias_scale_grad(dy_bits, wl.offs, synth.bf16_bits(bias))
     ok = rs.status == 1
     check(ds.cpu().numpy()[ok][:, None], rs.value[ok], rs.sabs[ok], wl.n, "bias_scale_grad qwen3")
+
+
+@pytest.mark.parametrize("masked", [False, True])
+def test_bias_grads_large_experts_partial_columns(masked):
+    """Experts of 1500-3000 rows (at least 2048 per expert on average, so
+    workgroups take 128 columns) with N = 200 / 136, a partial block."""
+    import torch
+    dev = device()
+    if masked:
+        wl = synth.custom_masked("dbias_wide_masked", [2100, 1234], 2100, 8, 136, seed=8)
+        groups_h = wl.masked_m
+    else:
+        wl = synth.custom_ragged("dbias_wide", [2048, 3000, 1500], 8, 200, seed=9, m=6548 + 100)
+        groups_h = wl.offs
+    t = synth.make_inputs(wl, dev, need=("dy",))
+    groups = t["masked_m"] if masked else t["offs"]
+    rows_total = wl.num_groups * wl.m if masked else wl.m
+    scale = torch.rand((rows_total,), device=dev)
+    say("bias grads, large experts", masked)
+    db = gg.bias_grad(t["dy"], groups, scale, masked=masked)
+    torch.cuda.synchronize()
+    ref = oracle.bias_grad(synth.bf16_bits(t["dy"]), groups_h, scale.cpu().numpy(), masked=masked)
+    check(db.cpu().numpy(), ref.value, ref.sabs, 3000, "bias_grad large experts")
