@@ -338,7 +338,8 @@ def main():
         # 16 with empty experts padded): routing, the row gather, the
         # forward on the padded layout, the weighted combine; and the
         # forward with the grouped bias scaled per token against the plain
-        # forward.
+        # forward; and the bias term's backward (dbias and the per-token
+        # factor's gradient) with the forward output standing in for dY.
         w4 = synth.qwen3_gateup()
         tokens4, topk4 = w4.m // 8, 8
         g4 = torch.Generator(device=dev)
@@ -360,6 +361,8 @@ def main():
         o4 = torch.empty((tokens4, w4.n), dtype=torch.bfloat16, device=dev)
         bias4 = (torch.randn((w4.num_groups, w4.n), generator=g4, device=dev) * 0.1).to(torch.bfloat16)
         bscale4 = torch.rand((cap4,), generator=g4, device=dev)
+        db4 = torch.empty((w4.num_groups, w4.n), dtype=torch.float32, device=dev)
+        ds4 = torch.empty((cap4,), dtype=torch.float32, device=dev)
         st4 = torch.cuda.current_stream(dev).cuda_stream
 
         def route4():
@@ -371,7 +374,9 @@ def main():
                               ("gather", lambda: gg.gather_rows(x4, rs4, topk4, offs4, out=xg4)),
                               ("forward", lambda: gg.forward(xg4, wt4, offs4, out=y4)),
                               ("forward_bias", lambda: gg.forward_bias(xg4, wt4, offs4, bias4, bscale4, out=y4)),
-                              ("combine", lambda: gg.combine_rows(y4, sr4, topk4, probs4, out=o4))],
+                              ("combine", lambda: gg.combine_rows(y4, sr4, topk4, probs4, out=o4)),
+                              ("bias_grad", lambda: gg.bias_grad(y4, offs4, bscale4, out=db4)),
+                              ("bias_scale_grad", lambda: gg.bias_scale_grad(y4, offs4, bias4, out=ds4))],
                              20, 3, torch)
         f4 = {k: sorted(v)[len(v) // 2] for k, v in ms4.items()}
         rows4 = int(offs4[-1].item())
@@ -384,8 +389,14 @@ def main():
             "forward_ms": round(f4["forward"], 4),
             "forward_bias_scaled_ms": round(f4["forward_bias"], 4),
             "combine_ms": round(f4["combine"], 4),
-            "combine_GB/s": round((tokens4 * topk4 * w4.n * 2 + tokens4 * w4.n * 2) / (f4["combine"] * 1e-3) / 1e9, 1)}
-        del x4, wt4, xg4, y4, o4, ws4, rs4, sr4
+            "combine_GB/s": round((tokens4 * topk4 * w4.n * 2 + tokens4 * w4.n * 2) / (f4["combine"] * 1e-3) / 1e9, 1),
+            "bias_grad_ms": round(f4["bias_grad"], 4),
+            "bias_grad_GB/s": round((rows4 * w4.n * 2 + rows4 * 4 + w4.num_groups * w4.n * 4)
+                                    / (f4["bias_grad"] * 1e-3) / 1e9, 1),
+            "bias_scale_grad_ms": round(f4["bias_scale_grad"], 4),
+            "bias_scale_grad_GB/s": round((rows4 * w4.n * 2 + rows4 * 4 + w4.num_groups * w4.n * 2)
+                                          / (f4["bias_scale_grad"] * 1e-3) / 1e9, 1)}
+        del x4, wt4, xg4, y4, o4, ws4, rs4, sr4, db4, ds4
         torch.cuda.empty_cache()
 
         # fp8 (e4m3) block-scaled forward: the GLM-up and Qwen3 gate/up
