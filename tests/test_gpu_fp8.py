@@ -126,22 +126,43 @@ def test_fp8_masked_inactive_rows_never_read():
     check_all_rows(wl, t, y1, "fp8 masked with garbage in inactive rows")
 
 
-def test_fp8_bad_scale_count_matches_oracle():
+@pytest.mark.parametrize("case", ["masked_scalar", "masked_vec", "ragged_vec"])
+def test_fp8_bad_scale_count_matches_oracle(case):
+    """Three non-UE8M0 scales planted in active rows are counted, and the
+    garbage in inactive rows (masked: past masked_m; ragged: capacity rows
+    past the last offset) is not.  K = 384 reads one scale per load; K = 1024
+    (8 k-blocks) takes the four-scales-per-load path."""
     dev = device()
     import torch
-    wl = synth.by_name("fp8_masked_gateup_small")
+    if case == "masked_scalar":
+        wl = synth.by_name("fp8_masked_gateup_small")
+    elif case == "masked_vec":
+        wl = synth.custom_masked("fp8_bad_vec", synth.uniform_masked_m(8, 256, 43), 256, 1024, 256, seed=43)
+    else:
+        sizes = np.array([300, 0, 77, 512, 129], dtype=np.int64)
+        wl = synth.custom_ragged("fp8_bad_ragged", sizes, 1024, 256, seed=44, m=int(sizes.sum()) + 40)
     t = synth.make_fp8_inputs(wl, dev)
     sizes = wl.group_sizes()
-    live = [e for e in range(wl.num_groups) if sizes[e] > 2]
     sx = t["sx"]
-    sx[live[0], 0, 0] = 0.3
-    sx[live[1], 1, 1] = -1.0
-    sx[live[-1], int(sizes[live[-1]]) - 1, 2] = 1.5
-    active = np.arange(wl.m)[None, :, None] < sizes[:, None, None]
+    if wl.layout == "masked":
+        live = [e for e in range(wl.num_groups) if sizes[e] > 2]
+        sx[live[0], 0, 0] = 0.3
+        sx[live[1], 1, 1] = -1.0
+        sx[live[-1], int(sizes[live[-1]]) - 1, 2] = 1.5
+        active = np.arange(wl.m)[None, :, None] < sizes[:, None, None]
+        layout, groups = gg.GG_FP8_ACT_MASKED, t["masked_m"]
+    else:
+        end = int(sizes.sum())
+        sx[end:, :] = 0.3                      # capacity rows: never validated
+        sx[0, 0] = 0.3
+        sx[350, 5] = -1.0
+        sx[end - 1, 7] = 1.5
+        active = (np.arange(wl.m) < end)[:, None]
+        layout, groups = gg.GG_FP8_ACT_RAGGED, t["offs"]
     want = oracle.ue8m0_violations(sx.cpu().numpy(), np.broadcast_to(active, sx.shape))
-    say("fp8 bad scale count")
+    say("fp8 bad scale count", case)
     bad = torch.zeros(1, dtype=torch.int32, device=dev)
-    gg.fp8_pack_scales(gg.GG_FP8_ACT_MASKED, sx, t["masked_m"], wl.m, wl.k, wl.num_groups, bad_count=bad)
+    gg.fp8_pack_scales(layout, sx, groups, wl.m, wl.k, wl.num_groups, bad_count=bad)
     torch.cuda.synchronize()
     assert want == 3
     assert int(bad.item()) == want
