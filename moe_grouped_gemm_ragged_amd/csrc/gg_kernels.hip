@@ -470,6 +470,225 @@ __device__ __attribute__((always_inline)) inline void mainloop(
 #undef GG_STAGE
 }
 
+// ---- full-line staging of reduction-contiguous operands (bf16 row passes) ----------
+//
+// One stage of a reduction-contiguous operand is 64 bytes per tile row: half
+// a cache line per row and load.  The row passes stage such an operand two
+// stages at a time instead, so that one load moves 128 contiguous bytes (both
+// stages) of 8 tile rows and every line is read whole.
+//
+// Stage pair j of A holds stages 2j and 2j + 1: tile rows 0..127 in A's
+// region of ring slot 2j mod 4, rows 128..255 in that of slot (2j + 1) mod
+// 4.  In a region, the 8 rows 8b..8b+7 (of its 128) fill 1 KB block b: the
+// first stage's 64 bytes of each row in the block's first 512 bytes, the
+// second stage's in the other 512, each row at 64 (r mod 8) with its 16-byte
+// chunks swizzled c ^ ((r / 4) mod 4) as in the single-stage layout
+// (fragment reads stay bank-conflict-free).  A pair can be loaded only when
+// both its regions are free, i.e. after stage 2j - 3, so its four loads per
+// wave are issued in the second half of that (odd) stage: two stages ahead,
+// not three.  B keeps one stage per slot and its loads three stages ahead,
+// whether reduction-strided (forward) or -contiguous (dgrad, whose B is the
+// weight stream: pairing it too measured slower, as it then has one stage
+// less to arrive).
+
+struct DmaPair {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t voff0;     // lane offset of loads 0 and 2
+  uint32_t voff1;     // of loads 1 and 3 (their rows' swizzle differs by 2)
+  uint32_t step;      // 8 rows (scalar offset per load)
+};
+
+// The 4 loads a wave issues for the stage pair of A whose first reduction
+// element is q0.  Load jj of
+// wave w covers tile rows 32 w + 8 jj .. + 7 (block 4 (w mod 4) + jj of
+// region w / 4); lane i: stage i / 32 of the pair, row 32 w + 8 jj + (i mod
+// 32) / 4, chunk position i mod 4, logical chunk (i mod 4) ^ ((row / 4) mod
+// 4).  Values outside [0, red) and rows past the tile read as zero.
+__device__ __forceinline__ DmaPair dma_pair(const Operand& op, int q0, int tid) {
+  const int lane = (int)opaque_v((uint32_t)(tid & 63));
+  const int w = tid >> 6;
+  DmaPair c;
+  const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - (uint32_t)(2 * q0) : 0u;
+  c.rs = make_rsrc(op.origin + (int64_t)2 * q0, nrec);
+  const int rin = (lane & 31) >> 2;
+  const int sw = rin >> 2;                           // ((32 w + rin) / 4) mod 4 for loads 0 and 2
+  const int kl = q0 + 32 * (lane >> 5);
+  const int k0 = kl + 8 * ((lane & 3) ^ sw);
+  const int k1 = kl + 8 * ((lane & 3) ^ sw ^ 2);
+  const uint32_t rowoff = (uint32_t)(32 * w + rin) * op.ld_bytes;
+  c.voff0 = k0 < op.red ? rowoff + (uint32_t)(2 * (k0 - q0)) : kOutOfRange;
+  c.voff1 = k1 < op.red ? rowoff + (uint32_t)(2 * (k1 - q0)) : kOutOfRange;
+  c.step = 8u * op.ld_bytes;
+  return c;
+}
+
+__device__ __forceinline__ void dma_load_pair(const DmaPair& c, uint8_t* region, int wave, int jj) {
+  const uint32_t wbase = opaque_s((uint32_t)uniform((wave & 3) * 4096));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, LDS_PTR(region + wbase + 1024 * jj), 16,
+                                           (jj & 1) ? c.voff1 : c.voff0, jj * c.step, 0, 0);
+}
+
+// Fragment addresses in the pair layout for a wave slice starting at tile
+// row r0 (a multiple of 64; the slice lies in one region): chunk 2 ks + l /
+// 32 of row r0 + l % 32.  Fragment i adds 4096, the second stage 512.
+__device__ __forceinline__ FragAddr frag_addr_pair(int r0, int lane) {
+  FragAddr f;
+  const int rr = (r0 & 127) + (lane & 31);
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    const int chunk = (2 * ks + (lane >> 5)) ^ ((rr >> 2) & 3);
+    f.o[ks] = (uint32_t)((rr >> 3) * 1024 + (rr & 7) * 64 + 16 * chunk);
+  }
+  return f;
+}
+
+__device__ __forceinline__ bf16x8 read_frag_pair(const uint8_t* region, const FragAddr& fa, int ks, int i,
+                                                 int par) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(region + fa.o[ks] +
+                                                                     (uint32_t)(i * 4096 + par * 512)));
+}
+
+// Loads a tile's main loop expects in flight when it starts, in this order:
+// A pair 0 (stages 0, 1), B stages 0 and 1, A pair 1 (stages 2, 3), B stage
+// 2; the first wait leaves the 8 after B stage 0 in flight.
+template <bool B_STRIDED>
+__device__ __attribute__((always_inline)) inline void prologue_loads_pair(
+    uint8_t* __restrict__ a0, uint8_t* __restrict__ a1, uint8_t* __restrict__ a2, uint8_t* __restrict__ a3,
+    uint8_t* __restrict__ b0, uint8_t* __restrict__ b1, uint8_t* __restrict__ b2, uint8_t* __restrict__ b3,
+    const uint8_t* __restrict__ a_origin, const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid,
+    int wave) {
+  A.origin = a_origin;
+  B.origin = b_origin;
+  const bool hi = wave >= 4;
+  {
+    const DmaPair c = dma_pair(A, 0, tid);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) dma_load_pair(c, hi ? a1 : a0, wave, jj);
+  }
+  {
+    const DmaCtx c0 = dma_ctx<B_STRIDED>(B, 0, tid);
+    dma_load(c0, b0, wave, 0);
+    dma_load(c0, b0, wave, 1);
+    const DmaCtx c1 = dma_ctx<B_STRIDED>(B, BK, tid);
+    dma_load(c1, b1, wave, 0);
+    dma_load(c1, b1, wave, 1);
+  }
+  {
+    const DmaPair c = dma_pair(A, 2 * BK, tid);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) dma_load_pair(c, hi ? a3 : a2, wave, jj);
+  }
+  {
+    const DmaCtx c2 = dma_ctx<B_STRIDED>(B, 2 * BK, tid);
+    dma_load(c2, b2, wave, 0);
+    dma_load(c2, b2, wave, 1);
+  }
+}
+constexpr int kPrologueLoadsPair = 8;   // per wave, after the first stage's loads
+
+// The reduction loop of one output tile with A in the pair layout and B one
+// stage per slot (loads three stages ahead, issued in the first half of
+// each stage).  ha: the region of the wave's A rows (0: tile rows 0..127,
+// 1: 128..255).  Loads in flight at each stage's wait: 8 in even stages, 4
+// in odd ones (an odd stage's wait is for the A pair issued two stages
+// before, followed only by two B stages).
+template <bool B_STRIDED, int TMA>
+__device__ __attribute__((always_inline)) inline void mainloop_pair(
+    uint8_t* __restrict__ a0, uint8_t* __restrict__ a1, uint8_t* __restrict__ a2, uint8_t* __restrict__ a3,
+    uint8_t* __restrict__ b0, uint8_t* __restrict__ b1, uint8_t* __restrict__ b2, uint8_t* __restrict__ b3,
+    const uint8_t* __restrict__ a_origin, const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid,
+    int wave, int ha, const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[TM][TN],
+    int prev_stores) {
+  constexpr int kSplitGap = TMA * TN / 2;     // B stage loads: two per first half
+  constexpr int kSplitAt = 1;
+  constexpr int kPairGap = TMA * TN / 4;      // pair loads: four per second half
+  A.origin = a_origin;
+  B.origin = b_origin;
+  const int nk = (A.red + BK - 1) / BK;
+  if (nk <= 0) return;
+  const bool hi = wave >= 4;
+  Frags f0, f1;
+  if (prev_stores == stores_f32<TM>())
+    stage_barrier_vm<kPrologueLoadsPair + stores_f32<TM>()>();
+  else if (prev_stores == stores_f32<2>())
+    stage_barrier_vm<kPrologueLoadsPair + stores_f32<2>()>();
+  else
+    stage_barrier_vm<kPrologueLoadsPair>();
+
+// Per stage U = KT mod 4 (a literal): the A region of stage U (pair slots
+// {0,1} or {2,3}, the wave's half), its parity in the pair, and B's slot.
+#define GG_RA(U) ((U) < 2 ? (ha ? a1 : a0) : (ha ? a3 : a2))
+#define GG_PA(U) ((U) & 1)
+#define GG_RB(U) ((U) == 0 ? b0 : (U) == 1 ? b1 : (U) == 2 ? b2 : b3)
+#define GG_READ_A(U, KS, I, F) \
+  { (F).a[(I)] = read_frag_pair(GG_RA(U), faa, (KS), (I), GG_PA(U)); }
+#define GG_READ_B(U, KS, J, F) \
+  { (F).b[(J)] = read_frag<B_STRIDED>(GG_RB(U), fab, (KS), (J)); }
+#pragma unroll
+  for (int i = 0; i < TMA; ++i) GG_READ_A(0, 0, i, f0)
+#pragma unroll
+  for (int j = 0; j < TN; ++j) GG_READ_B(0, 0, j, f0)
+#pragma unroll
+  for (int i = 0; i < TMA; ++i) GG_READ_A(0, 1, i, f1)
+#pragma unroll
+  for (int j = 0; j < TN; ++j) GG_READ_B(0, 1, j, f1)
+
+// One stage KT (U = KT mod 4).  First half: MFMAs on f0, with the loads of
+// B stage KT + 3 into slot U + 3.  Wait for stage KT + 1 and meet.  Second
+// half: MFMAs on f1, with (odd U) the loads of the A pair of stages KT + 3,
+// KT + 4 into slots {0,1} (U = 1) or {2,3} (U = 3), and the reads of stage
+// KT + 1's first-half fragments; then its second-half fragments.
+#define GG_STAGE_P(U, KT)                                                                         \
+  {                                                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    const DmaCtx cbs = dma_ctx<B_STRIDED>(B, ((KT) + 3) * BK, tid);                               \
+    _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                        \
+      const int i = q / TN, j = q % TN;                                                           \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.b[j], f0.a[i], acc[i][j], 0, 0, 0); \
+      if (q % kSplitGap == kSplitAt && q / kSplitGap < 2)                                         \
+        dma_load(cbs, ((U) == 0 ? b3 : (U) == 1 ? b0 : (U) == 2 ? b1 : b2), wave, q / kSplitGap);   \
+      __builtin_amdgcn_sched_barrier(0);                                                          \
+    }                                                                                             \
+    mfma_fence(acc);                                                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    if (((U) & 1) == 0) stage_barrier_vm<8>();                                                    \
+    else stage_barrier_vm<4>();                                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    constexpr bool kIssueA = ((U) & 1) == 1;                                                      \
+    DmaPair cp;                                                                                   \
+    if constexpr (kIssueA) cp = dma_pair(A, ((KT) + 3) * BK, tid);                                \
+    _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                        \
+      const int i = q / TN, j = q % TN;                                                           \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0); \
+      if (q % kPairGap == kPairGap - 1) {                                                         \
+        if constexpr (kIssueA)                                                                    \
+          dma_load_pair(cp, (U) == 1 ? (hi ? a1 : a0) : (hi ? a3 : a2), wave, q / kPairGap);      \
+      }                                                                                           \
+      if (q < TMA) GG_READ_A(((U) + 1) & 3, 0, q, f0)                                             \
+      else if (q < TMA + TN) GG_READ_B(((U) + 1) & 3, 0, q - TMA, f0)                             \
+      __builtin_amdgcn_sched_barrier(0);                                                          \
+    }                                                                                             \
+    mfma_fence(acc);                                                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    _Pragma("unroll") for (int i = 0; i < TMA; ++i) GG_READ_A(((U) + 1) & 3, 1, i, f1)            \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) GG_READ_B(((U) + 1) & 3, 1, j, f1)             \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+  }
+
+  for (int kt = 0; kt < nk; kt += 4) {
+    GG_STAGE_P(0, kt)
+    if (kt + 1 < nk) GG_STAGE_P(1, kt + 1)
+    if (kt + 2 < nk) GG_STAGE_P(2, kt + 2)
+    if (kt + 3 < nk) GG_STAGE_P(3, kt + 3)
+  }
+#undef GG_STAGE_P
+#undef GG_READ_A
+#undef GG_READ_B
+#undef GG_RA
+#undef GG_PA
+#undef GG_RB
+}
+
 // ---- fp8 (e4m3) block-scaled main loop ----------------------------------------------
 //
 // The same tile engine on bytes: a stage is 64 e4m3 values (64 bytes) of
@@ -1056,6 +1275,8 @@ template <int MODE, bool OUT_F32>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   constexpr bool A_STRIDED = is_wgrad(MODE);
   constexpr bool B_STRIDED = !is_dgrad(MODE) && !is_fp8(MODE);
+  // bf16 row passes: reduction-contiguous operands in the stage-pair layout
+  constexpr bool PAIRED = !is_wgrad(MODE) && !is_fp8(MODE);
 
   // LDS: NSTAGE stage buffers of 32 KB (A tile, then B tile); fp8: two
   // k-blocks of scales.
@@ -1099,9 +1320,14 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   const uint8_t* pa = reinterpret_cast<const uint8_t*>(p.a);
   const uint8_t* pb = reinterpret_cast<const uint8_t*>(p.b);
   uint8_t* pc = reinterpret_cast<uint8_t*>(p.c);
-  const FragAddr faa = frag_addr<A_STRIDED>(128 * wm, lane);
-  const FragAddr faa_half = frag_addr<A_STRIDED>(64 * wm, lane);   // half-height tiles
+  const FragAddr faa = PAIRED ? frag_addr_pair(128 * wm, lane) : frag_addr<A_STRIDED>(128 * wm, lane);
+  // half-height tiles
+  const FragAddr faa_half = PAIRED ? frag_addr_pair(64 * wm, lane) : frag_addr<A_STRIDED>(64 * wm, lane);
   const FragAddr fab = frag_addr<B_STRIDED>(64 * wn, lane);
+  uint8_t* const sa0 = smem;
+  uint8_t* const sa1 = smem + STAGE_BYTES;
+  uint8_t* const sa2 = smem + 2 * STAGE_BYTES;
+  uint8_t* const sa3 = smem + 3 * STAGE_BYTES;
 
   // Decode tile t (linear index over the output tile grid) into its
   // operand descriptions and output window.
@@ -1238,6 +1464,9 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
         prologue_loads8(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES, smem + 3 * STAGE_BYTES, s_sc,
                         T.A.origin, T.B.origin, T.sa, T.sb, (uint32_t)(p.k / 128 * 256), T.A, T.B, tid,
                         wave);
+      else if constexpr (PAIRED)
+        prologue_loads_pair<B_STRIDED>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
+                                       sa3 + OP_BYTES, T.A.origin, T.B.origin, T.A, T.B, tid, wave);
       else
         prologue_loads<A_STRIDED, B_STRIDED>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
                                              smem + 3 * STAGE_BYTES, T.A.origin, T.B.origin, T.A,
@@ -1280,6 +1509,16 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
         mainloop8<TM>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES, smem + 3 * STAGE_BYTES, s_sc,
                       cur.A.origin, cur.B.origin, cur.sa, cur.sb, sc_bytes, cur.A, cur.B, tid, wave, wm,
                       wn, faa, fab, acc);
+    } else if constexpr (PAIRED) {
+      // the wave's A rows: 128 wm.. (full height, region wm) or 64 wm.. (half, region 0)
+      if (half)
+        mainloop_pair<B_STRIDED, 2>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
+                                    sa3 + OP_BYTES, cur.A.origin, cur.B.origin, cur.A, cur.B, tid, wave, 0,
+                                    faa_half, fab, acc, prev_stores);
+      else
+        mainloop_pair<B_STRIDED, TM>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
+                                     sa3 + OP_BYTES, cur.A.origin, cur.B.origin, cur.A, cur.B, tid, wave, wm,
+                                     faa, fab, acc, prev_stores);
     } else {
       if (half)
         mainloop<A_STRIDED, B_STRIDED, 2>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
