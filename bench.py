@@ -46,8 +46,8 @@ KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_ragged_amd", "csrc", "gg_kerne
 # Valid only for the kernel source they were taken on (sha256 below); for any
 # other source the roofline reports traffic as null.
 MEASURED_TRAFFIC = {
-    "kernel_sha256": "d840fab8dcce00ceb7d28e6f8b174593b03e399b33d091112e935b44f15c46da",
-    "bytes": {"fwd": 23639475460, "dgrad": 25985065176, "wgrad": 32671123730},
+    "kernel_sha256": "5c830cd1f8a44ccdc2deda56b83d90e99067170ca9295079b93ca808ab935e5f",
+    "bytes": {"fwd": 23613605613, "dgrad": 25193938895, "wgrad": 31256210678},
 }
 
 
