@@ -345,9 +345,10 @@ __device__ __forceinline__ void stage_barrier_vm() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// The reduction loop of one output tile.  Stage kt (BK = 32 reduction
-// values of both operands) lives in LDS buffer kt mod 4, and the loads run
-// three stages ahead.  Per stage and wave, in this order:
+// The reduction loop of one output tile with both operands one stage per
+// slot (wgrad; the row passes use mainloop_pair below).  Stage kt (BK = 32
+// reduction values of both operands) lives in LDS buffer kt mod 4, and the
+// loads run three stages ahead.  Per stage and wave, in this order:
 //   MFMA sub-step 0 (fragments f0, read earlier), interleaved with the loads
 //   of the B half of stage kt+3 into the buffer of stage kt-1
 //   wait for stage kt+1, barrier
