@@ -500,25 +500,27 @@ struct DmaPair {
 };
 
 // The 4 loads a wave issues for the stage pair of A whose first reduction
-// element is q0.  Load jj of
+// element is q0 (ESZ bytes per element: a stage is 64 bytes of a row, 32 bf16
+// or 64 e4m3 values).  Load jj of
 // wave w covers tile rows 32 w + 8 jj .. + 7 (block 4 (w mod 4) + jj of
 // region w / 4); lane i: stage i / 32 of the pair, row 32 w + 8 jj + (i mod
 // 32) / 4, chunk position i mod 4, logical chunk (i mod 4) ^ ((row / 4) mod
 // 4).  Values outside [0, red) and rows past the tile read as zero.
+template <int ESZ = 2>
 __device__ __forceinline__ DmaPair dma_pair(const Operand& op, int q0, int tid) {
   const int lane = (int)opaque_v((uint32_t)(tid & 63));
   const int w = tid >> 6;
   DmaPair c;
-  const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - (uint32_t)(2 * q0) : 0u;
-  c.rs = make_rsrc(op.origin + (int64_t)2 * q0, nrec);
+  const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - (uint32_t)(ESZ * q0) : 0u;
+  c.rs = make_rsrc(op.origin + (int64_t)ESZ * q0, nrec);
   const int rin = (lane & 31) >> 2;
   const int sw = rin >> 2;                           // ((32 w + rin) / 4) mod 4 for loads 0 and 2
-  const int kl = q0 + 32 * (lane >> 5);
-  const int k0 = kl + 8 * ((lane & 3) ^ sw);
-  const int k1 = kl + 8 * ((lane & 3) ^ sw ^ 2);
+  const int kl = q0 + (64 / ESZ) * (lane >> 5);
+  const int k0 = kl + (16 / ESZ) * ((lane & 3) ^ sw);
+  const int k1 = kl + (16 / ESZ) * ((lane & 3) ^ sw ^ 2);
   const uint32_t rowoff = (uint32_t)(32 * w + rin) * op.ld_bytes;
-  c.voff0 = k0 < op.red ? rowoff + (uint32_t)(2 * (k0 - q0)) : kOutOfRange;
-  c.voff1 = k1 < op.red ? rowoff + (uint32_t)(2 * (k1 - q0)) : kOutOfRange;
+  c.voff0 = k0 < op.red ? rowoff + (uint32_t)(ESZ * (k0 - q0)) : kOutOfRange;
+  c.voff1 = k1 < op.red ? rowoff + (uint32_t)(ESZ * (k1 - q0)) : kOutOfRange;
   c.step = 8u * op.ld_bytes;
   return c;
 }
@@ -768,120 +770,154 @@ __device__ __forceinline__ void scale_read(const uint8_t* slot, int wm, int wn, 
   sb >>= 16 * (wn & 1);
 }
 
-template <int TMA>
-__device__ __forceinline__ void load_stage8(const Operand& A, const Operand& B, int st, uint8_t* buf,
-                                            int tid, int wave) {
-  const DmaCtx ca = dma_ctx<false, 1>(A, st * BK8, tid);
-  const DmaCtx cb = dma_ctx<false, 1>(B, st * BK8, tid);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) dma_load(ca, buf, wave, j);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) dma_load(cb, buf + OP_BYTES, wave, j);
+// Fragment i of a stage of X in the pair layout (the two chunks read_frag8
+// reads, at the pair layout's offsets).
+__device__ __forceinline__ i32x8 read_frag8_pair(const uint8_t* region, const FragAddr& fa, int i, int par) {
+  const uint32_t d = (uint32_t)(i * 4096 + par * 512);
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(region + fa.o[0] + d);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(region + fa.o[1] + d);
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// The fp8 tile's loads in flight when its main loop starts: stages 0..2,
-// the A half of stage 3, and the scales of k-blocks 0 and 1 (waves 0 and 1
-// only, issued before stages 0 and 2 so that every wait below finds them
-// complete when it finds the stage complete).
+// The fp8 tile's loads in flight when its main loop starts, in this order:
+// the scales of k-block 0, X pair 0 (stages 0, 1), W stages 0 and 1, the
+// scales of k-block 1, X pair 1 (stages 2, 3), W stage 2.  X is staged in
+// the pair layout of the bf16 row passes, W one stage per slot; the scales
+// are loaded by waves 0 and 1 only.
 __device__ __attribute__((always_inline)) inline void prologue_loads8(
-    uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
-    uint8_t* __restrict__ s3, uint8_t* __restrict__ sc, const uint8_t* __restrict__ a_origin,
-    const uint8_t* __restrict__ b_origin, const uint8_t* __restrict__ sa_tile,
-    const uint8_t* __restrict__ sb_tile, uint32_t sc_bytes, Operand A, Operand B, int tid, int wave) {
+    uint8_t* __restrict__ a0, uint8_t* __restrict__ a1, uint8_t* __restrict__ a2, uint8_t* __restrict__ a3,
+    uint8_t* __restrict__ b0, uint8_t* __restrict__ b1, uint8_t* __restrict__ b2, uint8_t* __restrict__ sc,
+    const uint8_t* __restrict__ a_origin, const uint8_t* __restrict__ b_origin,
+    const uint8_t* __restrict__ sa_tile, const uint8_t* __restrict__ sb_tile, uint32_t sc_bytes, Operand A,
+    Operand B, int tid, int wave) {
   A.origin = a_origin;
   B.origin = b_origin;
   const int lane = tid & 63;
+  const bool hi = wave >= 4;
   scale_load(sa_tile, sb_tile, sc_bytes, 0, sc, wave, lane);
-  load_stage8<TM>(A, B, 0, s0, tid, wave);
-  load_stage8<TM>(A, B, 1, s1, tid, wave);
+  {
+    const DmaPair c = dma_pair<1>(A, 0, tid);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) dma_load_pair(c, hi ? a1 : a0, wave, jj);
+  }
+  {
+    const DmaCtx c0 = dma_ctx<false, 1>(B, 0, tid);
+    dma_load(c0, b0, wave, 0);
+    dma_load(c0, b0, wave, 1);
+    const DmaCtx c1 = dma_ctx<false, 1>(B, BK8, tid);
+    dma_load(c1, b1, wave, 0);
+    dma_load(c1, b1, wave, 1);
+  }
   scale_load(sa_tile, sb_tile, sc_bytes, 1, sc + kScaleSlot, wave, lane);
-  load_stage8<TM>(A, B, 2, s2, tid, wave);
-  const DmaCtx ca = dma_ctx<false, 1>(A, 3 * BK8, tid);
-  dma_load(ca, s3, wave, 0);
-  dma_load(ca, s3, wave, 1);
+  {
+    const DmaPair c = dma_pair<1>(A, 2 * BK8, tid);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) dma_load_pair(c, hi ? a3 : a2, wave, jj);
+  }
+  {
+    const DmaCtx c2 = dma_ctx<false, 1>(B, 2 * BK8, tid);
+    dma_load(c2, b2, wave, 0);
+    dma_load(c2, b2, wave, 1);
+  }
 }
 
-// The fp8 reduction loop: the bf16 loop's stage schedule (loads of the B
-// half of stage kt+3 in the first half-stage, wait and barrier, loads of the
-// A half of stage kt+4 in the second), with the MFMAs of a stage split by
-// row blocks instead of reduction halves (first half: blocks i < TMA/2).
-// The W fragments of a stage serve both halves, so they are double-buffered
-// across stages (FB, NB); the X fragments of the first half of stage kt+1
-// are read during the second half of stage kt, the rest after it.  Even
-// stages also issue (waves 0, 1) the scales of k-block kt/2 + 2, into the
-// slot k-block kt/2 used; odd stages read the next k-block's scales right
-// after their barrier.  Waves 0 and 1 then have one more load in flight at every
-// wait.
+// The fp8 reduction loop: the bf16 row passes' schedule (W stage kt+3 loaded
+// in the first half-stage, wait and barrier, the X pair of stages kt+3, kt+4
+// in the second half of odd stages), with the MFMAs of a stage split by row
+// blocks instead of reduction halves (first half: blocks i < TMA/2).  The W
+// fragments of a stage serve both halves, so they are double-buffered across
+// stages (FB, NB); the X fragments of the first half of stage kt+1 are read
+// during the second half of stage kt, the rest after it.  Even stages also
+// issue (waves 0, 1) the scales of k-block kt/2 + 2, into the slot k-block
+// kt/2 used; odd stages read the next k-block's scales right after their
+// barrier.  Loads in flight at the waits: 8 in even stages and 4 in odd
+// ones, one more for waves 0 and 1 (a scale load).  ha: the pair-layout
+// region of the wave's X rows.
 template <int TMA>
 __device__ __attribute__((always_inline)) inline void mainloop8(
-    uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
-    uint8_t* __restrict__ s3, uint8_t* __restrict__ sc, const uint8_t* __restrict__ a_origin,
-    const uint8_t* __restrict__ b_origin, const uint8_t* __restrict__ sa_tile,
-    const uint8_t* __restrict__ sb_tile, uint32_t sc_bytes, Operand A, Operand B, int tid, int wave,
-    int wm, int wn, const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[TM][TN]) {
+    uint8_t* __restrict__ a0, uint8_t* __restrict__ a1, uint8_t* __restrict__ a2, uint8_t* __restrict__ a3,
+    uint8_t* __restrict__ b0, uint8_t* __restrict__ b1, uint8_t* __restrict__ b2, uint8_t* __restrict__ b3,
+    uint8_t* __restrict__ sc, const uint8_t* __restrict__ a_origin, const uint8_t* __restrict__ b_origin,
+    const uint8_t* __restrict__ sa_tile, const uint8_t* __restrict__ sb_tile, uint32_t sc_bytes, Operand A,
+    Operand B, int tid, int wave, int wm, int wn, int ha, const FragAddr& faa, const FragAddr& fab,
+    floatx16 (&acc)[TM][TN]) {
   constexpr int kSub = TMA / 2 * TN;                 // MFMAs per half-stage
   constexpr int kGap = kSub / 2 > 0 ? kSub / 2 : 1;
-  constexpr int kAt = 0;                            // loads with MFMAs 0 and kGap (measured best)
+  constexpr int kAt = 0;                            // W loads with MFMAs 0 and kGap (measured best)
   constexpr int kItems = TMA / 2 + TN;              // fragments read during the second half
   A.origin = a_origin;
   B.origin = b_origin;
   const int lane = tid & 63;
   const int nk = (A.red + BK8 - 1) / BK8;           // even: K is a multiple of 128
   if (nk <= 0) return;
+  const bool hi = wave >= 4;
   i32x8 fa[TMA], fb0[TN], fb1[TN];
   uint32_t sa0, sb0, sa1 = 0, sb1 = 0;
-  if (wave < 2) stage_barrier_vm<kPrologueLoads + 1>();
-  else stage_barrier_vm<kPrologueLoads>();
+  if (wave < 2) stage_barrier_vm<kPrologueLoadsPair + 1>();
+  else stage_barrier_vm<kPrologueLoadsPair>();
   scale_read<TMA>(sc, wm, wn, lane, sa0, sb0);
 #pragma unroll
-  for (int i = 0; i < TMA; ++i) fa[i] = read_frag8(s0, faa, i);
+  for (int i = 0; i < TMA; ++i) fa[i] = read_frag8_pair(ha ? a1 : a0, faa, i, 0);
 #pragma unroll
-  for (int j = 0; j < TN; ++j) fb0[j] = read_frag8(s0 + OP_BYTES, fab, j);
+  for (int j = 0; j < TN; ++j) fb0[j] = read_frag8(b0, fab, j);
 
-#define GG8_STAGE(BC, BN, BP, KT, FB, NB, SA, SB, ODD, SLOT, SA_N, SB_N)                   \
+// U = KT mod 4 (a literal): X of stage U in pair slots {0,1} or {2,3} (the
+// wave's half), parity U mod 2; W of stage U in slot U.
+#define GG8_RA(U) ((U) < 2 ? (ha ? a1 : a0) : (ha ? a3 : a2))
+#define GG8_RB(U) ((U) == 0 ? b0 : (U) == 1 ? b1 : (U) == 2 ? b2 : b3)
+#define GG8_STAGE(U, KT, FB, NB, SA, SB, SLOT, SA_N, SB_N)                                 \
   {                                                                                       \
+    constexpr bool kOdd = ((U) & 1) == 1;                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     const DmaCtx cb = dma_ctx<false, 1>(B, ((KT) + 3) * BK8, tid);                        \
     _Pragma("unroll") for (int q = 0; q < kSub; ++q) {                                    \
       const int i = q / TN, j = q % TN;                                                   \
       acc[i][j] = mfma8(i, j, FB[j], fa[i], acc[i][j], SA, SB);                           \
-      if (q % kGap == kAt && q / kGap < 2) dma_load(cb, (BP) + OP_BYTES, wave, q / kGap); \
+      if (q % kGap == kAt && q / kGap < 2) dma_load(cb, GG8_RB(((U) + 3) & 3), wave, q / kGap); \
       __builtin_amdgcn_sched_barrier(0);                                                  \
     }                                                                                     \
     mfma_fence(acc);                                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                    \
-    if (wave < 2) stage_barrier_vm<9>(); else stage_barrier_vm<8>();                      \
+    if (!kOdd) { if (wave < 2) stage_barrier_vm<9>(); else stage_barrier_vm<8>(); }       \
+    else { if (wave < 2) stage_barrier_vm<5>(); else stage_barrier_vm<4>(); }             \
     __builtin_amdgcn_sched_barrier(0);                                                    \
-    if (!(ODD)) scale_load(sa_tile, sb_tile, sc_bytes, (KT) / 2 + 2, sc + (SLOT) * kScaleSlot, wave, lane); \
-    if (ODD) scale_read<TMA>(sc + (SLOT) * kScaleSlot, wm, wn, lane, SA_N, SB_N);        \
-    const DmaCtx ca = dma_ctx<false, 1>(A, ((KT) + 4) * BK8, tid);                        \
+    if (!kOdd) scale_load(sa_tile, sb_tile, sc_bytes, (KT) / 2 + 2, sc + (SLOT) * kScaleSlot, wave, lane); \
+    if (kOdd) scale_read<TMA>(sc + (SLOT) * kScaleSlot, wm, wn, lane, SA_N, SB_N);        \
+    DmaPair cp;                                                                           \
+    if constexpr (kOdd) cp = dma_pair<1>(A, ((KT) + 3) * BK8, tid);                       \
     _Pragma("unroll") for (int q = 0; q < kSub; ++q) {                                    \
       const int i = TMA / 2 + q / TN, j = q % TN;                                         \
       acc[i][j] = mfma8(i, j, FB[j], fa[i], acc[i][j], SA, SB);                           \
-      if (q % kGap == kAt && q / kGap < 2) dma_load(ca, BC, wave, q / kGap);              \
-      if (q < TMA / 2) fa[q] = read_frag8(BN, faa, q);                                    \
-      else if (q < kItems) NB[q - TMA / 2] = read_frag8((BN) + OP_BYTES, fab, q - TMA / 2); \
+      if constexpr (kOdd) {                                                               \
+        _Pragma("unroll") for (int jj = q * 4 / kSub; jj < (q + 1) * 4 / kSub; ++jj)      \
+          dma_load_pair(cp, (U) == 1 ? (hi ? a1 : a0) : (hi ? a3 : a2), wave, jj);        \
+      }                                                                                   \
+      if (q < TMA / 2) fa[q] = read_frag8_pair(GG8_RA(((U) + 1) & 3), faa, q, ((U) + 1) & 1); \
+      else if (q < kItems) NB[q - TMA / 2] = read_frag8(GG8_RB(((U) + 1) & 3), fab, q - TMA / 2); \
       __builtin_amdgcn_sched_barrier(0);                                                  \
     }                                                                                     \
     mfma_fence(acc);                                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                    \
     _Pragma("unroll") for (int q = kSub; q < kItems; ++q) {                               \
-      if (q < TMA / 2) fa[q] = read_frag8(BN, faa, q);                                    \
-      else NB[q - TMA / 2] = read_frag8((BN) + OP_BYTES, fab, q - TMA / 2);               \
+      if (q < TMA / 2) fa[q] = read_frag8_pair(GG8_RA(((U) + 1) & 3), faa, q, ((U) + 1) & 1); \
+      else NB[q - TMA / 2] = read_frag8(GG8_RB(((U) + 1) & 3), fab, q - TMA / 2);        \
     }                                                                                     \
-    _Pragma("unroll") for (int i = TMA / 2; i < TMA; ++i) fa[i] = read_frag8(BN, faa, i); \
+    _Pragma("unroll") for (int i = TMA / 2; i < TMA; ++i)                                 \
+      fa[i] = read_frag8_pair(GG8_RA(((U) + 1) & 3), faa, i, ((U) + 1) & 1);              \
     __builtin_amdgcn_sched_barrier(0);                                                    \
   }
 
   for (int kt = 0; kt < nk; kt += 4) {
-    GG8_STAGE(s0, s1, s3, kt, fb0, fb1, sa0, sb0, false, 0, sa1, sb1)
-    GG8_STAGE(s1, s2, s0, kt + 1, fb1, fb0, sa0, sb0, true, 1, sa1, sb1)
+    GG8_STAGE(0, kt, fb0, fb1, sa0, sb0, 0, sa1, sb1)
+    GG8_STAGE(1, kt + 1, fb1, fb0, sa0, sb0, 1, sa1, sb1)
     if (kt + 2 < nk) {
-      GG8_STAGE(s2, s3, s1, kt + 2, fb0, fb1, sa1, sb1, false, 1, sa0, sb0)
-      GG8_STAGE(s3, s0, s2, kt + 3, fb1, fb0, sa1, sb1, true, 0, sa0, sb0)
+      GG8_STAGE(2, kt + 2, fb0, fb1, sa1, sb1, 1, sa0, sb0)
+      GG8_STAGE(3, kt + 3, fb1, fb0, sa1, sb1, 0, sa0, sb0)
     }
   }
 #undef GG8_STAGE
+#undef GG8_RA
+#undef GG8_RB
 }
 
 // ---- epilogue --------------------------------------------------------------------
@@ -1323,9 +1359,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   const uint8_t* pa = reinterpret_cast<const uint8_t*>(p.a);
   const uint8_t* pb = reinterpret_cast<const uint8_t*>(p.b);
   uint8_t* pc = reinterpret_cast<uint8_t*>(p.c);
-  const FragAddr faa = PAIRED ? frag_addr_pair(128 * wm, lane) : frag_addr<A_STRIDED>(128 * wm, lane);
+  // A in the pair layout for the row passes (bf16 and fp8), one stage per slot for wgrad
+  constexpr bool A_PAIRED = !is_wgrad(MODE);
+  const FragAddr faa = A_PAIRED ? frag_addr_pair(128 * wm, lane) : frag_addr<A_STRIDED>(128 * wm, lane);
   // half-height tiles
-  const FragAddr faa_half = PAIRED ? frag_addr_pair(64 * wm, lane) : frag_addr<A_STRIDED>(64 * wm, lane);
+  const FragAddr faa_half = A_PAIRED ? frag_addr_pair(64 * wm, lane) : frag_addr<A_STRIDED>(64 * wm, lane);
   const FragAddr fab = frag_addr<B_STRIDED>(64 * wn, lane);
   uint8_t* const sa0 = smem;
   uint8_t* const sa1 = smem + STAGE_BYTES;
@@ -1464,9 +1502,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   auto issue_prologue = [&](const Tile& T) __attribute__((always_inline)) {
     if (T.A.red > 0) {
       if constexpr (is_fp8(MODE))
-        prologue_loads8(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES, smem + 3 * STAGE_BYTES, s_sc,
-                        T.A.origin, T.B.origin, T.sa, T.sb, (uint32_t)(p.k / 128 * 256), T.A, T.B, tid,
-                        wave);
+        prologue_loads8(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES, s_sc, T.A.origin,
+                        T.B.origin, T.sa, T.sb, (uint32_t)(p.k / 128 * 256), T.A, T.B, tid, wave);
       else if constexpr (PAIRED)
         prologue_loads_pair<B_STRIDED>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
                                        sa3 + OP_BYTES, T.A.origin, T.B.origin, T.A, T.B, tid, wave);
@@ -1505,13 +1542,13 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     if constexpr (is_fp8(MODE)) {
       const uint32_t sc_bytes = (uint32_t)(p.k / 128 * 256);
       if (half)
-        mainloop8<2>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES, smem + 3 * STAGE_BYTES, s_sc,
-                     cur.A.origin, cur.B.origin, cur.sa, cur.sb, sc_bytes, cur.A, cur.B, tid, wave, wm,
-                     wn, faa_half, fab, acc);
+        mainloop8<2>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES, sa3 + OP_BYTES, s_sc,
+                     cur.A.origin, cur.B.origin, cur.sa, cur.sb, sc_bytes, cur.A, cur.B, tid, wave, wm, wn, 0,
+                     faa_half, fab, acc);
       else
-        mainloop8<TM>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES, smem + 3 * STAGE_BYTES, s_sc,
-                      cur.A.origin, cur.B.origin, cur.sa, cur.sb, sc_bytes, cur.A, cur.B, tid, wave, wm,
-                      wn, faa, fab, acc);
+        mainloop8<TM>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES, sa3 + OP_BYTES, s_sc,
+                      cur.A.origin, cur.B.origin, cur.sa, cur.sb, sc_bytes, cur.A, cur.B, tid, wave, wm, wn, wm,
+                      faa, fab, acc);
     } else if constexpr (PAIRED) {
       // the wave's A rows: 128 wm.. (full height, region wm) or 64 wm.. (half, region 0)
       if (half)
