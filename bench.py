@@ -46,8 +46,8 @@ KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_ragged_amd", "csrc", "gg_kerne
 # Valid only for the kernel source they were taken on (sha256 below); for any
 # other source the roofline reports traffic as null.
 MEASURED_TRAFFIC = {
-    "kernel_sha256": "5c830cd1f8a44ccdc2deda56b83d90e99067170ca9295079b93ca808ab935e5f",
-    "bytes": {"fwd": 23613605613, "dgrad": 25193938895, "wgrad": 31256210678},
+    "kernel_sha256": "642f6b985115e9091ba9dfb1d8f578fa37104324e308afb5a4180c0999b032d7",
+    "bytes": {"fwd": 23613794665, "dgrad": 24800790861, "wgrad": 31912930453},
 }
 
 
@@ -234,8 +234,8 @@ def main():
                           "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                           "algorithmic_GB/s": round(algorithmic_bytes(wl, name) / (avg * 1e-3) / 1e9, 1)}
     dom = max(per_pass, key=lambda k: per_pass[k]["ms"])
-    kernel_names = {"fwd": "grouped_gemm_kernel<0,false>", "dgrad": "grouped_gemm_kernel<1,false>",
-                    "wgrad": "grouped_gemm_kernel<2,true>"}
+    kernel_names = {"fwd": "grouped_gemm_kernel<0,false,false>", "dgrad": "grouped_gemm_kernel<1,false,false>",
+                    "wgrad": "grouped_gemm_kernel<2,true,false>"}
     # wgrad accumulating into the fp32 main-grad (beta = 1), same workload
     _, msa = time_passes([("wgrad_acc", lambda: gg.wgrad(t["x"], t["dy"], t["offs"], out=dw, beta=1.0))],
                          3, 1, torch)
