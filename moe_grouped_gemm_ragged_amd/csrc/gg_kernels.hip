@@ -1167,6 +1167,10 @@ __device__ __forceinline__ T block_scan_incl(T v, T* scratch, int tid) {
   return v;
 }
 
+// wgrad takes its experts longest first when there are at most this many
+// (the ordering costs each workgroup E^2 / 512 comparisons).
+constexpr int kOrderMaxGroups = 512;
+
 // First row of group g within its row range (the ragged layout's groups
 // follow one another; a masked group's rows start at 0 of its block).
 template <int MODE>
@@ -1241,6 +1245,29 @@ __device__ void decode_groups(const Params& p, int32_t* s_end, int32_t* s_pref, 
       s_half[E] = (int)(incl >> 32);
     }
     __syncthreads();
+  } else if (E <= kOrderMaxGroups) {
+    // wgrad: a wgrad tile lasts as many stages as its expert has 32-row
+    // blocks, and every expert has the same number of tiles.  Take the
+    // experts longest first -- by a quarter-octave class of their stage
+    // count, ties by index -- so that the persistent loop ends on short tiles
+    // (and, with rounds alternating direction, every workgroup gets about the
+    // same work).  The order is a function of the offsets alone, identical
+    // in every workgroup: key k(g) = class * 4096 + 4095 - g is unique, and
+    // an expert's rank is the number of larger keys.  s_half holds the keys,
+    // s_pref[rank] the expert.
+    for (int g = tid; g < E; g += NT) {
+      const int stages = (s_end[g] - group_start<MODE>(s_end, g) + 31) >> 5;
+      const int cls = (int)(4.0f * __log2f((float)(stages + 1)));
+      s_half[g] = cls * 4096 + (4095 - g);
+    }
+    __syncthreads();
+    for (int g = tid; g < E; g += NT) {
+      const int key = s_half[g];
+      int rank = 0;
+      for (int h = 0; h < E; ++h) rank += s_half[h] > key ? 1 : 0;
+      s_pref[rank] = g;
+    }
+    __syncthreads();
   }
 }
 
@@ -1263,12 +1290,16 @@ __device__ __forceinline__ int find_group(const int32_t* pref, int E, int t) {
 // workgroup b takes position (b mod 8) (G / 8) + b / 8, so each XCD works on
 // a contiguous run of the order below.  The last, partial round keeps the
 // plain order (any bijection works there).
-__device__ __forceinline__ int64_t xcd_tile(int64_t t, int64_t total) {
+// snake: odd rounds take the positions in reverse (wgrad with its experts
+// longest first, where consecutive rounds then even out).
+__device__ __forceinline__ int64_t xcd_tile(int64_t t, int64_t total, bool snake) {
   const int G = gridDim.x;
   const int b = blockIdx.x;
   const int64_t round0 = t - b;
   if ((G & 7) != 0 || round0 + G > total) return t;
-  return round0 + (int64_t)(b & 7) * (G >> 3) + (b >> 3);
+  int64_t pos = (int64_t)(b & 7) * (G >> 3) + (b >> 3);
+  if (snake && ((round0 / G) & 1)) pos = G - 1 - pos;
+  return round0 + pos;
 }
 
 // Order of an rows x cols grid of tiles: column strips of (up to) 8 tiles,
@@ -1372,17 +1403,20 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
 
   // Decode tile t (linear index over the output tile grid) into its
   // operand descriptions and output window.
+  // wgrad experts longest first (see decode_groups)
+  const bool ordered = is_wgrad(MODE) && E <= kOrderMaxGroups;
   auto decode_tile = [&](int64_t t, Tile& T) __attribute__((always_inline)) {
-    const int64_t u = xcd_tile(t, total);
+    const int64_t u = xcd_tile(t, total, ordered);
     int ct;
     int64_t rt_all;
     if constexpr (is_wgrad(MODE)) {
       // per expert: a row_tiles_w x col_tiles grid in strip order
       const int64_t per_g = (int64_t)row_tiles_w * col_tiles;
-      const int64_t gq = u / per_g;
+      const int64_t gq = u / per_g;             // position of the expert in the order
       int64_t rr;
       strip_order(u - gq * per_g, row_tiles_w, col_tiles, rr, ct);
-      rt_all = gq * row_tiles_w + rr;
+      const int64_t gx = ordered ? (int64_t)uniform(s_pref[gq]) : gq;
+      rt_all = gx * row_tiles_w + rr;
     } else if (u < full_tiles) {
       strip_order(u, full_tiles / col_tiles, col_tiles, rt_all, ct);
     } else {
