@@ -46,8 +46,8 @@ KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_ragged_amd", "csrc", "gg_kerne
 # Valid only for the kernel source they were taken on (sha256 below); for any
 # other source the roofline reports traffic as null.
 MEASURED_TRAFFIC = {
-    "kernel_sha256": "642f6b985115e9091ba9dfb1d8f578fa37104324e308afb5a4180c0999b032d7",
-    "bytes": {"fwd": 23613794665, "dgrad": 24800790861, "wgrad": 31912930453},
+    "kernel_sha256": "050048d7db26e58a161a742eccae00ecd4ae190623ebb9b91c398380d88a7df5",
+    "bytes": {"fwd": 23613100242, "dgrad": 25037699873, "wgrad": 23468592206},
 }
 
 
