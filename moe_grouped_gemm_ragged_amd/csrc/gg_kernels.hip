@@ -16,9 +16,9 @@
 //
 // (The [E, N, K] weight layout of the bf16 passes is these modes with the
 // dimensions exchanged; the host entry points do the mapping.)  Epilogues:
-// fp32 straight from the accumulators, or through LDS for bf16, for
-// alpha * P + beta * C, for the grouped bias s[i] * bias[g], and for the
-// SiLU-mul activation.
+// fp32 straight from the accumulators, or through LDS for bf16, for fp32
+// wgrad on short experts, for alpha * P + beta * C, for the grouped bias
+// s[i] * bias[g], and for the SiLU-mul activation.
 //
 // "red-contig" means the reduction index is the contiguous one in memory;
 // "red-strided" means the tile's row index is.
@@ -27,8 +27,10 @@
 // memory straight into LDS with buffer loads in LDS mode (16 bytes per lane,
 // 1 KB per wave instruction), one 32-deep reduction stage at a time, through
 // a ring of 4 LDS stages: the loads for stage s + 3 are issued while the
-// MFMAs consume stage s, so three stages of loads are always in flight.
-// Each operand keeps its memory layout in LDS:
+// MFMAs consume stage s.  In the row passes (bf16 and fp8) the A operand is
+// staged two stages at a time instead, so that its loads read whole cache
+// lines (the pair layout, stated with mainloop_pair).  Each operand keeps
+// its memory layout in LDS:
 //   red-contig  : 256 tile rows x 64 bytes (32 reduction values), the
 //                 16-byte chunk c of row r at position c ^ ((r / 4) mod 4);
 //                 MFMA fragments come from ds_read_b128.
@@ -50,7 +52,8 @@
 // Work decomposition (no host sync, no workspace): one workgroup per compute
 // unit.  Each workgroup decodes the device-side end offsets (or masked_m)
 // into LDS -- clamped ends by a prefix max, then a prefix sum of per-expert
-// tile counts -- and walks tiles t = blockIdx.x, blockIdx.x + gridDim.x, ...
+// tile counts (wgrad: its experts ranked longest first) -- and walks tiles
+// t = blockIdx.x, blockIdx.x + gridDim.x, ...
 // Stores are predicated by the buffer range check and per column group, so
 // rows that belong to no expert are never written and there is no output
 // memset; an expert with no rows costs nothing in forward/dgrad and still
