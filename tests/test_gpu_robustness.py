@@ -235,3 +235,23 @@ def test_masked_extremes(out):
     check(yh[act], ref.value[act], ref.sabs[act], k, "masked extremes", rep)
     assert np.all(raw_bits(yh[~act]) == sentinel_bits(odt)), "an inactive row was written"
     print(out, rep)
+
+
+@pytest.mark.parametrize("e,k,n", [(512, 64, 72), (513, 64, 72), (100, 296, 520)])
+def test_wgrad_expert_order_boundary(e, k, n):
+    """wgrad takes its experts longest first (and alternates the direction of
+    its rounds) up to 512 experts, in index order above: 512 and 513 experts
+    of one tile each (two rounds of the 256-workgroup grid), and 100 experts
+    of 6 tiles each (2.3 rounds); sizes skewed (many empty or tiny, a few
+    large) so that the order differs from the index order.  Every pass is
+    checked against the oracle on every element."""
+    import torch
+    dev = device()
+    rng = np.random.default_rng(e + k)
+    sizes = rng.choice([0, 0, 1, 5, 17, 40], size=e)
+    big = rng.choice(e, size=max(2, e // 40), replace=False)
+    sizes[big] = rng.integers(200, 700, size=len(big))
+    wl = synth.custom_ragged(f"wgrad_order_{e}", sizes, k, n, seed=e + 3)
+    t = synth.make_inputs(wl, dev)
+    _run_all_passes(wl, t)
+    torch.cuda.empty_cache()
