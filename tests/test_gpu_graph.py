@@ -80,3 +80,77 @@ def test_graph_replay_follows_device_offsets():
             rf = oracle.forward(hx, hw, new)
             ok = rf.status == 1
             check(host(y)[ok], rf.value[ok], rf.sabs[ok], k, "graph fwd vs oracle")
+
+
+def test_graph_replay_fp8_and_bias_paths():
+    """The fp8 path (activation-scale packing, then the fp8 forward) and the
+    grouped bias (forward with a per-token factor, then both bias gradients)
+    captured in one graph.  Between replays the offsets and the fp8
+    activation scales change in place on the device; every replay must equal
+    an eager run of the same calls bit for bit, and the bad-scale counter
+    (zeroed by a fill kernel inside the graph) must count afresh."""
+    import torch
+    dev = device()
+    E, k, n = 6, 256, 264
+    rng = np.random.default_rng(78)
+    groupings = []
+    for _ in range(3):
+        sizes = rng.multinomial(900, rng.dirichlet(np.ones(E)))
+        sizes[rng.integers(0, E)] = 0
+        groupings.append(np.cumsum(sizes).astype(np.int32))
+    m = int(max(g[-1] for g in groupings)) + 8
+    wl = synth.Workload("graph8", "ragged", E, m, k, n, seed=22, offs=groupings[0])
+    t8 = synth.make_fp8_inputs(wl, dev)
+    t = synth.make_inputs(wl, dev)
+    offs = t8["offs"]
+    sx = t8["sx"]
+    xs = torch.empty(gg.fp8_scale_bytes(gg.GG_FP8_ACT_RAGGED, m, k, E), dtype=torch.uint8, device=dev)
+    ws = gg.fp8_pack_scales(gg.GG_FP8_WEIGHT, t8["sw"], None, n, k, E)
+    bad = torch.zeros(1, dtype=torch.int32, device=dev)
+    bias = (torch.randn((E, n), device=dev) * 0.5).to(torch.bfloat16)
+    bscale = torch.rand((m,), device=dev)
+    y8 = torch.zeros((m, n), dtype=torch.bfloat16, device=dev)
+    yb = torch.zeros((m, n), dtype=torch.float32, device=dev)
+    db = torch.zeros((E, n), dtype=torch.float32, device=dev)
+    ds = torch.zeros((m,), dtype=torch.float32, device=dev)
+
+    def calls(y8o, ybo, dbo, dso, bado):
+        bado.zero_()
+        gg.fp8_pack_scales(gg.GG_FP8_ACT_RAGGED, sx, offs, m, k, E, out=xs, bad_count=bado)
+        gg.fp8_forward(t8["x8"], xs, t8["w8"], ws, offs, out=y8o)
+        gg.forward_bias(t["x"], t["w"], offs, bias, bscale, out=ybo)
+        gg.bias_grad(t["dy"], offs, bscale, out=dbo)
+        gg.bias_scale_grad(t["dy"], offs, bias, out=dso)
+
+    say("graph fp8 + bias: warm-up and capture")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        calls(y8, yb, db, ds, bad)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls(y8, yb, db, ds, bad)
+    torch.cuda.synchronize()
+
+    y8e, ybe, dbe, dse = (torch.zeros_like(a) for a in (y8, yb, db, ds))
+    bade = torch.zeros_like(bad)
+    for rep, new in enumerate(groupings[1:] + groupings[:1]):
+        offs.copy_(torch.from_numpy(new).to(dev))
+        sx[0, 0] = 0.3 if rep % 2 == 0 else 1.0       # a non-UE8M0 scale in row 0 on even replays
+        torch.cuda.synchronize()
+        say("graph fp8 + bias replay", rep)
+        graph.replay()
+        torch.cuda.synchronize()
+        junk = torch.randn(256, 256, device=dev) @ torch.randn(256, 256, device=dev)
+        calls(y8e, ybe, dbe, dse, bade)
+        torch.cuda.synchronize()
+        used = int(new[-1])
+        assert torch.equal(y8[:used].view(torch.int16), y8e[:used].view(torch.int16)), f"replay {rep}: fp8 Y"
+        assert torch.equal(yb[:used], ybe[:used]), f"replay {rep}: biased Y"
+        assert torch.equal(db, dbe), f"replay {rep}: dbias"
+        assert torch.equal(ds[:used], dse[:used]), f"replay {rep}: ds"
+        want_bad = 1 if (rep % 2 == 0 and used > 0) else 0     # row 0 belongs to the first non-empty expert
+        assert int(bad.item()) == int(bade.item()) == want_bad, f"replay {rep}: bad-scale count"
+        del junk
