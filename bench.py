@@ -177,7 +177,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path)", file=sys.stderr)
+              "(there is no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import torch
