@@ -91,6 +91,27 @@ def time_passes(fns, steps, warmup, torch):
     return t1 - t0, ms
 
 
+def device_info(torch):
+    """CU count and peak engine clock as the HIP runtime reports them, and the
+    dense bf16 MFMA peak they imply (CUs x clock x 4096 FLOP/clk/CU).  The
+    roofline keeps the published 2516.6 TFLOP/s; this is the cross-check."""
+    import ctypes
+    props = torch.cuda.get_device_properties(0)
+    info = {"name": props.name, "arch": props.gcnArchName, "cus": props.multi_processor_count,
+            "hbm_GiB": round(props.total_memory / 2**30, 1)}
+    try:
+        path = next(line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64.so" in line)
+        hip = ctypes.CDLL(path)
+        khz = ctypes.c_int(0)
+        # hipDeviceAttributeClockRate (5): peak engine clock in kHz
+        if hip.hipDeviceGetAttribute(ctypes.byref(khz), ctypes.c_int(5), ctypes.c_int(0)) == 0 and khz.value > 0:
+            info["max_sclk_MHz"] = khz.value // 1000
+            info["bf16_peak_from_device_TFLOP/s"] = round(props.multi_processor_count * khz.value * 1e3 * 4096 / 1e12, 1)
+    except (StopIteration, OSError, AttributeError):
+        pass
+    return info
+
+
 def algorithmic_bytes(wl, pass_):
     """Bytes the pass must move at minimum: active rows of its inputs and
     outputs and the weights of experts with rows (wgrad: all of fp32 dW)."""
@@ -467,6 +488,7 @@ def main():
             "flop_per_step": flop_step,
         },
         "frac_of_mfma_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "device": device_info(torch),
         "per_pass": per_pass,
         "roofline": roofline,
         "cpu_baseline": cpu,
