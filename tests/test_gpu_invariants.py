@@ -103,3 +103,62 @@ def test_masked_equals_ragged_on_compacted_rows():
     torch.cuda.synchronize()
     got = torch.cat([ym[e, :int(mm[e])] for e in range(len(mm))])
     assert torch.equal(got, yr)
+
+
+def test_concurrent_streams_match_serial():
+    """The library keeps no device state between calls (no workspace, no
+    counters): the four passes launched together on four streams, each
+    kernel persistent over every CU, give the same bits as one after another
+    on one stream, and leave the rows they must not write untouched."""
+    import torch
+    dev = device()
+    wl = _wl()
+    t = synth.make_inputs(wl, dev)
+    mwl = synth.masked_down("small")
+    mt = synth.make_inputs(mwl, dev, need=("x", "w"))
+    used = int(t["offs"][-1])
+    mm = mt["masked_m"].to(torch.int64).cpu()
+    active = (torch.arange(mwl.m)[None, :] < mm[:, None]).to(dev)     # [E, max_m]
+    sentinel = -63             # 0xFFC1 (bf16) or 0xFFFFFFC1 (fp32): a NaN no pass writes
+    say("concurrent streams")
+
+    def bits(x):
+        return x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32)
+
+    def prefilled(shape, dtype):
+        o = torch.empty(shape, dtype=dtype, device=dev)
+        bits(o).fill_(sentinel)
+        return o
+
+    y0 = prefilled((wl.m, wl.n), torch.bfloat16)
+    dx0 = prefilled((wl.m, wl.k), torch.bfloat16)
+    dw0 = prefilled((wl.num_groups, wl.k, wl.n), torch.float32)
+    ym0 = prefilled((mwl.num_groups, mwl.m, mwl.n), torch.bfloat16)
+    gg.forward(t["x"], t["w"], t["offs"], out=y0)
+    gg.dgrad(t["dy"], t["w"], t["offs"], out=dx0)
+    gg.wgrad(t["x"], t["dy"], t["offs"], out=dw0)
+    gg.masked_forward(mt["x"], mt["w"], mt["masked_m"], out=ym0)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(device=dev) for _ in range(4)]
+    main = torch.cuda.current_stream(dev)
+    calls = (lambda o: gg.forward(t["x"], t["w"], t["offs"], out=o),
+             lambda o: gg.dgrad(t["dy"], t["w"], t["offs"], out=o),
+             lambda o: gg.wgrad(t["x"], t["dy"], t["offs"], out=o),
+             lambda o: gg.masked_forward(mt["x"], mt["w"], mt["masked_m"], out=o))
+    for rep in range(3):
+        outs = [prefilled(r.shape, r.dtype) for r in (y0, dx0, dw0, ym0)]
+        for s in streams:
+            s.wait_stream(main)
+        for s, o, call in zip(streams, outs, calls):
+            with torch.cuda.stream(s):
+                call(o)
+        for s in streams:
+            main.wait_stream(s)
+        torch.cuda.synchronize()
+        for name, got, want in zip(("forward", "dgrad", "wgrad", "masked forward"), outs, (y0, dx0, dw0, ym0)):
+            assert torch.equal(bits(got), bits(want)), f"{name} differs on concurrent streams (repeat {rep})"
+    # the serial outputs themselves: rows past the last offset and inactive
+    # masked rows kept the sentinel, every written element did not
+    assert bool((bits(y0[used:]) == sentinel).all()) and bool((bits(dx0[used:]) == sentinel).all())
+    assert not bool((bits(y0[:used]) == sentinel).any()) and not bool((bits(dw0) == sentinel).any())
+    assert bool((bits(ym0)[~active] == sentinel).all()) and not bool((bits(ym0)[active] == sentinel).any())
