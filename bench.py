@@ -18,6 +18,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 
 Profiling helpers (each prints one JSON line of its own, not the bench line):
   --profile-pass {fwd,dgrad,wgrad}  run only that pass of the workload
+  --profile-workload NAME           ... of this workload instead (glm_up,
+                                    qwen3_gateup or dsv3)
   --copy-calibration                run a plain device-to-device copy of known
                                     size, to scale the FETCH_SIZE / WRITE_SIZE
                                     counters into bytes
@@ -193,6 +195,9 @@ def main():
                     help="skip the other workloads reported as context")
     ap.add_argument("--profile-pass", choices=("fwd", "dgrad", "wgrad"),
                     help="run only this pass (for counter collection) and exit")
+    ap.add_argument("--profile-workload", default="glm_up",
+                    choices=("glm_up", "qwen3_gateup", "dsv3"),
+                    help="the workload --profile-pass runs (default glm_up, the bench workload)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain copy of known size (counter calibration) and exit")
     args = ap.parse_args()
@@ -221,7 +226,7 @@ def main():
               flush=True)
         return
 
-    wl = synth.glm_up()
+    wl = synth.by_name(args.profile_workload) if args.profile_pass else synth.glm_up()
     log("generating", wl.name)
     t = synth.make_inputs(wl, dev)
     y = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device=dev)
