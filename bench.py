@@ -48,8 +48,8 @@ KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_ragged_amd", "csrc", "gg_kerne
 # Valid only for the kernel source they were taken on (sha256 below); for any
 # other source the roofline reports traffic as null.
 MEASURED_TRAFFIC = {
-    "kernel_sha256": "050048d7db26e58a161a742eccae00ecd4ae190623ebb9b91c398380d88a7df5",
-    "bytes": {"fwd": 23613100242, "dgrad": 25037699873, "wgrad": 23468592206},
+    "kernel_sha256": "fd91abfe4730992ba492957464a1800b0926314edad94b890b44730992a8f526",
+    "bytes": {"fwd": 23613423734, "dgrad": 25322833866, "wgrad": 23794400172},
 }
 
 
@@ -260,8 +260,8 @@ def main():
                           "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                           "algorithmic_GB/s": round(algorithmic_bytes(wl, name) / (avg * 1e-3) / 1e9, 1)}
     dom = max(per_pass, key=lambda k: per_pass[k]["ms"])
-    kernel_names = {"fwd": "grouped_gemm_kernel<0,false,false>", "dgrad": "grouped_gemm_kernel<1,false,false>",
-                    "wgrad": "grouped_gemm_kernel<2,true,false>"}
+    kernel_names = {"fwd": "grouped_gemm_kernel<0,false,false,false>", "dgrad": "grouped_gemm_kernel<1,false,false,false>",
+                    "wgrad": "grouped_gemm_kernel<2,true,false,false>"}
     # wgrad accumulating into the fp32 main-grad (beta = 1), same workload
     _, msa = time_passes([("wgrad_acc", lambda: gg.wgrad(t["x"], t["dy"], t["offs"], out=dw, beta=1.0))],
                          3, 1, torch)

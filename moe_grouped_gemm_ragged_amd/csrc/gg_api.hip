@@ -65,6 +65,11 @@ gg_status check(const void* p0, const void* p1, const void* groups, const void* 
   // Per-tile byte offsets are 32-bit: 256 rows of k or n fp32 values must
   // stay below 2^31 bytes.
   if (k > GG_MAX_KN || n > GG_MAX_KN) return fail(GG_ERR_BAD_DIM, "k and n must not exceed GG_MAX_KN");
+  // A weight operand is read down its rows through one 32-bit buffer range
+  // per stage that runs to its last row: one expert's k x n bf16 matrix
+  // must stay below 2^32 bytes.
+  if (k * n >= (int64_t(1) << 31))
+    return fail(GG_ERR_BAD_DIM, "k * n must be below 2^31 (each expert's weights under 4 GiB)");
   if ((double)(rows + E) * (double)(k > n ? k : n) * 4.0 > 4.0e18)
     return fail(GG_ERR_BAD_DIM, "problem too large");
   if (!aligned16(p0) || !aligned16(p1) || !aligned16(out) || !aligned16(groups))

@@ -189,7 +189,7 @@ struct DmaCtx {
   uint32_t step;      // extra byte offset per load (scalar offset)
 };
 
-template <bool STRIDED, int ESZ = 2>
+template <bool STRIDED, int ESZ = 2, bool WIDE = false>
 __device__ __forceinline__ DmaCtx dma_ctx(const Operand& op, int q0, int tid) {
   DmaCtx c;
   // lane terms recomputed per stage (a few VALU ops) rather than hoisted and
@@ -201,8 +201,16 @@ __device__ __forceinline__ DmaCtx dma_ctx(const Operand& op, int q0, int tid) {
     // load j covers reduction rows 16 (w mod 2) + 8 j .. + 7; lane i: row
     // 16 (w mod 2) + 8 j + i / 8, chunk position i mod 8, logical chunk
     // (i mod 8) ^ 4 ((row / 2) mod 2) = (i mod 8) ^ 4 ((i / 16) mod 2).
+    // The range ends at the last reduction row.  WIDE: that row can lie
+    // 4 GB or more past this stage (a wgrad expert of 300k rows at k =
+    // 7168), which would wrap 32 bits.  A stage reads rows 0..31 of its
+    // origin only, so the range then stops at row 63 at most: every valid
+    // byte of those rows stays inside it, and it spans at most 2^27 bytes.
+    // Otherwise the host has bounded the whole span below 2^32.
     const int left = op.red - q0;
-    const uint32_t nrec = left > 0 ? (uint32_t)(left - 1) * op.ld_bytes + op.row_tail : 0u;
+    int last = left - 1;
+    if constexpr (WIDE) last = last < 63 ? last : 63;
+    const uint32_t nrec = left > 0 ? (uint32_t)last * op.ld_bytes + op.row_tail : 0u;
     c.rs = make_rsrc(op.origin + (int64_t)q0 * op.ld_bytes, nrec);
     const int chunk = (lane & 7) ^ (4 * ((lane >> 4) & 1));
     c.voff = (uint32_t)((lane >> 3) + 16 * (w & 1)) * op.ld_bytes + (uint32_t)(128 * (w >> 1) + 16 * chunk) +
@@ -320,11 +328,11 @@ __device__ __forceinline__ void mfma_fence(floatx16 (&acc)[TM][TN]) {
 
 // Issue the 4 global->LDS loads (2 per operand) of stage `st` into stage
 // buffer `buf` (A tile at +0, B tile at +OP_BYTES).
-template <bool A_STRIDED, bool B_STRIDED>
+template <bool A_STRIDED, bool B_STRIDED, bool WIDE>
 __device__ __forceinline__ void load_stage(const Operand& A, const Operand& B, int st, uint8_t* buf,
                                            int tid, int wave) {
-  const DmaCtx ca = dma_ctx<A_STRIDED>(A, st * BK, tid);
-  const DmaCtx cb = dma_ctx<B_STRIDED>(B, st * BK, tid);
+  const DmaCtx ca = dma_ctx<A_STRIDED, 2, WIDE>(A, st * BK, tid);
+  const DmaCtx cb = dma_ctx<B_STRIDED, 2, WIDE>(B, st * BK, tid);
 #pragma unroll
   for (int j = 0; j < 2; ++j) dma_load(ca, buf, wave, j);
 #pragma unroll
@@ -370,17 +378,17 @@ __device__ __forceinline__ void stage_barrier_vm() {
 // 0..2 and the A half of stage 3 (stage 0's first sub-step issues the B half
 // of stage 3).  Issued by the caller, so they can overlap the previous tile's
 // stores.  Only for tiles with at least one reduction step.
-template <bool A_STRIDED, bool B_STRIDED>
+template <bool A_STRIDED, bool B_STRIDED, bool WIDE = false>
 __device__ __attribute__((always_inline)) inline void prologue_loads(
     uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
     uint8_t* __restrict__ s3, const uint8_t* __restrict__ a_origin,
     const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid, int wave) {
   A.origin = a_origin;
   B.origin = b_origin;
-  load_stage<A_STRIDED, B_STRIDED>(A, B, 0, s0, tid, wave);
-  load_stage<A_STRIDED, B_STRIDED>(A, B, 1, s1, tid, wave);
-  load_stage<A_STRIDED, B_STRIDED>(A, B, 2, s2, tid, wave);
-  const DmaCtx ca = dma_ctx<A_STRIDED>(A, 3 * BK, tid);
+  load_stage<A_STRIDED, B_STRIDED, WIDE>(A, B, 0, s0, tid, wave);
+  load_stage<A_STRIDED, B_STRIDED, WIDE>(A, B, 1, s1, tid, wave);
+  load_stage<A_STRIDED, B_STRIDED, WIDE>(A, B, 2, s2, tid, wave);
+  const DmaCtx ca = dma_ctx<A_STRIDED, 2, WIDE>(A, 3 * BK, tid);
   dma_load(ca, s3, wave, 0);
   dma_load(ca, s3, wave, 1);
 }
@@ -395,7 +403,7 @@ constexpr int stores_f32() { return TMA * TN * 4; }
 // for a half-height tile (an expert's last 128 rows or fewer), whose waves
 // then own 64 x 64 each.  prev_stores: fp32 stores issued after this tile's
 // prologue loads (the previous tile's), 0 if none.
-template <bool A_STRIDED, bool B_STRIDED, int TMA>
+template <bool A_STRIDED, bool B_STRIDED, int TMA, bool WIDE = false>
 __device__ __attribute__((always_inline)) inline void mainloop(
     uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
     uint8_t* __restrict__ s3, const uint8_t* __restrict__ a_origin,
@@ -437,7 +445,7 @@ __device__ __attribute__((always_inline)) inline void mainloop(
 #define GG_STAGE(BC, BN, BP, KT)                                                          \
   {                                                                                       \
     __builtin_amdgcn_sched_barrier(0);                                                    \
-    const DmaCtx cb = dma_ctx<B_STRIDED>(B, ((KT) + 3) * BK, tid);                        \
+    const DmaCtx cb = dma_ctx<B_STRIDED, 2, WIDE>(B, ((KT) + 3) * BK, tid);               \
     _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                \
       const int i = q / TN, j = q % TN;                                                   \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.b[j], f0.a[i], acc[i][j], 0, 0, 0); \
@@ -449,7 +457,7 @@ __device__ __attribute__((always_inline)) inline void mainloop(
     __builtin_amdgcn_sched_barrier(0);                                                    \
     stage_barrier_vm<8>(); /* stage KT+1 landed; stage KT consumed */                     \
     __builtin_amdgcn_sched_barrier(0);                                                    \
-    const DmaCtx ca = dma_ctx<A_STRIDED>(A, ((KT) + 4) * BK, tid);                        \
+    const DmaCtx ca = dma_ctx<A_STRIDED, 2, WIDE>(A, ((KT) + 4) * BK, tid);               \
     _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                \
       const int i = q / TN, j = q % TN;                                                   \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0); \
@@ -1343,9 +1351,12 @@ struct Tile {
 
 
 // STAGED_F32: fp32 output through the LDS epilogue even when unscaled (the
-// host picks it for wgrad on short experts; see launch()).
-template <int MODE, bool OUT_F32, bool STAGED_F32 = false>
+// host picks it for wgrad on short experts; see launch()).  WIDE (wgrad
+// only): an expert's rows may span 4 GB or more of X or dY, so the load
+// ranges are capped per stage (see dma_ctx); the host picks it from m.
+template <int MODE, bool OUT_F32, bool STAGED_F32 = false, bool WIDE = false>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
+  static_assert(!WIDE || is_wgrad(MODE), "only wgrad reads an operand down a data-dependent span");
   constexpr bool A_STRIDED = is_wgrad(MODE);
   constexpr bool B_STRIDED = !is_dgrad(MODE) && !is_fp8(MODE);
   // bf16 row passes: reduction-contiguous operands in the stage-pair layout
@@ -1545,7 +1556,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
         prologue_loads_pair<B_STRIDED>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
                                        sa3 + OP_BYTES, T.A.origin, T.B.origin, T.A, T.B, tid, wave);
       else
-        prologue_loads<A_STRIDED, B_STRIDED>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
+        prologue_loads<A_STRIDED, B_STRIDED, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
                                              smem + 3 * STAGE_BYTES, T.A.origin, T.B.origin, T.A,
                                              T.B, tid, wave);
     }
@@ -1598,11 +1609,11 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
                                      faa, fab, acc, prev_stores);
     } else {
       if (half)
-        mainloop<A_STRIDED, B_STRIDED, 2>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
+        mainloop<A_STRIDED, B_STRIDED, 2, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
                                           smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
                                           cur.B, tid, wave, faa_half, fab, acc, prev_stores);
       else
-        mainloop<A_STRIDED, B_STRIDED, TM>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
+        mainloop<A_STRIDED, B_STRIDED, TM, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
                                            smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
                                            cur.B, tid, wave, faa, fab, acc, prev_stores);
     }
@@ -1666,9 +1677,9 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
 
 // ---- host-side launchers -------------------------------------------------------
 
-template <int MODE, bool OUT_F32, bool STAGED_F32 = false>
+template <int MODE, bool OUT_F32, bool STAGED_F32 = false, bool WIDE = false>
 static hipError_t launch_one(const Params& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, OUT_F32, STAGED_F32>), dim3(grid), dim3(NT), 0, stream, p);
+  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, OUT_F32, STAGED_F32, WIDE>), dim3(grid), dim3(NT), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -1683,6 +1694,21 @@ constexpr int64_t kStagedF32Rows = 2048;
 template <int MODE>
 static hipError_t launch_mode(const Params& p, bool out_f32, int grid, hipStream_t stream) {
   return out_f32 ? launch_one<MODE, true>(p, grid, stream) : launch_one<MODE, false>(p, grid, stream);
+}
+
+// wgrad reads X and dY down each expert's rows, one buffer range per stage
+// running to the expert's last row.  When an expert could span 4 GB of
+// either (bounded by all m rows, or max_m), the kernel caps those ranges.
+template <int MODE>
+static hipError_t launch_wgrad(const Params& p, bool out_f32, bool staged, int grid, hipStream_t stream) {
+  const int64_t widest = 2 * (p.k > p.n ? p.k : p.n);
+  if (p.m * widest < (int64_t(1) << 32)) {
+    if (staged) return launch_one<MODE, true, true>(p, grid, stream);
+    return launch_mode<MODE>(p, out_f32, grid, stream);
+  }
+  if (staged) return launch_one<MODE, true, true, true>(p, grid, stream);
+  return out_f32 ? launch_one<MODE, true, false, true>(p, grid, stream)
+                 : launch_one<MODE, false, false, true>(p, grid, stream);
 }
 
 // Upper bound on the number of output tiles, from host-known sizes only
@@ -1727,15 +1753,13 @@ hipError_t launch(int mode, const void* a, const void* b, const int32_t* groups,
     case FWD: return launch_mode<FWD>(p, out_f32, grid, stream);
     case DGRAD: return launch_mode<DGRAD>(p, out_f32, grid, stream);
     case WGRAD:
-      if (out_f32 && alpha == 1.0f && beta == 0.0f && m / num_groups < kStagedF32Rows)
-        return launch_one<WGRAD, true, true>(p, grid, stream);
-      return launch_mode<WGRAD>(p, out_f32, grid, stream);
+      return launch_wgrad<WGRAD>(p, out_f32, out_f32 && alpha == 1.0f && beta == 0.0f &&
+                                                 m / num_groups < kStagedF32Rows, grid, stream);
     case MASKED: return launch_mode<MASKED>(p, out_f32, grid, stream);
     case MASKED_DGRAD: return launch_mode<MASKED_DGRAD>(p, out_f32, grid, stream);
     case MASKED_WGRAD:
-      if (out_f32 && alpha == 1.0f && beta == 0.0f && m < kStagedF32Rows)
-        return launch_one<MASKED_WGRAD, true, true>(p, grid, stream);
-      return launch_mode<MASKED_WGRAD>(p, out_f32, grid, stream);
+      return launch_wgrad<MASKED_WGRAD>(p, out_f32, out_f32 && alpha == 1.0f && beta == 0.0f &&
+                                                       m < kStagedF32Rows, grid, stream);
     case FWD_SILU: return launch_mode<FWD_SILU>(p, out_f32, grid, stream);
     case MASKED_SILU: return launch_mode<MASKED_SILU>(p, out_f32, grid, stream);
   }

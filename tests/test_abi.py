@@ -274,3 +274,10 @@ def test_bias_grad_entry_points_check_arguments(lib, name, case, status):
     v.update(case)
     rc = gg.call_raw(name, v["dy"] or None, v["g"] or None, v["x"], v["o"] or None, v["m"], v["n"], v["e"], v["s"])
     assert rc == status, (name, case, rc, gg.last_error())
+
+
+@pytest.mark.parametrize("name", ENTRY)
+def test_weight_size_limit(lib, name):
+    # one expert's k x n weights must stay under 4 GiB (k * n < 2^31)
+    rc = call(name, k=65536, n=32768)
+    assert rc == 2 and "k * n" in gg.last_error(), (name, rc, gg.last_error())
