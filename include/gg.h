@@ -44,9 +44,9 @@
  *  - Requirements: k % 8 == 0 and n % 8 == 0 (16-byte rows), every pointer
  *    16-byte aligned, 1 <= num_groups <= GG_MAX_GROUPS, m (or max_m) >= 0,
  *    8 <= k, n <= GG_MAX_KN, k * n < 2^31 (each expert's weight matrix
- *    under 4 GiB in bf16), and fewer than 2^31 rows (m, or num_groups *
- *    max_m for the masked layout).  An expert's rows may span any number
- *    of bytes.
+ *    under 4 GiB in bf16), and fewer than 2^31 - 2^16 rows (m, or
+ *    num_groups * max_m for the masked layout).  An expert's rows may
+ *    span any number of bytes.
  *  - Concurrent calls on different streams that write the same output race;
  *    calls on one stream are ordered.
  */

@@ -48,6 +48,8 @@ gg_status device_cus(int* out) {
   return GG_OK;
 }
 
+constexpr int64_t kRowLimit = (int64_t(1) << 31) - (int64_t(1) << 16);
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // Shared checks.  rows = m (ragged) or max_m (masked).
@@ -60,8 +62,9 @@ gg_status check(const void* p0, const void* p1, const void* groups, const void* 
   if (k % 8 != 0 || n % 8 != 0) return fail(GG_ERR_BAD_DIM, "k and n must be multiples of 8");
   // Row indices and reduction lengths are int32 on the device; element
   // offsets are int64.  Keep every count comfortably inside both.
-  const int64_t lim31 = (int64_t(1) << 31) - 1;
-  if (rows > lim31) return fail(GG_ERR_BAD_DIM, "row count exceeds 2^31 - 1");
+  // (2^16 below 2^31, so that a row count plus a tile or a few stages of
+  // reduction rows still fits an int32 on the device)
+  if (rows >= kRowLimit) return fail(GG_ERR_BAD_DIM, "row count must be below 2^31 - 2^16");
   // Per-tile byte offsets are 32-bit: 256 rows of k or n fp32 values must
   // stay below 2^31 bytes.
   if (k > GG_MAX_KN || n > GG_MAX_KN) return fail(GG_ERR_BAD_DIM, "k and n must not exceed GG_MAX_KN");
@@ -94,8 +97,8 @@ gg_status run(int mode, const void* a, const void* b, const int32_t* groups, voi
 }
 
 gg_status masked_rows(int64_t max_m, int32_t E) {
-  if ((double)E * (double)max_m > 2147483647.0)
-    return fail(GG_ERR_BAD_DIM, "num_groups * max_m exceeds 2^31 - 1");
+  if ((double)E * (double)max_m >= (double)kRowLimit)
+    return fail(GG_ERR_BAD_DIM, "num_groups * max_m must be below 2^31 - 2^16");
   return GG_OK;
 }
 

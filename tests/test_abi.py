@@ -55,7 +55,7 @@ def call(name, **kw):
 @pytest.mark.parametrize("case,status", [
     (dict(a=0), 1), (dict(b=0), 1), (dict(g=0), 1), (dict(c=0), 1),
     (dict(m=-1), 2), (dict(k=0), 2), (dict(n=0), 2), (dict(k=12), 2), (dict(n=20), 2),
-    (dict(k=(1 << 20) + 8), 2), (dict(m=1 << 31), 2),
+    (dict(k=(1 << 20) + 8), 2), (dict(m=1 << 31), 2), (dict(m=(1 << 31) - (1 << 16)), 2),
     (dict(a=A + 8), 3), (dict(b=A + 2), 3), (dict(c=A + 4), 3), (dict(g=A + 4), 3),
     (dict(dt=2), 4), (dict(dt=-1), 4),
     (dict(e=0), 5), (dict(e=-3), 5), (dict(e=2049), 5),
