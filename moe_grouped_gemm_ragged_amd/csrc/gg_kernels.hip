@@ -1557,8 +1557,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
                                        sa3 + OP_BYTES, T.A.origin, T.B.origin, T.A, T.B, tid, wave);
       else
         prologue_loads<A_STRIDED, B_STRIDED, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
-                                             smem + 3 * STAGE_BYTES, T.A.origin, T.B.origin, T.A,
-                                             T.B, tid, wave);
+                                                   smem + 3 * STAGE_BYTES, T.A.origin, T.B.origin, T.A,
+                                                   T.B, tid, wave);
     }
   };
 
@@ -1610,12 +1610,12 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     } else {
       if (half)
         mainloop<A_STRIDED, B_STRIDED, 2, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
-                                          smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
-                                          cur.B, tid, wave, faa_half, fab, acc, prev_stores);
+                                                smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
+                                                cur.B, tid, wave, faa_half, fab, acc, prev_stores);
       else
         mainloop<A_STRIDED, B_STRIDED, TM, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
-                                           smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
-                                           cur.B, tid, wave, faa, fab, acc, prev_stores);
+                                                 smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
+                                                 cur.B, tid, wave, faa, fab, acc, prev_stores);
     }
     const int64_t tn = t + gridDim.x;
     if (OUT_F32 && !STAGED_F32 && !scaled && !is_silu(MODE) && !is_fp8(MODE)) {
