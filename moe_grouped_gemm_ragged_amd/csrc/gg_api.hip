@@ -455,7 +455,7 @@ int64_t gg_fp8_scale_bytes(gg_fp8_scale_layout layout, int64_t rows, int64_t k, 
   if (layout < GG_FP8_ACT_RAGGED || layout > GG_FP8_WEIGHT) return -1;
   if (rows < 0 || k < 128 || k % 128 != 0 || k > GG_MAX_KN) return -1;
   if (num_groups < 1 || num_groups > GG_MAX_GROUPS) return -1;
-  if (rows > (int64_t(1) << 31) - 1) return -1;
+  if (rows >= kRowLimit) return -1;
   return gg::fp8_scale_tiles((int)layout, rows, num_groups) * (k / 128) * 256;
 }
 
@@ -471,7 +471,7 @@ gg_status gg_fp8_pack_scales(gg_fp8_scale_layout layout, const void* src, int sr
   const int64_t kb = k / 128;
   if (ld_src < kb) return fail(GG_ERR_BAD_DIM, "ld_src must be at least k / 128");
   const double src_rows = layout == GG_FP8_ACT_RAGGED ? (double)rows : (double)rows * num_groups;
-  if (src_rows > 2147483647.0) return fail(GG_ERR_BAD_DIM, "row count exceeds 2^31 - 1");
+  if (src_rows >= (double)kRowLimit) return fail(GG_ERR_BAD_DIM, "row count must be below 2^31 - 2^16");
   if (src_rows * (double)ld_src * 4.0 > 4.0e18) return fail(GG_ERR_BAD_DIM, "problem too large");
   if (!aligned16(dst) || (groups && !aligned16(groups)) || (src_is_f32 && (reinterpret_cast<uintptr_t>(src) & 3u)))
     return fail(GG_ERR_ALIGNMENT, "dst and groups must be 16-byte aligned, fp32 src 4-byte aligned");

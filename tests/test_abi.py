@@ -163,7 +163,8 @@ def test_fp8_scale_bytes(lib, layout, rows, k, e, expect):
     assert gg.fp8_scale_bytes(layout, rows, k, e) == expect
 
 
-@pytest.mark.parametrize("args", [(3, 64, 128, 1), (0, 64, 100, 1), (0, -1, 128, 1), (0, 64, 128, 0)])
+@pytest.mark.parametrize("args", [(3, 64, 128, 1), (0, 64, 100, 1), (0, -1, 128, 1), (0, 64, 128, 0),
+                                  (0, (1 << 31) - (1 << 16), 128, 1)])
 def test_fp8_scale_bytes_rejects(lib, args):
     assert lib.gg_fp8_scale_bytes(*args) == -1
 
@@ -180,6 +181,7 @@ def call_pack(**kw):
 @pytest.mark.parametrize("case,status", [
     (dict(src=0), 1), (dict(dst=0), 1), (dict(g=0), 1), (dict(layout=1, g=0), 1),
     (dict(layout=5), 2), (dict(k=200), 2), (dict(ld=1), 2), (dict(rows=-1), 2),
+    (dict(rows=(1 << 31) - (1 << 16)), 2),
     (dict(dst=A + 8), 3), (dict(src=A + 2), 3),
     (dict(e=0), 5),
 ])
