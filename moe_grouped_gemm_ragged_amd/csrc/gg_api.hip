@@ -404,7 +404,7 @@ static gg_status bias_grad_check(const void* dy, const int32_t* groups, const vo
   if (rows < 0 || n < 8 || n % 8 != 0 || n > GG_MAX_KN)
     return fail(GG_ERR_BAD_DIM, "need rows >= 0 and n a positive multiple of 8 up to GG_MAX_KN");
   const double total = masked ? (double)rows * E : (double)rows;
-  if (total > 2147483647.0) return fail(GG_ERR_BAD_DIM, "row count exceeds 2^31 - 1");
+  if (total >= (double)kRowLimit) return fail(GG_ERR_BAD_DIM, "row count must be below 2^31 - 2^16");
   if (!aligned16(dy) || !aligned4(groups) || !aligned4(out))
     return fail(GG_ERR_ALIGNMENT, "dy must be 16-byte aligned");
   return GG_OK;
