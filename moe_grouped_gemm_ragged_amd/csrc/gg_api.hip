@@ -353,7 +353,9 @@ gg_status gg_route(const int32_t* expert_of_slot, int64_t slots, int32_t num_gro
     return fail(GG_ERR_BAD_DIM, "min_alignment must be in [1, 4096]");
   if (slots < 0) return fail(GG_ERR_BAD_DIM, "slots must be >= 0");
   const int64_t bound = gg_route_rows_bound(slots, num_groups, min_alignment);
-  if (bound > (int64_t(1) << 31) - 1) return fail(GG_ERR_BAD_DIM, "slots + num_groups * min_alignment exceeds 2^31 - 1");
+  // the rows it produces must be acceptable to the GEMMs (and fit int32)
+  if (bound >= kRowLimit)
+    return fail(GG_ERR_BAD_DIM, "slots + num_groups * min_alignment must be below 2^31 - 2^16");
   if (rows_cap < bound) return fail(GG_ERR_BAD_DIM, "rows_cap is below gg_route_rows_bound");
   if (!aligned4(expert_of_slot) || !aligned4(offs) || !aligned4(row_slot) || !aligned4(slot_row) ||
       !aligned16(workspace))
@@ -370,8 +372,8 @@ gg_status gg_gather_rows(const void* src, int64_t tokens, int64_t row_bytes, con
   if (num_groups < 1 || num_groups > GG_MAX_GROUPS) return fail(GG_ERR_LIMIT, "num_groups must be in [1, GG_MAX_GROUPS]");
   if (tokens < 0 || rows_cap < 0 || topk < 1 || row_bytes < 16 || row_bytes % 16 != 0)
     return fail(GG_ERR_BAD_DIM, "need tokens, rows_cap >= 0, topk >= 1, row_bytes a positive multiple of 16");
-  if (rows_cap > (int64_t(1) << 31) - 1 || tokens * (int64_t)topk > (int64_t(1) << 31) - 1)
-    return fail(GG_ERR_BAD_DIM, "row or slot count exceeds 2^31 - 1");
+  if (rows_cap >= kRowLimit || tokens * (int64_t)topk >= kRowLimit)
+    return fail(GG_ERR_BAD_DIM, "row and slot counts must be below 2^31 - 2^16");
   if (!aligned16(src) || !aligned16(dst) || !aligned4(row_slot) || !aligned4(offs))
     return fail(GG_ERR_ALIGNMENT, "src and dst must be 16-byte aligned");
   int cus = 0;
@@ -387,7 +389,8 @@ gg_status gg_combine_rows(const void* y, int64_t n, const int32_t* slot_row, con
   if (out_dtype != GG_BF16 && out_dtype != GG_F32) return fail(GG_ERR_BAD_DTYPE, "output dtype must be GG_BF16 or GG_F32");
   if (n < 8 || n % 8 != 0 || tokens < 0 || topk < 1 || rows_cap < 0)
     return fail(GG_ERR_BAD_DIM, "need n a positive multiple of 8, tokens, rows_cap >= 0, topk >= 1");
-  if (tokens * (int64_t)topk > (int64_t(1) << 31) - 1) return fail(GG_ERR_BAD_DIM, "slot count exceeds 2^31 - 1");
+  if (rows_cap >= kRowLimit || tokens * (int64_t)topk >= kRowLimit)
+    return fail(GG_ERR_BAD_DIM, "row and slot counts must be below 2^31 - 2^16");
   if (!aligned16(y) || !aligned16(out) || !aligned4(slot_row) || !aligned4(weights))
     return fail(GG_ERR_ALIGNMENT, "y and out must be 16-byte aligned");
   int cus = 0;

@@ -235,14 +235,12 @@ hipError_t launch_dbias(bool masked, const void* dy, const int32_t* groups, cons
   const dim3 grid((unsigned)(E * ((n + cols - 1) / cols)));
   const uint16_t* d = static_cast<const uint16_t*>(dy);
   if (masked && wide)
-    hipLaunchKernelGGL((dbias_kernel<true, 128>), grid, dim3(kThreads), 0, stream, d, groups, scale, m, n, E, dbias);
-  else if (masked)
-    hipLaunchKernelGGL((dbias_kernel<true, 64>), grid, dim3(kThreads), 0, stream, d, groups, scale, m, n, E, dbias);
-  else if (wide)
-    hipLaunchKernelGGL((dbias_kernel<false, 128>), grid, dim3(kThreads), 0, stream, d, groups, scale, m, n, E, dbias);
-  else
-    hipLaunchKernelGGL((dbias_kernel<false, 64>), grid, dim3(kThreads), 0, stream, d, groups, scale, m, n, E, dbias);
-  return hipGetLastError();
+    return launch_kernel(dbias_kernel<true, 128>, grid, dim3(kThreads), stream, d, groups, scale, m, n, E, dbias);
+  if (masked)
+    return launch_kernel(dbias_kernel<true, 64>, grid, dim3(kThreads), stream, d, groups, scale, m, n, E, dbias);
+  if (wide)
+    return launch_kernel(dbias_kernel<false, 128>, grid, dim3(kThreads), stream, d, groups, scale, m, n, E, dbias);
+  return launch_kernel(dbias_kernel<false, 64>, grid, dim3(kThreads), stream, d, groups, scale, m, n, E, dbias);
 }
 
 hipError_t launch_dscale(bool masked, const void* dy, const int32_t* groups, const void* bias, int64_t m,
@@ -252,14 +250,12 @@ hipError_t launch_dscale(bool masked, const void* dy, const int32_t* groups, con
   const int64_t cap = 8 * (int64_t)num_cus;
   const int grid = (int)(want < 1 ? 1 : (want < cap ? want : cap));
   if (masked)
-    hipLaunchKernelGGL(dscale_kernel<true>, dim3(grid), dim3(kThreads), 0, stream,
+    return launch_kernel(dscale_kernel<true>, dim3(grid), dim3(kThreads), stream,
+                         static_cast<const uint16_t*>(dy), groups, static_cast<const uint16_t*>(bias), m, n, E,
+                         rows, ds);
+  return launch_kernel(dscale_kernel<false>, dim3(grid), dim3(kThreads), stream,
                        static_cast<const uint16_t*>(dy), groups, static_cast<const uint16_t*>(bias), m, n, E,
                        rows, ds);
-  else
-    hipLaunchKernelGGL(dscale_kernel<false>, dim3(grid), dim3(kThreads), 0, stream,
-                       static_cast<const uint16_t*>(dy), groups, static_cast<const uint16_t*>(bias), m, n, E,
-                       rows, ds);
-  return hipGetLastError();
 }
 
 }  // namespace gg

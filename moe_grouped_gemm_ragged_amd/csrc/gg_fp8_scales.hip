@@ -218,15 +218,13 @@ hipError_t launch_layout(bool src_f32, const void* src, int64_t ld_src, const in
   const int grid = (int)(want > 0 ? want : 1);
   const bool vec = src_f32 && ld_src % 4 == 0 && kblocks % 4 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0;
   if (vec)
-    hipLaunchKernelGGL((pack_scales_kernel<LAYOUT, true, true>), dim3(grid), dim3(kThreads), 0, stream, src,
+    return launch_kernel(pack_scales_kernel<LAYOUT, true, true>, dim3(grid), dim3(kThreads), stream, src,
+                         ld_src, groups, rows, kblocks, E, tiles, dst, bad);
+  if (src_f32)
+    return launch_kernel(pack_scales_kernel<LAYOUT, true, false>, dim3(grid), dim3(kThreads), stream, src,
+                         ld_src, groups, rows, kblocks, E, tiles, dst, bad);
+  return launch_kernel(pack_scales_kernel<LAYOUT, false, false>, dim3(grid), dim3(kThreads), stream, src,
                        ld_src, groups, rows, kblocks, E, tiles, dst, bad);
-  else if (src_f32)
-    hipLaunchKernelGGL((pack_scales_kernel<LAYOUT, true, false>), dim3(grid), dim3(kThreads), 0, stream, src,
-                       ld_src, groups, rows, kblocks, E, tiles, dst, bad);
-  else
-    hipLaunchKernelGGL((pack_scales_kernel<LAYOUT, false, false>), dim3(grid), dim3(kThreads), 0, stream, src,
-                       ld_src, groups, rows, kblocks, E, tiles, dst, bad);
-  return hipGetLastError();
 }
 
 }  // namespace

@@ -3,11 +3,35 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
 // Experts per call the device-side decode holds in LDS.  Must equal
 // GG_MAX_GROUPS in include/gg.h.
 #define GG_MAX_GROUPS_DEV 2048
 
 namespace gg {
+// Launches `kernel` and returns the status of this launch itself, not the
+// thread's last error: an error that earlier, unrelated HIP work left behind
+// is not reported as this call's failure.  Arguments are converted to the
+// kernel's parameter types and passed by address, as hipLaunchKernel takes
+// them.
+template <typename... KArgs, typename... Args, size_t... I>
+inline hipError_t launch_kernel_impl(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                                     std::index_sequence<I...>, Args&&... args) {
+  std::tuple<KArgs...> vals(static_cast<KArgs>(args)...);
+  void* ptrs[sizeof...(KArgs) > 0 ? sizeof...(KArgs) : 1] = {static_cast<void*>(&std::get<I>(vals))...};
+  return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, ptrs, 0, stream);
+}
+
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t stream,
+                                Args&&... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count differs from the kernel's");
+  return launch_kernel_impl(kernel, grid, block, stream, std::index_sequence_for<KArgs...>{},
+                            std::forward<Args>(args)...);
+}
+
 // mode: 0 forward, 1 dgrad, 2 wgrad, 3 masked forward, 4 masked dgrad,
 // 5 masked wgrad, 6 forward with the SiLU-mul activation, 7 masked forward
 // with the SiLU-mul activation.  Arguments were

@@ -1679,8 +1679,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
 
 template <int MODE, bool OUT_F32, bool STAGED_F32 = false, bool WIDE = false>
 static hipError_t launch_one(const Params& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((grouped_gemm_kernel<MODE, OUT_F32, STAGED_F32, WIDE>), dim3(grid), dim3(NT), 0, stream, p);
-  return hipGetLastError();
+  return launch_kernel(grouped_gemm_kernel<MODE, OUT_F32, STAGED_F32, WIDE>, dim3(grid), dim3(NT), stream, p);
 }
 
 // Unscaled fp32 wgrad tiles store straight from the accumulators, with the

@@ -35,8 +35,17 @@ constexpr int kRouteThreads = 512;
 constexpr int kChunk = 1024;          // slots per block in the route passes
 constexpr int kPerThread = kChunk / kRouteThreads;
 
+// End offsets saturate here: the grouped GEMMs take at most this many rows
+// (2^31 - 2^16), and clamp every end offset to their row count, so a
+// saturated sum stays monotone and reads as "up to the last row" instead of
+// wrapping negative in int32.
+constexpr int64_t kOffsetCap = (int64_t(1) << 31) - (int64_t(1) << 16);
+
+__device__ __forceinline__ int32_t cap_offset(int64_t v) { return (int32_t)(v < kOffsetCap ? v : kOffsetCap); }
+
 __device__ __forceinline__ int64_t pad_count(int64_t c, int align, bool pad_empty) {
   c = c < 0 ? 0 : c;
+  c = c < kOffsetCap ? c : kOffsetCap;      // a sum of such counts stays far inside int64
   int64_t p = (c + align - 1) / align * align;
   if (pad_empty && p < align) p = align;
   return p;
@@ -73,7 +82,7 @@ __global__ __launch_bounds__(1024) void offsets_from_splits_kernel(const int64_t
   block_exclusive_scan(local, s, tid, 1024);
   for (int g = g0; g < g1; ++g) {
     local += pad_count(splits[g], align, pad_empty != 0);
-    offs[g] = (int32_t)local;
+    offs[g] = cap_offset(local);
   }
 }
 
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(int32_t* hist, int32_t
     }
     const int64_t end = start + pad_count(run - start, align, pad_empty != 0);
     for (int64_t r = run; r < end; ++r) row_slot[r] = -1;
-    offs[g] = (int32_t)end;
+    offs[g] = cap_offset(end);   // below the cap: the host bounds the rows
     start = end;
   }
 }
@@ -279,9 +288,8 @@ int64_t route_blocks(int64_t slots) { return (slots + kChunk - 1) / kChunk; }
 
 hipError_t launch_offsets_from_splits(const int64_t* splits, int32_t E, int32_t align, bool pad_empty,
                                       int32_t* offs, hipStream_t stream) {
-  hipLaunchKernelGGL(offsets_from_splits_kernel, dim3(1), dim3(1024), 0, stream, splits, E, align,
-                     pad_empty ? 1 : 0, offs);
-  return hipGetLastError();
+  return launch_kernel(offsets_from_splits_kernel, dim3(1), dim3(1024), stream, splits, E, align,
+                       pad_empty ? 1 : 0, offs);
 }
 
 hipError_t launch_route(const int32_t* expert, int64_t slots, int32_t E, int32_t align, bool pad_empty,
@@ -289,26 +297,23 @@ hipError_t launch_route(const int32_t* expert, int64_t slots, int32_t E, int32_t
                         hipStream_t stream) {
   const int nb = (int)route_blocks(slots);
   if (nb > 0) {
-    hipLaunchKernelGGL(route_count_kernel, dim3(nb), dim3(kRouteThreads), 0, stream, expert, slots, E, hist);
-    hipError_t e = hipGetLastError();
+    const hipError_t e = launch_kernel(route_count_kernel, dim3(nb), dim3(kRouteThreads), stream, expert, slots,
+                                       E, hist);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, stream, hist, nb, E, align,
-                     pad_empty ? 1 : 0, offs, row_slot);
-  hipError_t e = hipGetLastError();
+  const hipError_t e = launch_kernel(route_scan_kernel, dim3(1), dim3(1024), stream, hist, nb, E, align,
+                                     pad_empty ? 1 : 0, offs, row_slot);
   if (e != hipSuccess || nb == 0) return e;
-  hipLaunchKernelGGL(route_place_kernel, dim3(nb), dim3(kRouteThreads), 0, stream, expert, slots, E, hist,
-                     row_slot, slot_row);
-  return hipGetLastError();
+  return launch_kernel(route_place_kernel, dim3(nb), dim3(kRouteThreads), stream, expert, slots, E, hist,
+                       row_slot, slot_row);
 }
 
 hipError_t launch_gather_rows(const void* src, int64_t row_bytes, const int32_t* row_slot, int32_t topk,
                               const int32_t* offs, int32_t E, int64_t rows_cap, int64_t tokens, void* dst,
                               int num_cus, hipStream_t stream) {
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(grid_for(rows_cap * (row_bytes / 16), num_cus)), dim3(256), 0,
-                     stream, static_cast<const uint8_t*>(src), row_bytes, row_slot, topk, offs, E, rows_cap,
-                     tokens, static_cast<uint8_t*>(dst));
-  return hipGetLastError();
+  return launch_kernel(gather_rows_kernel, dim3(grid_for(rows_cap * (row_bytes / 16), num_cus)), dim3(256),
+                       stream, static_cast<const uint8_t*>(src), row_bytes, row_slot, topk, offs, E, rows_cap,
+                       tokens, static_cast<uint8_t*>(dst));
 }
 
 hipError_t launch_combine_rows(const void* y, int64_t n, const int32_t* slot_row, const float* w, int32_t topk,
@@ -316,12 +321,10 @@ hipError_t launch_combine_rows(const void* y, int64_t n, const int32_t* slot_row
                                hipStream_t stream) {
   const int grid = grid_for(tokens * (n / 8), num_cus);
   if (out_f32)
-    hipLaunchKernelGGL(combine_rows_kernel<true>, dim3(grid), dim3(256), 0, stream,
+    return launch_kernel(combine_rows_kernel<true>, dim3(grid), dim3(256), stream,
+                         static_cast<const uint16_t*>(y), n, slot_row, w, topk, tokens, rows_cap, out);
+  return launch_kernel(combine_rows_kernel<false>, dim3(grid), dim3(256), stream,
                        static_cast<const uint16_t*>(y), n, slot_row, w, topk, tokens, rows_cap, out);
-  else
-    hipLaunchKernelGGL(combine_rows_kernel<false>, dim3(grid), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(y), n, slot_row, w, topk, tokens, rows_cap, out);
-  return hipGetLastError();
 }
 
 }  // namespace gg

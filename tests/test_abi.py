@@ -236,6 +236,8 @@ def test_route_sizes(lib):
 @pytest.mark.parametrize("case,status", [
     (dict(ids=0), 1), (dict(offs=0), 1), (dict(ws=0), 1), (dict(e=0), 5), (dict(align=0), 2),
     (dict(align=5000), 2), (dict(cap=90), 2), (dict(slots=-1), 2), (dict(ws=A + 8), 3), (dict(offs=A + 2), 3),
+    # the rows it may produce must be acceptable to the GEMMs: below 2^31 - 2^16
+    (dict(slots=(1 << 31) - (1 << 16) - 4 * 8, cap=1 << 31), 2),
 ])
 def test_route_checks_arguments(lib, case, status):
     v = dict(ids=A, slots=64, e=4, align=8, pad=1, offs=A + 0x100, rs=A + 0x200, cap=64 + 32, sr=A + 0x300,
@@ -247,7 +249,8 @@ def test_route_checks_arguments(lib, case, status):
 
 
 @pytest.mark.parametrize("case,status", [
-    (dict(src=0), 1), (dict(rb=24), 2), (dict(topk=0), 2), (dict(src=A + 8), 3), (dict(e=0), 5)])
+    (dict(src=0), 1), (dict(rb=24), 2), (dict(topk=0), 2), (dict(src=A + 8), 3), (dict(e=0), 5),
+    (dict(cap=(1 << 31) - (1 << 16)), 2), (dict(tokens=1 << 30), 2)])
 def test_gather_checks_arguments(lib, case, status):
     v = dict(src=A, tokens=10, rb=32, rs=A + 0x100, topk=2, offs=A + 0x200, e=4, cap=40, dst=A + 0x300, s=0)
     v.update(case)
@@ -257,7 +260,8 @@ def test_gather_checks_arguments(lib, case, status):
 
 
 @pytest.mark.parametrize("case,status", [
-    (dict(y=0), 1), (dict(n=12), 2), (dict(topk=0), 2), (dict(out=A + 4), 3), (dict(dt=3), 4)])
+    (dict(y=0), 1), (dict(n=12), 2), (dict(topk=0), 2), (dict(out=A + 4), 3), (dict(dt=3), 4),
+    (dict(cap=(1 << 31) - (1 << 16)), 2), (dict(tokens=1 << 30), 2)])
 def test_combine_checks_arguments(lib, case, status):
     v = dict(y=A, n=64, sr=A + 0x100, w=A + 0x200, topk=2, tokens=10, cap=40, out=A + 0x300, dt=0, s=0)
     v.update(case)

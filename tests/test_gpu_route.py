@@ -133,3 +133,20 @@ def test_routed_layer_end_to_end():
     check(yb, ref.value, ref.sabs, k, "routed forward")
     cref = oracle.combine_rows(yb, rs, topk, probs.cpu().numpy())
     check(synth.bf16_bits(out), cref.value, cref.sabs, topk, "routed combine")
+
+
+def test_offsets_from_splits_saturate_at_the_row_limit():
+    """Counts whose running sum passes 2^31 - 2^16 (the GEMMs' row limit)
+    give offsets saturated there, never int32 wrap-around: the oracle's sums
+    capped at the limit, bit for bit, and still monotone."""
+    dev = device()
+    import torch
+    cap = (1 << 31) - (1 << 16)
+    splits = np.array([5, 1 << 30, (1 << 30) - 7, 1 << 20, 3, 1 << 40, 0, 9], dtype=np.int64)
+    say("offsets_from_splits saturation")
+    got = gg.offsets_from_splits(torch.from_numpy(splits).to(dev), 8, True)
+    torch.cuda.synchronize()
+    want = np.minimum(oracle.offsets_from_splits(splits, 8, True), cap)
+    g = got.cpu().numpy().astype(np.int64)
+    assert g.tolist() == want.tolist()
+    assert np.all(np.diff(g) >= 0)

@@ -4,7 +4,9 @@ offsets of PyTorch issue #152668's reproduction), and invariants on random
 routings -- every kept slot lands on exactly one row, an expert's rows hold
 its slots in ascending order then padding, sizes are padded as defined, the
 offsets equal offsets_from_splits of the counts, and gather followed by an
-unweighted topk = 1 combine returns the input."""
+unweighted topk = 1 combine returns the input.  The gather and the weighted
+combine at topk = 2 and 3, with dropped slots and padding rows, are pinned by
+hand-worked values (tests/golden/gather_hand.json)."""
 import json
 import os
 
@@ -82,3 +84,60 @@ def test_combine_weighted_brute_force():
     yd = oracle.decode_bf16(y)
     want = np.stack([0.5 * yd[0] + 2.0 * yd[3], -1.0 * yd[5], 0.25 * yd[2] + 0.25 * yd[2]])
     assert np.array_equal(r.value, want)
+
+
+# ---- gather and combine at topk > 1 (hand-worked) --------------------------------
+# A row's token is its slot // topk; a mapping by the slot itself, or by
+# slot % topk, gathers other rows (or runs off the source) and fails these.
+
+GATHER_GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "gather_hand.json")
+
+
+def gather_cases():
+    with open(GATHER_GOLDEN) as f:
+        return json.load(f)["cases"]
+
+
+def _bits(v):
+    return (np.asarray(v, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("i", range(3))
+def test_gather_hand_worked(i):
+    c = gather_cases()[i]
+    offs, row_slot, slot_row = oracle.route(c["expert_of_slot"], c["num_groups"], c["align"], c["pad_empty"])
+    assert offs.tolist() == c["offs"]
+    assert row_slot.tolist() == c["row_slot"]
+    assert slot_row.tolist() == c["slot_row"]
+    got = oracle.gather_rows(_bits(c["src"]), row_slot, c["topk"])
+    assert np.array_equal(got, _bits(c["gathered"]))
+
+
+@pytest.mark.parametrize("i", range(3))
+def test_combine_hand_worked(i):
+    c = gather_cases()[i]
+    r = oracle.combine_rows(_bits(c["gathered"]), np.array(c["slot_row"]), c["topk"],
+                            np.array(c["weights"], dtype=np.float32))
+    assert np.array_equal(r.value, np.array(c["combined"], dtype=np.float64))
+
+
+@pytest.mark.parametrize("seed,topk", [(11, 2), (12, 3), (13, 8)])
+def test_gather_brute_force_distinct_tokens(seed, topk):
+    """Every token row is distinct (its first column holds the token index),
+    so each gathered row names the token it came from: that must be the
+    slot's token for kept slots, and the row is zero for padding."""
+    rng = np.random.default_rng(seed)
+    tokens, e = 37, 5
+    ids = rng.integers(-1, e + 1, size=(tokens, topk))
+    src = np.zeros((tokens, 4), dtype=np.float32)
+    src[:, 0] = np.arange(tokens) + 1
+    src[:, 1:] = rng.standard_normal((tokens, 3))
+    offs, row_slot, slot_row = oracle.route(ids, e, 4, True)
+    g = oracle.gather_rows(_bits(src), row_slot, topk)
+    back = oracle.decode_bf16(g)
+    for r, s in enumerate(row_slot):
+        if s < 0:
+            assert np.all(g[r] == 0)
+        else:
+            assert back[r, 0] == s // topk + 1
+            assert np.array_equal(g[r], _bits(src[s // topk]))
