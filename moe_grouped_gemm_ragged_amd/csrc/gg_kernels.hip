@@ -482,6 +482,247 @@ __device__ __attribute__((always_inline)) inline void mainloop(
 #undef GG_STAGE
 }
 
+// ---- ping-pong main loop -----------------------------------------------------------
+#ifndef GG_PP_PRIO
+#define GG_PP_PRIO 0
+#endif
+#if GG_PP_PRIO
+#define GG_PP_PRIO_UP __builtin_amdgcn_s_setprio(1);
+#define GG_PP_PRIO_DOWN __builtin_amdgcn_s_setprio(0);
+#else
+#define GG_PP_PRIO_UP
+#define GG_PP_PRIO_DOWN
+#endif
+//
+// The two waves of each SIMD take turns: while one issues a stage's 16
+// MFMAs back to back from fragments already in its registers, the other
+// reads its fragments of the stage it computes next and issues its share of
+// the global->LDS loads.  A load that cannot issue yet, or an LDS read still
+// in flight, then holds up only the wave that is not computing, and the
+// matrix core sees one uninterrupted MFMA stream after another.  Group g =
+// wm (waves 4 g .. 4 g + 3, one per SIMD) owns tile rows 128 g .. (64 g ..
+// for a half-height tile), as in the interleaved loop.
+//
+// Steps alternate: in step 2s group 0 computes stage s while group 1 reads
+// stage s and loads B of stage s + 3; in step 2s + 1 group 1 computes stage
+// s while group 0 reads stage s + 1 and loads A of stage s + 4.  Each step
+// ends at a barrier.  Stage s lives in slot s mod 4 (one stage per slot for
+// both operands); it is read in steps 2s - 1 and 2s, so its slot is free for
+// stage s + 4 from step 2s + 1 on (A) and B of stage s + 3 goes into the
+// slot of stage s - 1, free since step 2s - 1.  Group 0 issues every A load
+// (4 per wave per odd step), group 1 every B load (4 per wave per even
+// step); stage s + 1 must have landed at the barrier that ends step 2s, where
+// each wave has at most the 8 loads of the two later stages in flight.
+//
+// A group's 4 loads per step fill its wave's 4 KB of the operand's 16 KB
+// stage tile (wave w of the group: LDS bytes [4096 w, +4096)), the same
+// placement the interleaved loop's 2 loads per wave of all 8 waves produce.
+
+// Lane offset of the group's load 0 for its wave w (0..3) of a group; load
+// jj (0..3) adds jj * step.  Equal to dma_ctx for virtual wave 2 w + jj / 2,
+// load jj mod 2.
+template <bool STRIDED, bool WIDE = false>
+__device__ __forceinline__ DmaCtx dma_ctx_grp(const Operand& op, int q0, int lane_in, int w) {
+  DmaCtx c;
+  const int lane = (int)opaque_v((uint32_t)lane_in);
+  if constexpr (STRIDED) {
+    const int left = op.red - q0;
+    int last = left - 1;
+    if constexpr (WIDE) last = last < 63 ? last : 63;
+    const uint32_t nrec = left > 0 ? (uint32_t)last * op.ld_bytes + op.row_tail : 0u;
+    c.rs = make_rsrc(op.origin + (int64_t)q0 * op.ld_bytes, nrec);
+    const int chunk = (lane & 7) ^ (4 * ((lane >> 4) & 1));
+    c.voff = (uint32_t)(lane >> 3) * op.ld_bytes + (uint32_t)(128 * w + 16 * chunk) + (w >= 2 ? op.split : 0u);
+    c.step = 8u * op.ld_bytes;
+  } else {
+    const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - (uint32_t)(2 * q0) : 0u;
+    c.rs = make_rsrc(op.origin + (int64_t)2 * q0, nrec);
+    const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
+    uint32_t v = (uint32_t)(64 * w + (lane >> 2)) * op.ld_bytes + 16u * (uint32_t)chunk;
+    if (q0 + 8 * chunk >= op.red) v = kOutOfRange;
+    c.voff = v;
+    c.step = 16u * op.ld_bytes;
+  }
+  return c;
+}
+
+// (The row step goes through a scalar register: it is uniform, but where the
+// two groups' code paths merge the compiler can lose track of that and wrap
+// the load in a loop over its distinct values.)
+__device__ __forceinline__ void dma_load_grp(const DmaCtx& c, uint8_t* lds_op, int w, int jj) {
+  const uint32_t wbase = opaque_s((uint32_t)uniform(w * 4096));
+  const uint32_t soff = (uint32_t)uniform((int)(jj * c.step));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, LDS_PTR(lds_op + wbase + 1024 * jj), 16, c.voff, soff, 0, 0);
+}
+
+// The loads in flight when a tile's ping-pong loop starts: group 0 A of
+// stages 0..3, group 1 B of stages 0..2 (16 and 12 per wave).
+template <bool A_STRIDED, bool B_STRIDED, bool WIDE = false>
+__device__ __attribute__((always_inline)) inline void prologue_loads_pp(
+    uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
+    uint8_t* __restrict__ s3, const uint8_t* __restrict__ a_origin,
+    const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid, int wave) {
+  A.origin = a_origin;
+  B.origin = b_origin;
+  const int lane = tid & 63;
+  const int w = wave & 3;
+  if (wave < 4) {
+#define GG_PP_PRO(S, BUF)                                                   \
+    {                                                                       \
+      const DmaCtx c = dma_ctx_grp<A_STRIDED, WIDE>(A, (S) * BK, lane, w); \
+      _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) dma_load_grp(c, (BUF), w, jj); \
+    }
+    GG_PP_PRO(0, s0) GG_PP_PRO(1, s1) GG_PP_PRO(2, s2) GG_PP_PRO(3, s3)
+#undef GG_PP_PRO
+  } else {
+#define GG_PP_PRO(S, BUF)                                                   \
+    {                                                                       \
+      const DmaCtx c = dma_ctx_grp<B_STRIDED, WIDE>(B, (S) * BK, lane, w); \
+      _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) dma_load_grp(c, (BUF) + OP_BYTES, w, jj); \
+    }
+    GG_PP_PRO(0, s0) GG_PP_PRO(1, s1) GG_PP_PRO(2, s2)
+#undef GG_PP_PRO
+  }
+}
+
+// Barriers of the ping-pong loops.  The stage buffers are restrict-qualified
+// (so that an LDS read need not wait for global->LDS loads into other
+// buffers), but here a group reads regions that only the other group's waves
+// write.  Seen from one wave, nothing in its own code writes them, and once
+// the loop is inlined the compiler takes a barrier (an asm statement) not to
+// touch restrict memory whose pointer has not escaped before it, so it would
+// be free to reuse a fragment read across iterations.  pp_regions_escape,
+// called once at the top of each ping-pong loop, lets every region pointer
+// escape into an (empty) asm statement; every later barrier then counts as
+// reading and writing them, and no LDS access moves across it.
+struct Regions {
+  const void* p[8];
+};
+
+__device__ __forceinline__ void pp_regions_escape(const Regions& r) {
+  asm volatile("" ::"s"((uint32_t)(uintptr_t)r.p[0]), "s"((uint32_t)(uintptr_t)r.p[1]),
+               "s"((uint32_t)(uintptr_t)r.p[2]), "s"((uint32_t)(uintptr_t)r.p[3]),
+               "s"((uint32_t)(uintptr_t)r.p[4]), "s"((uint32_t)(uintptr_t)r.p[5]),
+               "s"((uint32_t)(uintptr_t)r.p[6]), "s"((uint32_t)(uintptr_t)r.p[7])
+               : "memory");
+}
+
+// s_waitcnt vmcnt(N) expcnt(7) lgkmcnt(0) (N < 64 a count of this wave's
+// loads, 64 no wait on loads), then barrier.
+template <int N>
+__device__ __forceinline__ void pp_sync(const Regions&) {
+  if constexpr (N < 64) __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+  else __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("s_barrier" ::: "memory");
+}
+constexpr int kNoVm = 64;
+
+// prev_stores: fp32 stores of the previous tile issued after this tile's
+// prologue loads (they complete before those loads in the count).
+template <bool A_STRIDED, bool B_STRIDED, int TMA, bool WIDE = false>
+__device__ __attribute__((always_inline)) inline void mainloop_pp(
+    uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
+    uint8_t* __restrict__ s3, const uint8_t* __restrict__ a_origin,
+    const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid, int wave,
+    const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[TM][TN], int prev_stores) {
+  A.origin = a_origin;
+  B.origin = b_origin;
+  const int nk = (A.red + BK - 1) / BK;
+  if (nk <= 0) return;
+  const int lane = tid & 63;
+  const int w = wave & 3;
+  const bool g0 = wave < 4;
+  const Regions rg = {{s0, s1, s2, s3, s0 + OP_BYTES, s1 + OP_BYTES, s2 + OP_BYTES, s3 + OP_BYTES}};
+  pp_regions_escape(rg);
+  Frags f0, f1;     // sub-steps 0 and 1 of the stage this wave computes next
+  // stage 0 landed: group 0 leaves A of stages 1..3 in flight, group 1 B of
+  // stages 1, 2 (plus, after a direct fp32 epilogue, the previous tile's
+  // stores, which were issued after these loads)
+  if (prev_stores == stores_f32<TM>()) {
+    if (g0) pp_sync<12 + stores_f32<TM>()>(rg); else pp_sync<8 + stores_f32<TM>()>(rg);
+  } else if (prev_stores == stores_f32<2>()) {
+    if (g0) pp_sync<12 + stores_f32<2>()>(rg); else pp_sync<8 + stores_f32<2>()>(rg);
+  } else {
+    if (g0) pp_sync<12>(rg); else pp_sync<8>(rg);
+  }
+  if (g0) {
+    read_stage_frags<A_STRIDED, B_STRIDED, TMA>(s0, s0 + OP_BYTES, faa, fab, 0, f0);
+    read_stage_frags<A_STRIDED, B_STRIDED, TMA>(s0, s0 + OP_BYTES, faa, fab, 1, f1);
+  }
+
+#define GG_PP_MFMA()                                                                              \
+  {                                                                                               \
+    GG_PP_PRIO_UP                                                                                 \
+    _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                        \
+      const int i = q / TN, j = q % TN;                                                           \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.b[j], f0.a[i], acc[i][j], 0, 0, 0); \
+    }                                                                                             \
+    _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                        \
+      const int i = q / TN, j = q % TN;                                                           \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0); \
+    }                                                                                             \
+    mfma_fence(acc);                                                                              \
+    GG_PP_PRIO_DOWN                                                                               \
+  }
+#define GG_PP_READ(BUF)                                                                           \
+  {                                                                                               \
+    read_stage_frags<A_STRIDED, B_STRIDED, TMA>(BUF, (BUF) + OP_BYTES, faa, fab, 0, f0);         \
+    read_stage_frags<A_STRIDED, B_STRIDED, TMA>(BUF, (BUF) + OP_BYTES, faa, fab, 1, f1);         \
+  }
+  // Each group runs its own loop (every wave meets the same barriers in the
+  // same order: one after each step).  BC: the slot of stage KT; BN: of
+  // KT + 1; BP: of KT - 1 (= KT + 3 mod 4).
+  if (g0) {
+#define GG_PP_STAGE0(BC, BN, BP, KT)                                                              \
+  {                                                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    GG_PP_MFMA()                                     /* step 2 KT: compute stage KT */            \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    pp_sync<8>(rg);                           /* stage KT + 1 landed */                    \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    if ((KT) + 1 < nk) GG_PP_READ(BN)                /* step 2 KT + 1: read stage KT + 1 */       \
+    {                                                                                             \
+      const DmaCtx ca = dma_ctx_grp<A_STRIDED, WIDE>(A, ((KT) + 4) * BK, lane, w);               \
+      _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) dma_load_grp(ca, BC, w, jj);               \
+    }                                                                                             \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    pp_sync<kNoVm>(rg);                                   /* fragments in registers */                 \
+  }
+    for (int kt = 0; kt < nk; kt += 4) {
+      GG_PP_STAGE0(s0, s1, s3, kt)
+      if (kt + 1 < nk) GG_PP_STAGE0(s1, s2, s0, kt + 1)
+      if (kt + 2 < nk) GG_PP_STAGE0(s2, s3, s1, kt + 2)
+      if (kt + 3 < nk) GG_PP_STAGE0(s3, s0, s2, kt + 3)
+    }
+#undef GG_PP_STAGE0
+  } else {
+#define GG_PP_STAGE1(BC, BN, BP, KT)                                                              \
+  {                                                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    GG_PP_READ(BC)                                   /* step 2 KT: read stage KT */               \
+    {                                                                                             \
+      const DmaCtx cb = dma_ctx_grp<B_STRIDED, WIDE>(B, ((KT) + 3) * BK, lane, w);               \
+      _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) dma_load_grp(cb, (BP) + OP_BYTES, w, jj);  \
+    }                                                                                             \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    pp_sync<8>(rg);                           /* stage KT + 1 landed */                    \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    GG_PP_MFMA()                                     /* step 2 KT + 1: compute stage KT */        \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    pp_sync<kNoVm>(rg);                                                                                \
+  }
+    for (int kt = 0; kt < nk; kt += 4) {
+      GG_PP_STAGE1(s0, s1, s3, kt)
+      if (kt + 1 < nk) GG_PP_STAGE1(s1, s2, s0, kt + 1)
+      if (kt + 2 < nk) GG_PP_STAGE1(s2, s3, s1, kt + 2)
+      if (kt + 3 < nk) GG_PP_STAGE1(s3, s0, s2, kt + 3)
+    }
+#undef GG_PP_STAGE1
+  }
+#undef GG_PP_READ
+#undef GG_PP_MFMA
+}
+
 // ---- full-line staging of reduction-contiguous operands (bf16 row passes) ----------
 //
 // One stage of a reduction-contiguous operand is 64 bytes per tile row: half
@@ -540,6 +781,16 @@ __device__ __forceinline__ void dma_load_pair(const DmaPair& c, uint8_t* region,
   const uint32_t wbase = opaque_s((uint32_t)uniform((wave & 3) * 4096));
   __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, LDS_PTR(region + wbase + 1024 * jj), 16,
                                            (jj & 1) ? c.voff1 : c.voff0, jj * c.step, 0, 0);
+}
+
+// dma_load_pair with its row step moved to a scalar register: the value is
+// uniform, but where the two groups' code paths merge the compiler can lose
+// track of that and wrap the load in a loop over its distinct values.
+__device__ __forceinline__ void dma_load_pair_s(const DmaPair& c, uint8_t* region, int wave, int jj) {
+  const uint32_t wbase = opaque_s((uint32_t)uniform((wave & 3) * 4096));
+  const uint32_t soff = (uint32_t)uniform((int)(jj * c.step));
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, LDS_PTR(region + wbase + 1024 * jj), 16,
+                                           (jj & 1) ? c.voff1 : c.voff0, soff, 0, 0);
 }
 
 // Fragment addresses in the pair layout for a wave slice starting at tile
@@ -701,6 +952,223 @@ __device__ __attribute__((always_inline)) inline void mainloop_pair(
 #undef GG_RA
 #undef GG_PA
 #undef GG_RB
+}
+
+// ---- ping-pong main loop with A in the pair layout (bf16 row passes) ----------------
+#ifndef GG_PP_LOADFIRST
+#define GG_PP_LOADFIRST 0
+#endif
+#ifndef GG_PP2_SAFE
+#define GG_PP2_SAFE 0
+#endif
+#if GG_PP2_SAFE
+#define GG_PP2_WAIT4(R) pp_sync<0>(R)
+#define GG_PP2_WAITL(R) pp_sync<0>(R)
+#else
+#define GG_PP2_WAIT4(R) pp_sync<4>(R)
+#define GG_PP2_WAITL(R) pp_sync<kNoVm>(R)
+#endif
+//
+// The ping-pong schedule above, with the reduction-contiguous A operand
+// staged two stages at a time in the pair layout (whole cache lines), B one
+// stage per slot.  Group g's rows of A pair p (stages 2p, 2p + 1) sit in the
+// A region of slot (2p + g) mod 4, and group g loads them itself (the pair
+// loads of its waves); B of a stage is loaded by one group's 4 waves.  Over
+// each pair of stages s = 2j, 2j + 1 (steps 4j .. 4j + 3):
+//   step 4j     group 0 computes stage 2j;     group 1 reads stage 2j and
+//               loads its half of A pair j + 1
+//   step 4j + 1 group 1 computes stage 2j;     group 0 reads stage 2j + 1 and
+//               loads B of stage 2j + 4
+//   step 4j + 2 group 0 computes stage 2j + 1; group 1 reads stage 2j + 1
+//               and loads B of stage 2j + 3
+//   step 4j + 3 group 1 computes stage 2j + 1; group 0 reads stage 2j + 2
+//               and loads its half of A pair j + 2
+// Every load goes into a region whose earlier contents were last read at
+// least one barrier before, and lands 3 to 6 steps later; the barrier that
+// precedes its first reader waits for it (vmcnt(4): the group's one later
+// batch of 4 may still be in flight).  For a half-height tile every wave's
+// rows lie in group 0's region (ha = 0); group 1's pair loads then read only
+// rows past the tile, which land as zeros and are never read.
+
+// Loads in flight when the loop starts, in this order: group 0 B of stage 0,
+// its half of A pair 0, B of stage 2, its half of A pair 1; group 1 its half
+// of A pair 0, B of stage 1.
+template <bool B_STRIDED>
+__device__ __attribute__((always_inline)) inline void prologue_loads_pp_pair(
+    uint8_t* __restrict__ a0, uint8_t* __restrict__ a1, uint8_t* __restrict__ a2, uint8_t* __restrict__ a3,
+    uint8_t* __restrict__ b0, uint8_t* __restrict__ b1, uint8_t* __restrict__ b2,
+    const uint8_t* __restrict__ a_origin, const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid,
+    int wave) {
+  A.origin = a_origin;
+  B.origin = b_origin;
+  const int lane = tid & 63;
+  const int w = wave & 3;
+  if (wave < 4) {
+    {
+      const DmaCtx c = dma_ctx_grp<B_STRIDED>(B, 0, lane, w);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dma_load_grp(c, b0, w, jj);
+    }
+    {
+      const DmaPair c = dma_pair(A, 0, tid);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dma_load_pair_s(c, a0, wave, jj);
+    }
+    {
+      const DmaCtx c = dma_ctx_grp<B_STRIDED>(B, 2 * BK, lane, w);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dma_load_grp(c, b2, w, jj);
+    }
+    {
+      const DmaPair c = dma_pair(A, 2 * BK, tid);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dma_load_pair_s(c, a2, wave, jj);
+    }
+  } else {
+    {
+      const DmaPair c = dma_pair(A, 0, tid);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dma_load_pair_s(c, a1, wave, jj);
+    }
+    {
+      const DmaCtx c = dma_ctx_grp<B_STRIDED>(B, BK, lane, w);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dma_load_grp(c, b1, w, jj);
+    }
+  }
+}
+
+template <bool B_STRIDED, int TMA>
+__device__ __attribute__((always_inline)) inline void mainloop_pp_pair(
+    uint8_t* __restrict__ a0, uint8_t* __restrict__ a1, uint8_t* __restrict__ a2, uint8_t* __restrict__ a3,
+    uint8_t* __restrict__ b0, uint8_t* __restrict__ b1, uint8_t* __restrict__ b2, uint8_t* __restrict__ b3,
+    const uint8_t* __restrict__ a_origin, const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid,
+    int wave, int ha, const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[TM][TN],
+    int prev_stores) {
+  A.origin = a_origin;
+  B.origin = b_origin;
+  const int nk = (A.red + BK - 1) / BK;
+  if (nk <= 0) return;
+  const int lane = tid & 63;
+  const int w = wave & 3;
+  const bool g0 = wave < 4;
+  const Regions rg = {{a0, a1, a2, a3, b0, b1, b2, b3}};
+  pp_regions_escape(rg);
+  Frags f0, f1;
+  // group 0: B of stage 0 and its half of A pair 0 landed (its other 8 loads
+  // and the previous tile's direct stores, issued after them, may be in
+  // flight); group 1 waits at the next barrier
+  if (prev_stores == stores_f32<TM>()) {
+    if (g0) pp_sync<8 + stores_f32<TM>()>(rg); else GG_PP2_WAITL(rg);
+  } else if (prev_stores == stores_f32<2>()) {
+    if (g0) pp_sync<8 + stores_f32<2>()>(rg); else GG_PP2_WAITL(rg);
+  } else {
+    if (g0) pp_sync<8>(rg); else GG_PP2_WAITL(rg);
+  }
+
+#define GG_RA(U) ((U) < 2 ? (ha ? a1 : a0) : (ha ? a3 : a2))
+#define GG_RB(U) ((U) == 0 ? b0 : (U) == 1 ? b1 : (U) == 2 ? b2 : b3)
+#define GG_PP_READ(U)                                                                             \
+  {                                                                                               \
+    _Pragma("unroll") for (int i = 0; i < TMA; ++i) f0.a[i] = read_frag_pair(GG_RA(U), faa, 0, i, (U) & 1); \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) f0.b[j] = read_frag<B_STRIDED>(GG_RB(U), fab, 0, j);    \
+    _Pragma("unroll") for (int i = 0; i < TMA; ++i) f1.a[i] = read_frag_pair(GG_RA(U), faa, 1, i, (U) & 1); \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) f1.b[j] = read_frag<B_STRIDED>(GG_RB(U), fab, 1, j);    \
+  }
+#define GG_PP_MFMA()                                                                              \
+  {                                                                                               \
+    GG_PP_PRIO_UP                                                                                 \
+    _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                        \
+      const int i = q / TN, j = q % TN;                                                           \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.b[j], f0.a[i], acc[i][j], 0, 0, 0); \
+    }                                                                                             \
+    _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                        \
+      const int i = q / TN, j = q % TN;                                                           \
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0); \
+    }                                                                                             \
+    mfma_fence(acc);                                                                              \
+    GG_PP_PRIO_DOWN                                                                               \
+  }
+// B of stage Q into slot U (one group's 4 waves)
+#define GG_PP_LOAD_B(U, Q)                                                                        \
+  {                                                                                               \
+    const DmaCtx cb = dma_ctx_grp<B_STRIDED>(B, (Q) * BK, lane, w);                               \
+    _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) dma_load_grp(cb, GG_RB(U), w, jj);            \
+  }
+// this wave's rows of the A pair whose first stage is Q, into region R
+#define GG_PP_LOAD_A(R, Q)                                                                        \
+  {                                                                                               \
+    const DmaPair cp = dma_pair(A, (Q) * BK, tid);                                                \
+    _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) dma_load_pair_s(cp, (R), wave, jj);          \
+  }
+
+  if (g0) {
+    // step -1: read stage 0
+    GG_PP_READ(0)
+    __builtin_amdgcn_sched_barrier(0);
+    GG_PP2_WAITL(rg);
+    // stage KT = kt + U: compute it, then read stage KT + 1 and load (U even)
+    // B of stage KT + 4 into slot U or (U odd) this group's half of the A
+    // pair of stages KT + 3, KT + 4 into slot (U + 3) mod 4
+#define GG_PP_STAGE0(U, KT)                                                                       \
+  {                                                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    GG_PP_MFMA()                                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    if ((U) & 1) GG_PP2_WAIT4(rg); else GG_PP2_WAITL(rg);                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    if (!GG_PP_LOADFIRST && (KT) + 1 < nk) GG_PP_READ(((U) + 1) & 3)                              \
+    if (((U) & 1) == 0) GG_PP_LOAD_B(U, (KT) + 4)                                                 \
+    else GG_PP_LOAD_A((U) == 1 ? a0 : a2, (KT) + 3)                                               \
+    if (GG_PP_LOADFIRST && (KT) + 1 < nk) GG_PP_READ(((U) + 1) & 3)                               \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    GG_PP2_WAITL(rg);                                                                                \
+  }
+    for (int kt = 0; kt < nk; kt += 4) {
+      GG_PP_STAGE0(0, kt)
+      if (kt + 1 < nk) GG_PP_STAGE0(1, kt + 1)
+      if (kt + 2 < nk) GG_PP_STAGE0(2, kt + 2)
+      if (kt + 3 < nk) GG_PP_STAGE0(3, kt + 3)
+    }
+#undef GG_PP_STAGE0
+  } else {
+    // step -1: this group's half of A pair 0 landed (B of stage 1 may be in
+    // flight, and the previous tile's direct stores after it)
+    __builtin_amdgcn_sched_barrier(0);
+    if (prev_stores == stores_f32<TM>()) pp_sync<4 + stores_f32<TM>()>(rg);
+    else if (prev_stores == stores_f32<2>()) pp_sync<4 + stores_f32<2>()>(rg);
+    else GG_PP2_WAIT4(rg);
+    // stage KT = kt + U: read it and load (U even) this group's half of the A
+    // pair of stages KT + 2, KT + 3 into slot (U + 3) mod 4 or (U odd) B of
+    // stage KT + 2 into slot (U + 2) mod 4; then compute it
+#define GG_PP_STAGE1(U, KT)                                                                       \
+  {                                                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    if (!GG_PP_LOADFIRST) GG_PP_READ(U)                                                           \
+    if (((U) & 1) == 0) GG_PP_LOAD_A((U) == 0 ? a3 : a1, (KT) + 2)                                \
+    else GG_PP_LOAD_B(((U) + 2) & 3, (KT) + 2)                                                    \
+    if (GG_PP_LOADFIRST) GG_PP_READ(U)                                                            \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    if (((U) & 1) == 0) GG_PP2_WAIT4(rg); else GG_PP2_WAITL(rg);                               \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    GG_PP_MFMA()                                                                                  \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    if ((U) & 1) GG_PP2_WAIT4(rg); else GG_PP2_WAITL(rg);                                      \
+  }
+    for (int kt = 0; kt < nk; kt += 4) {
+      GG_PP_STAGE1(0, kt)
+      if (kt + 1 < nk) GG_PP_STAGE1(1, kt + 1)
+      if (kt + 2 < nk) GG_PP_STAGE1(2, kt + 2)
+      if (kt + 3 < nk) GG_PP_STAGE1(3, kt + 3)
+    }
+#undef GG_PP_STAGE1
+  }
+#undef GG_PP_LOAD_A
+#undef GG_PP_LOAD_B
+#undef GG_PP_MFMA
+#undef GG_PP_READ
+#undef GG_RB
+#undef GG_RA
 }
 
 // ---- fp8 (e4m3) block-scaled main loop ----------------------------------------------
@@ -1354,13 +1822,21 @@ struct Tile {
 // host picks it for wgrad on short experts; see launch()).  WIDE (wgrad
 // only): an expert's rows may span 4 GB or more of X or dY, so the load
 // ranges are capped per stage (see dma_ctx); the host picks it from m.
+#ifndef GG_PINGPONG
+#define GG_PINGPONG 2
+#endif
+
 template <int MODE, bool OUT_F32, bool STAGED_F32 = false, bool WIDE = false>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   static_assert(!WIDE || is_wgrad(MODE), "only wgrad reads an operand down a data-dependent span");
   constexpr bool A_STRIDED = is_wgrad(MODE);
   constexpr bool B_STRIDED = !is_dgrad(MODE) && !is_fp8(MODE);
+  // bf16 passes on the ping-pong main loop (one stage per slot)
+  constexpr bool PP = GG_PINGPONG >= 1 && !is_fp8(MODE);
+  // ... the row passes with A in the pair layout
+  constexpr bool PP_PAIR = GG_PINGPONG >= 2 && PP && !is_wgrad(MODE);
   // bf16 row passes: reduction-contiguous operands in the stage-pair layout
-  constexpr bool PAIRED = !is_wgrad(MODE) && !is_fp8(MODE);
+  constexpr bool PAIRED = !PP && !is_wgrad(MODE) && !is_fp8(MODE);
 
   // LDS: NSTAGE stage buffers of 32 KB (A tile, then B tile); fp8: two
   // k-blocks of scales.
@@ -1405,7 +1881,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   const uint8_t* pb = reinterpret_cast<const uint8_t*>(p.b);
   uint8_t* pc = reinterpret_cast<uint8_t*>(p.c);
   // A in the pair layout for the row passes (bf16 and fp8), one stage per slot for wgrad
-  constexpr bool A_PAIRED = !is_wgrad(MODE);
+  constexpr bool A_PAIRED = !is_wgrad(MODE) && (!PP || PP_PAIR);
   const FragAddr faa = A_PAIRED ? frag_addr_pair(128 * wm, lane) : frag_addr<A_STRIDED>(128 * wm, lane);
   // half-height tiles
   const FragAddr faa_half = A_PAIRED ? frag_addr_pair(64 * wm, lane) : frag_addr<A_STRIDED>(64 * wm, lane);
@@ -1552,6 +2028,13 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
       if constexpr (is_fp8(MODE))
         prologue_loads8(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES, s_sc, T.A.origin,
                         T.B.origin, T.sa, T.sb, (uint32_t)(p.k / 128 * 256), T.A, T.B, tid, wave);
+      else if constexpr (PP_PAIR)
+        prologue_loads_pp_pair<B_STRIDED>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
+                                          T.A.origin, T.B.origin, T.A, T.B, tid, wave);
+      else if constexpr (PP)
+        prologue_loads_pp<A_STRIDED, B_STRIDED, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
+                                                      smem + 3 * STAGE_BYTES, T.A.origin, T.B.origin, T.A,
+                                                      T.B, tid, wave);
       else if constexpr (PAIRED)
         prologue_loads_pair<B_STRIDED>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
                                        sa3 + OP_BYTES, T.A.origin, T.B.origin, T.A, T.B, tid, wave);
@@ -1597,6 +2080,24 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
         mainloop8<TM>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES, sa3 + OP_BYTES, s_sc,
                       cur.A.origin, cur.B.origin, cur.sa, cur.sb, sc_bytes, cur.A, cur.B, tid, wave, wm, wn, wm,
                       faa, fab, acc);
+    } else if constexpr (PP_PAIR) {
+      if (half)
+        mainloop_pp_pair<B_STRIDED, 2>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
+                                       sa3 + OP_BYTES, cur.A.origin, cur.B.origin, cur.A, cur.B, tid, wave, 0,
+                                       faa_half, fab, acc, prev_stores);
+      else
+        mainloop_pp_pair<B_STRIDED, TM>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
+                                        sa3 + OP_BYTES, cur.A.origin, cur.B.origin, cur.A, cur.B, tid, wave, wm,
+                                        faa, fab, acc, prev_stores);
+    } else if constexpr (PP) {
+      if (half)
+        mainloop_pp<A_STRIDED, B_STRIDED, 2, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
+                                                   smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
+                                                   cur.B, tid, wave, faa_half, fab, acc, prev_stores);
+      else
+        mainloop_pp<A_STRIDED, B_STRIDED, TM, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
+                                                    smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
+                                                    cur.B, tid, wave, faa, fab, acc, prev_stores);
     } else if constexpr (PAIRED) {
       // the wave's A rows: 128 wm.. (full height, region wm) or 64 wm.. (half, region 0)
       if (half)
