@@ -409,6 +409,24 @@ gg_status gg_route(const int32_t* expert_of_slot, int64_t slots,
                    int32_t num_groups, int32_t min_alignment, int pad_empty,
                    int32_t* offs, int32_t* row_slot, int64_t rows_cap,
                    int32_t* slot_row, void* workspace, void* stream);
+/*
+ * gg_route_noalloc -- gg_route for callers that cannot allocate device
+ *   memory (code under HIP graph capture, tight serving loops, harnesses
+ *   that forbid hipMalloc): the same arguments and results without the
+ *   workspace.  The route histograms go to a scratch array of
+ *   GG_ROUTE_NOALLOC_SCRATCH_BYTES that the library holds per GPU until the
+ *   process ends; gg_route_workspace_bytes(slots, num_groups) must not exceed
+ *   it (GG_ERR_LIMIT otherwise: 4 MiB covers, for example, 4M slots with 256
+ *   experts).  Allocates nothing.  Every call on one GPU shares that GPU's
+ *   array, so calls whose executions overlap on one GPU (different streams,
+ *   or host threads racing on one stream) race and may corrupt each other's
+ *   results; calls ordered on one stream are safe.
+ */
+#define GG_ROUTE_NOALLOC_SCRATCH_BYTES (4 << 20)
+gg_status gg_route_noalloc(const int32_t* expert_of_slot, int64_t slots,
+                           int32_t num_groups, int32_t min_alignment,
+                           int pad_empty, int32_t* offs, int32_t* row_slot,
+                           int64_t rows_cap, int32_t* slot_row, void* stream);
 gg_status gg_gather_rows(const void* src, int64_t tokens, int64_t row_bytes,
                          const int32_t* row_slot, int32_t topk,
                          const int32_t* offs, int32_t num_groups,

@@ -88,6 +88,8 @@ def load():
     lib.gg_route_workspace_bytes.restype = ctypes.c_int64
     lib.gg_route.argtypes = [P, I64, I32, I32, ctypes.c_int, P, P, I64, P, P, P]
     lib.gg_route.restype = ctypes.c_int
+    lib.gg_route_noalloc.argtypes = [P, I64, I32, I32, ctypes.c_int, P, P, I64, P, P]
+    lib.gg_route_noalloc.restype = ctypes.c_int
     lib.gg_gather_rows.argtypes = [P, I64, I64, P, I32, P, I32, I64, P, P]
     lib.gg_gather_rows.restype = ctypes.c_int
     lib.gg_combine_rows.argtypes = [P, I64, P, P, I32, I64, I64, P, ctypes.c_int, P]

@@ -6,6 +6,7 @@
 
 #include <atomic>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "gg.h"
@@ -363,6 +364,74 @@ gg_status gg_route(const int32_t* expert_of_slot, int64_t slots, int32_t num_gro
   return hip_result(gg::launch_route(expert_of_slot, slots, num_groups, min_alignment, pad_empty != 0, offs,
                                      row_slot, slot_row, static_cast<int32_t*>(workspace),
                                      static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+// ---- routing without a workspace argument (gg_route_noalloc) -----------------------
+//
+// The route histograms live in this array instead of a caller's workspace:
+// one copy per GPU, held until the process ends.  In host code `scratch`
+// names a host-side stand-in, not the device memory: the device address is
+// taken once per device with hipGetSymbolAddress (that device current) and
+// only that address is ever passed to a kernel.
+static __device__ __align__(256) int32_t scratch[GG_ROUTE_NOALLOC_SCRATCH_BYTES / 4];
+
+namespace {
+
+constexpr int64_t kNoAllocScratchBytes = GG_ROUTE_NOALLOC_SCRATCH_BYTES;
+
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices];   // per device, set once under g_scratch_mu
+
+gg_status scratch_for_current_device(int32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    g_last_error = std::string("hipGetDevice: ") + hipGetErrorString(e);
+    return GG_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(GG_ERR_HIP, "device ordinal out of range");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      g_last_error = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+      return GG_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  *out = g_scratch_ptr[dev];
+  return GG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gg_status gg_route_noalloc(const int32_t* expert_of_slot, int64_t slots, int32_t num_groups,
+                           int32_t min_alignment, int pad_empty, int32_t* offs, int32_t* row_slot,
+                           int64_t rows_cap, int32_t* slot_row, void* stream) {
+  if (!offs || !row_slot || (slots > 0 && (!expert_of_slot || !slot_row)))
+    return fail(GG_ERR_NULL_PTR, "a required pointer is NULL");
+  if (num_groups < 1 || num_groups > GG_MAX_GROUPS) return fail(GG_ERR_LIMIT, "num_groups must be in [1, GG_MAX_GROUPS]");
+  if (min_alignment < 1 || min_alignment > kMaxAlignment)
+    return fail(GG_ERR_BAD_DIM, "min_alignment must be in [1, 4096]");
+  if (slots < 0) return fail(GG_ERR_BAD_DIM, "slots must be >= 0");
+  const int64_t bound = gg_route_rows_bound(slots, num_groups, min_alignment);
+  if (bound >= kRowLimit)
+    return fail(GG_ERR_BAD_DIM, "slots + num_groups * min_alignment must be below 2^31 - 2^16");
+  if (rows_cap < bound) return fail(GG_ERR_BAD_DIM, "rows_cap is below gg_route_rows_bound");
+  if (gg_route_workspace_bytes(slots, num_groups) > kNoAllocScratchBytes)
+    return fail(GG_ERR_LIMIT, "the route histograms exceed GG_ROUTE_NOALLOC_SCRATCH_BYTES; use gg_route");
+  if (!aligned4(expert_of_slot) || !aligned4(offs) || !aligned4(row_slot) || !aligned4(slot_row))
+    return fail(GG_ERR_ALIGNMENT, "int32 arrays must be 4-byte aligned");
+  int32_t* hist = nullptr;
+  const gg_status s = scratch_for_current_device(&hist);
+  if (s != GG_OK) return s;
+  return hip_result(gg::launch_route(expert_of_slot, slots, num_groups, min_alignment, pad_empty != 0, offs,
+                                     row_slot, slot_row, hist, static_cast<hipStream_t>(stream)));
 }
 
 gg_status gg_gather_rows(const void* src, int64_t tokens, int64_t row_bytes, const int32_t* row_slot,

@@ -287,3 +287,19 @@ def test_weight_size_limit(lib, name):
     # one expert's k x n weights must stay under 4 GiB (k * n < 2^31)
     rc = call(name, k=65536, n=32768)
     assert rc == 2 and "k * n" in gg.last_error(), (name, rc, gg.last_error())
+
+
+@pytest.mark.parametrize("case,status", [
+    (dict(ids=0), 1), (dict(offs=0), 1), (dict(e=0), 5), (dict(align=0), 2), (dict(cap=90), 2),
+    (dict(slots=-1), 2), (dict(offs=A + 2), 3),
+    # histograms beyond the fixed scratch array: rejected before any launch
+    (dict(slots=1024 * 1025, e=1024, align=1, cap=1024 * 1025 + 1024), 5),
+])
+def test_route_noalloc_checks_arguments(lib, case, status):
+    v = dict(ids=A, slots=64, e=4, align=8, pad=1, offs=A + 0x100, rs=A + 0x200, cap=64 + 32, sr=A + 0x300, s=0)
+    v.update(case)
+    rc = gg.call_raw("gg_route_noalloc", v["ids"] or None, v["slots"], v["e"], v["align"], v["pad"],
+                     v["offs"] or None, v["rs"], v["cap"], v["sr"], v["s"])
+    assert rc == status, (case, rc, gg.last_error())
+    if status == 5 and case.get("slots"):
+        assert "GG_ROUTE_NOALLOC_SCRATCH_BYTES" in gg.last_error()
