@@ -26,11 +26,11 @@
 // Data path (no register staging): every operand tile goes from global
 // memory straight into LDS with buffer loads in LDS mode (16 bytes per lane,
 // 1 KB per wave instruction), one 32-deep reduction stage at a time, through
-// a ring of 4 LDS stages: the loads for stage s + 3 are issued while the
-// MFMAs consume stage s.  In the row passes (bf16 and fp8) the A operand is
-// staged two stages at a time instead, so that its loads read whole cache
-// lines (the pair layout, stated with mainloop_pair).  Each operand keeps
-// its memory layout in LDS:
+// a ring of 4 LDS stages, loads running 3 to 6 half-stages ahead of their
+// first reader.  In the bf16 row passes the A operand is staged two stages
+// at a time instead, so that its loads read whole cache lines (the pair
+// layout, stated with dma_pair).  Each operand keeps its memory layout in
+// LDS:
 //   red-contig  : 256 tile rows x 64 bytes (32 reduction values), the
 //                 16-byte chunk c of row r at position c ^ ((r / 4) mod 4);
 //                 MFMA fragments come from ds_read_b128.
@@ -62,9 +62,12 @@
 // MFMA: v_mfma_f32_32x32x16_bf16, fp32 accumulation.  A workgroup is 8 waves
 // (2 x 4) over a 256 x 256 output tile; each wave owns 128 x 64, i.e. 4 x 2
 // MFMA blocks of 32 x 32 (128 accumulator registers per lane), so two waves
-// share each SIMD: while one waits at the stage barrier or on its loads, the
-// other keeps the matrix core busy, and the global->LDS loads (whose rate is
-// bounded per wave) are spread over twice as many waves.
+// share each SIMD.  In the bf16 passes those two take turns (the ping-pong
+// loops): one issues a stage's 16 MFMAs back to back from fragments already
+// in its registers while the other reads its next fragments from LDS and
+// issues its share of the global->LDS loads, so a load that cannot issue yet
+// or an LDS read in flight holds up only the wave that is not computing.  The
+// fp8 forward interleaves loads with the MFMAs of both waves (mainloop8).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -326,19 +329,6 @@ __device__ __forceinline__ void mfma_fence(floatx16 (&acc)[TM][TN]) {
 
 // ---- the main loop ---------------------------------------------------------------
 
-// Issue the 4 global->LDS loads (2 per operand) of stage `st` into stage
-// buffer `buf` (A tile at +0, B tile at +OP_BYTES).
-template <bool A_STRIDED, bool B_STRIDED, bool WIDE>
-__device__ __forceinline__ void load_stage(const Operand& A, const Operand& B, int st, uint8_t* buf,
-                                           int tid, int wave) {
-  const DmaCtx ca = dma_ctx<A_STRIDED, 2, WIDE>(A, st * BK, tid);
-  const DmaCtx cb = dma_ctx<B_STRIDED, 2, WIDE>(B, st * BK, tid);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) dma_load(ca, buf, wave, j);
-#pragma unroll
-  for (int j = 0; j < 2; ++j) dma_load(cb, buf + OP_BYTES, wave, j);
-}
-
 // LDS operations of this wave complete, then all waves meet (no wait on
 // global memory operations).
 __device__ __forceinline__ void lds_barrier() {
@@ -356,143 +346,12 @@ __device__ __forceinline__ void stage_barrier_vm() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// The reduction loop of one output tile with both operands one stage per
-// slot (wgrad; the row passes use mainloop_pair below).  Stage kt (BK = 32
-// reduction values of both operands) lives in LDS buffer kt mod 4, and the
-// loads run three stages ahead.  Per stage and wave, in this order:
-//   MFMA sub-step 0 (fragments f0, read earlier), interleaved with the loads
-//   of the B half of stage kt+3 into the buffer of stage kt-1
-//   wait for stage kt+1, barrier
-//   MFMA sub-step 1 (f1), interleaved with the loads of the A half of stage
-//   kt+4 into the buffer of stage kt and the reads of sub-step 0 of stage
-//   kt+1 -> f0
-//   read sub-step 1 of stage kt+1 -> f1
-// The four buffers are distinct restrict-qualified pointers and the loop is
-// unrolled by four so that every LDS access names its buffer: the compiler
-// then knows a fragment read never overlaps a load in flight to another
-// buffer and does not make the read wait for it.  Loads past the reduction
-// end write zeros (never read for this tile); the caller waits for them
-// before the LDS is reused.
-
-// The loads a tile's main loop expects in flight when it starts: stages
-// 0..2 and the A half of stage 3 (stage 0's first sub-step issues the B half
-// of stage 3).  Issued by the caller, so they can overlap the previous tile's
-// stores.  Only for tiles with at least one reduction step.
-template <bool A_STRIDED, bool B_STRIDED, bool WIDE = false>
-__device__ __attribute__((always_inline)) inline void prologue_loads(
-    uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
-    uint8_t* __restrict__ s3, const uint8_t* __restrict__ a_origin,
-    const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid, int wave) {
-  A.origin = a_origin;
-  B.origin = b_origin;
-  load_stage<A_STRIDED, B_STRIDED, WIDE>(A, B, 0, s0, tid, wave);
-  load_stage<A_STRIDED, B_STRIDED, WIDE>(A, B, 1, s1, tid, wave);
-  load_stage<A_STRIDED, B_STRIDED, WIDE>(A, B, 2, s2, tid, wave);
-  const DmaCtx ca = dma_ctx<A_STRIDED, 2, WIDE>(A, 3 * BK, tid);
-  dma_load(ca, s3, wave, 0);
-  dma_load(ca, s3, wave, 1);
-}
-constexpr int kPrologueLoads = 10;     // per wave, after stage 0's four
-
 // Stores a wave issues for one fp32 output tile of TMA active row blocks
 // (store_tile<true, TMA> issues exactly this many, in or out of range).
 template <int TMA>
 constexpr int stores_f32() { return TMA * TN * 4; }
 
-// TMA: active 32-row blocks of A per wave -- TM for a full 256-row tile, 2
-// for a half-height tile (an expert's last 128 rows or fewer), whose waves
-// then own 64 x 64 each.  prev_stores: fp32 stores issued after this tile's
-// prologue loads (the previous tile's), 0 if none.
-template <bool A_STRIDED, bool B_STRIDED, int TMA, bool WIDE = false>
-__device__ __attribute__((always_inline)) inline void mainloop(
-    uint8_t* __restrict__ s0, uint8_t* __restrict__ s1, uint8_t* __restrict__ s2,
-    uint8_t* __restrict__ s3, const uint8_t* __restrict__ a_origin,
-    const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid, int wave,
-    const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[TM][TN], int prev_stores) {
-  // loads spread over each sub-step's MFMAs: two per sub-step, half a
-  // sub-step apart
-  constexpr int kSplitGap = TMA * TN / 2;
-  constexpr int kSplitAt = 1;
-  // The global operands are only read here; deriving every load from these
-  // restrict-qualified pointers (and every LDS access from s0..s3) lets each
-  // global->LDS load carry the identity of the one stage buffer it writes.
-  A.origin = a_origin;
-  B.origin = b_origin;
-  const int nk = (A.red + BK - 1) / BK;
-  if (nk <= 0) return;
-  Frags f0, f1;
-  // stage 0 landed (vector memory operations complete in issue order; when
-  // the previous tile's stores were issued after this tile's prologue loads,
-  // they may still be in flight)
-  if (prev_stores == stores_f32<TM>())
-    stage_barrier_vm<kPrologueLoads + stores_f32<TM>()>();
-  else if (prev_stores == stores_f32<2>())
-    stage_barrier_vm<kPrologueLoads + stores_f32<2>()>();
-  else
-    stage_barrier_vm<kPrologueLoads>();
-  read_stage_frags<A_STRIDED, B_STRIDED, TMA>(s0, s0 + OP_BYTES, faa, fab, 0, f0);
-  read_stage_frags<A_STRIDED, B_STRIDED, TMA>(s0, s0 + OP_BYTES, faa, fab, 1, f1);
-
-// One stage (buffers named directly, so every access is based on one of the
-// restrict-qualified parameters).  BC, BN, BP: the buffers of stages KT,
-// KT + 1 and KT - 1 (= KT + 3 mod 4).  A wave's global->LDS loads are
-// accepted at a bounded rate, and a load that cannot issue yet stalls the
-// (in-order) wave -- and with it the MFMAs behind it.  So each sub-step
-// issues only two loads, kSplitGap MFMAs apart: the first sub-step the B
-// half of stage KT + 3 (into BP, whose reads all finished before the
-// previous stage's barrier), the second the A half of stage KT + 4 (into BC,
-// free once this stage's barrier is passed).
-#define GG_STAGE(BC, BN, BP, KT)                                                          \
-  {                                                                                       \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    const DmaCtx cb = dma_ctx<B_STRIDED, 2, WIDE>(B, ((KT) + 3) * BK, tid);               \
-    _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                \
-      const int i = q / TN, j = q % TN;                                                   \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.b[j], f0.a[i], acc[i][j], 0, 0, 0); \
-      if (q % kSplitGap == kSplitAt && q / kSplitGap < 2)                                 \
-        dma_load(cb, (BP) + OP_BYTES, wave, q / kSplitGap);                               \
-      __builtin_amdgcn_sched_barrier(0);                                                  \
-    }                                                                                     \
-    mfma_fence(acc);                                                                      \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    stage_barrier_vm<8>(); /* stage KT+1 landed; stage KT consumed */                     \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    const DmaCtx ca = dma_ctx<A_STRIDED, 2, WIDE>(A, ((KT) + 4) * BK, tid);               \
-    _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                \
-      const int i = q / TN, j = q % TN;                                                   \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0); \
-      if (q % kSplitGap == kSplitAt && q / kSplitGap < 2)                                 \
-        dma_load(ca, BC, wave, q / kSplitGap);                                            \
-      if (q < TMA) f0.a[q] = read_frag<A_STRIDED>(BN, faa, 0, q);                         \
-      else if (q < TMA + TN) f0.b[q - TMA] = read_frag<B_STRIDED>((BN) + OP_BYTES, fab, 0, q - TMA); \
-      __builtin_amdgcn_sched_barrier(0);                                                  \
-    }                                                                                     \
-    mfma_fence(acc);                                                                      \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    read_stage_frags<A_STRIDED, B_STRIDED, TMA>(BN, (BN) + OP_BYTES, faa, fab, 1, f1);    \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-  }
-
-  for (int kt = 0; kt < nk; kt += 4) {
-    GG_STAGE(s0, s1, s3, kt)
-    if (kt + 1 < nk) GG_STAGE(s1, s2, s0, kt + 1)
-    if (kt + 2 < nk) GG_STAGE(s2, s3, s1, kt + 2)
-    if (kt + 3 < nk) GG_STAGE(s3, s0, s2, kt + 3)
-  }
-#undef GG_STAGE
-}
-
 // ---- ping-pong main loop -----------------------------------------------------------
-#ifndef GG_PP_PRIO
-#define GG_PP_PRIO 0
-#endif
-#if GG_PP_PRIO
-#define GG_PP_PRIO_UP __builtin_amdgcn_s_setprio(1);
-#define GG_PP_PRIO_DOWN __builtin_amdgcn_s_setprio(0);
-#else
-#define GG_PP_PRIO_UP
-#define GG_PP_PRIO_DOWN
-#endif
 //
 // The two waves of each SIMD take turns: while one issues a stage's 16
 // MFMAs back to back from fragments already in its registers, the other
@@ -652,7 +511,6 @@ __device__ __attribute__((always_inline)) inline void mainloop_pp(
 
 #define GG_PP_MFMA()                                                                              \
   {                                                                                               \
-    GG_PP_PRIO_UP                                                                                 \
     _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                        \
       const int i = q / TN, j = q % TN;                                                           \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.b[j], f0.a[i], acc[i][j], 0, 0, 0); \
@@ -662,7 +520,6 @@ __device__ __attribute__((always_inline)) inline void mainloop_pp(
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0); \
     }                                                                                             \
     mfma_fence(acc);                                                                              \
-    GG_PP_PRIO_DOWN                                                                               \
   }
 #define GG_PP_READ(BUF)                                                                           \
   {                                                                                               \
@@ -723,12 +580,12 @@ __device__ __attribute__((always_inline)) inline void mainloop_pp(
 #undef GG_PP_MFMA
 }
 
-// ---- full-line staging of reduction-contiguous operands (bf16 row passes) ----------
+// ---- full-line staging of reduction-contiguous operands (row passes) ---------------
 //
 // One stage of a reduction-contiguous operand is 64 bytes per tile row: half
-// a cache line per row and load.  The row passes stage such an operand two
-// stages at a time instead, so that one load moves 128 contiguous bytes (both
-// stages) of 8 tile rows and every line is read whole.
+// a cache line per row and load.  The row passes (bf16 and fp8) stage their A
+// operand two stages at a time instead, so that one load moves 128 contiguous
+// bytes (both stages) of 8 tile rows and every line is read whole.
 //
 // Stage pair j of A holds stages 2j and 2j + 1: tile rows 0..127 in A's
 // region of ring slot 2j mod 4, rows 128..255 in that of slot (2j + 1) mod
@@ -736,13 +593,10 @@ __device__ __attribute__((always_inline)) inline void mainloop_pp(
 // first stage's 64 bytes of each row in the block's first 512 bytes, the
 // second stage's in the other 512, each row at 64 (r mod 8) with its 16-byte
 // chunks swizzled c ^ ((r / 4) mod 4) as in the single-stage layout
-// (fragment reads stay bank-conflict-free).  A pair can be loaded only when
-// both its regions are free, i.e. after stage 2j - 3, so its four loads per
-// wave are issued in the second half of that (odd) stage: two stages ahead,
-// not three.  B keeps one stage per slot and its loads three stages ahead,
+// (fragment reads stay bank-conflict-free).  B keeps one stage per slot,
 // whether reduction-strided (forward) or -contiguous (dgrad, whose B is the
-// weight stream: pairing it too measured slower, as it then has one stage
-// less to arrive).
+// weight stream: pairing it too measured slower, as it then has less time to
+// arrive).
 
 struct DmaPair {
   __amdgpu_buffer_rsrc_t rs;
@@ -813,161 +667,7 @@ __device__ __forceinline__ bf16x8 read_frag_pair(const uint8_t* region, const Fr
                                                                      (uint32_t)(i * 4096 + par * 512)));
 }
 
-// Loads a tile's main loop expects in flight when it starts, in this order:
-// A pair 0 (stages 0, 1), B stages 0 and 1, A pair 1 (stages 2, 3), B stage
-// 2; the first wait leaves the 8 after B stage 0 in flight.
-template <bool B_STRIDED>
-__device__ __attribute__((always_inline)) inline void prologue_loads_pair(
-    uint8_t* __restrict__ a0, uint8_t* __restrict__ a1, uint8_t* __restrict__ a2, uint8_t* __restrict__ a3,
-    uint8_t* __restrict__ b0, uint8_t* __restrict__ b1, uint8_t* __restrict__ b2, uint8_t* __restrict__ b3,
-    const uint8_t* __restrict__ a_origin, const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid,
-    int wave) {
-  A.origin = a_origin;
-  B.origin = b_origin;
-  const bool hi = wave >= 4;
-  {
-    const DmaPair c = dma_pair(A, 0, tid);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) dma_load_pair(c, hi ? a1 : a0, wave, jj);
-  }
-  {
-    const DmaCtx c0 = dma_ctx<B_STRIDED>(B, 0, tid);
-    dma_load(c0, b0, wave, 0);
-    dma_load(c0, b0, wave, 1);
-    const DmaCtx c1 = dma_ctx<B_STRIDED>(B, BK, tid);
-    dma_load(c1, b1, wave, 0);
-    dma_load(c1, b1, wave, 1);
-  }
-  {
-    const DmaPair c = dma_pair(A, 2 * BK, tid);
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) dma_load_pair(c, hi ? a3 : a2, wave, jj);
-  }
-  {
-    const DmaCtx c2 = dma_ctx<B_STRIDED>(B, 2 * BK, tid);
-    dma_load(c2, b2, wave, 0);
-    dma_load(c2, b2, wave, 1);
-  }
-}
-constexpr int kPrologueLoadsPair = 8;   // per wave, after the first stage's loads
-
-// The reduction loop of one output tile with A in the pair layout and B one
-// stage per slot (loads three stages ahead, issued in the first half of
-// each stage).  ha: the region of the wave's A rows (0: tile rows 0..127,
-// 1: 128..255).  Loads in flight at each stage's wait: 8 in even stages, 4
-// in odd ones (an odd stage's wait is for the A pair issued two stages
-// before, followed only by two B stages).
-template <bool B_STRIDED, int TMA>
-__device__ __attribute__((always_inline)) inline void mainloop_pair(
-    uint8_t* __restrict__ a0, uint8_t* __restrict__ a1, uint8_t* __restrict__ a2, uint8_t* __restrict__ a3,
-    uint8_t* __restrict__ b0, uint8_t* __restrict__ b1, uint8_t* __restrict__ b2, uint8_t* __restrict__ b3,
-    const uint8_t* __restrict__ a_origin, const uint8_t* __restrict__ b_origin, Operand A, Operand B, int tid,
-    int wave, int ha, const FragAddr& faa, const FragAddr& fab, floatx16 (&acc)[TM][TN],
-    int prev_stores) {
-  constexpr int kSplitGap = TMA * TN / 2;     // B stage loads: two per first half
-  constexpr int kSplitAt = 1;
-  constexpr int kPairGap = TMA * TN / 4;      // pair loads: four per second half
-  A.origin = a_origin;
-  B.origin = b_origin;
-  const int nk = (A.red + BK - 1) / BK;
-  if (nk <= 0) return;
-  const bool hi = wave >= 4;
-  Frags f0, f1;
-  if (prev_stores == stores_f32<TM>())
-    stage_barrier_vm<kPrologueLoadsPair + stores_f32<TM>()>();
-  else if (prev_stores == stores_f32<2>())
-    stage_barrier_vm<kPrologueLoadsPair + stores_f32<2>()>();
-  else
-    stage_barrier_vm<kPrologueLoadsPair>();
-
-// Per stage U = KT mod 4 (a literal): the A region of stage U (pair slots
-// {0,1} or {2,3}, the wave's half), its parity in the pair, and B's slot.
-#define GG_RA(U) ((U) < 2 ? (ha ? a1 : a0) : (ha ? a3 : a2))
-#define GG_PA(U) ((U) & 1)
-#define GG_RB(U) ((U) == 0 ? b0 : (U) == 1 ? b1 : (U) == 2 ? b2 : b3)
-#define GG_READ_A(U, KS, I, F) \
-  { (F).a[(I)] = read_frag_pair(GG_RA(U), faa, (KS), (I), GG_PA(U)); }
-#define GG_READ_B(U, KS, J, F) \
-  { (F).b[(J)] = read_frag<B_STRIDED>(GG_RB(U), fab, (KS), (J)); }
-#pragma unroll
-  for (int i = 0; i < TMA; ++i) GG_READ_A(0, 0, i, f0)
-#pragma unroll
-  for (int j = 0; j < TN; ++j) GG_READ_B(0, 0, j, f0)
-#pragma unroll
-  for (int i = 0; i < TMA; ++i) GG_READ_A(0, 1, i, f1)
-#pragma unroll
-  for (int j = 0; j < TN; ++j) GG_READ_B(0, 1, j, f1)
-
-// One stage KT (U = KT mod 4).  First half: MFMAs on f0, with the loads of
-// B stage KT + 3 into slot U + 3.  Wait for stage KT + 1 and meet.  Second
-// half: MFMAs on f1, with (odd U) the loads of the A pair of stages KT + 3,
-// KT + 4 into slots {0,1} (U = 1) or {2,3} (U = 3), and the reads of stage
-// KT + 1's first-half fragments; then its second-half fragments.
-#define GG_STAGE_P(U, KT)                                                                         \
-  {                                                                                               \
-    __builtin_amdgcn_sched_barrier(0);                                                            \
-    const DmaCtx cbs = dma_ctx<B_STRIDED>(B, ((KT) + 3) * BK, tid);                               \
-    _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                        \
-      const int i = q / TN, j = q % TN;                                                           \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.b[j], f0.a[i], acc[i][j], 0, 0, 0); \
-      if (q % kSplitGap == kSplitAt && q / kSplitGap < 2)                                         \
-        dma_load(cbs, ((U) == 0 ? b3 : (U) == 1 ? b0 : (U) == 2 ? b1 : b2), wave, q / kSplitGap);   \
-      __builtin_amdgcn_sched_barrier(0);                                                          \
-    }                                                                                             \
-    mfma_fence(acc);                                                                              \
-    __builtin_amdgcn_sched_barrier(0);                                                            \
-    if (((U) & 1) == 0) stage_barrier_vm<8>();                                                    \
-    else stage_barrier_vm<4>();                                                                   \
-    __builtin_amdgcn_sched_barrier(0);                                                            \
-    constexpr bool kIssueA = ((U) & 1) == 1;                                                      \
-    DmaPair cp;                                                                                   \
-    if constexpr (kIssueA) cp = dma_pair(A, ((KT) + 3) * BK, tid);                                \
-    _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                        \
-      const int i = q / TN, j = q % TN;                                                           \
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0); \
-      if (q % kPairGap == kPairGap - 1) {                                                         \
-        if constexpr (kIssueA)                                                                    \
-          dma_load_pair(cp, (U) == 1 ? (hi ? a1 : a0) : (hi ? a3 : a2), wave, q / kPairGap);      \
-      }                                                                                           \
-      if (q < TMA) GG_READ_A(((U) + 1) & 3, 0, q, f0)                                             \
-      else if (q < TMA + TN) GG_READ_B(((U) + 1) & 3, 0, q - TMA, f0)                             \
-      __builtin_amdgcn_sched_barrier(0);                                                          \
-    }                                                                                             \
-    mfma_fence(acc);                                                                              \
-    __builtin_amdgcn_sched_barrier(0);                                                            \
-    _Pragma("unroll") for (int i = 0; i < TMA; ++i) GG_READ_A(((U) + 1) & 3, 1, i, f1)            \
-    _Pragma("unroll") for (int j = 0; j < TN; ++j) GG_READ_B(((U) + 1) & 3, 1, j, f1)             \
-    __builtin_amdgcn_sched_barrier(0);                                                            \
-  }
-
-  for (int kt = 0; kt < nk; kt += 4) {
-    GG_STAGE_P(0, kt)
-    if (kt + 1 < nk) GG_STAGE_P(1, kt + 1)
-    if (kt + 2 < nk) GG_STAGE_P(2, kt + 2)
-    if (kt + 3 < nk) GG_STAGE_P(3, kt + 3)
-  }
-#undef GG_STAGE_P
-#undef GG_READ_A
-#undef GG_READ_B
-#undef GG_RA
-#undef GG_PA
-#undef GG_RB
-}
-
 // ---- ping-pong main loop with A in the pair layout (bf16 row passes) ----------------
-#ifndef GG_PP_LOADFIRST
-#define GG_PP_LOADFIRST 0
-#endif
-#ifndef GG_PP2_SAFE
-#define GG_PP2_SAFE 0
-#endif
-#if GG_PP2_SAFE
-#define GG_PP2_WAIT4(R) pp_sync<0>(R)
-#define GG_PP2_WAITL(R) pp_sync<0>(R)
-#else
-#define GG_PP2_WAIT4(R) pp_sync<4>(R)
-#define GG_PP2_WAITL(R) pp_sync<kNoVm>(R)
-#endif
 //
 // The ping-pong schedule above, with the reduction-contiguous A operand
 // staged two stages at a time in the pair layout (whole cache lines), B one
@@ -1059,11 +759,11 @@ __device__ __attribute__((always_inline)) inline void mainloop_pp_pair(
   // and the previous tile's direct stores, issued after them, may be in
   // flight); group 1 waits at the next barrier
   if (prev_stores == stores_f32<TM>()) {
-    if (g0) pp_sync<8 + stores_f32<TM>()>(rg); else GG_PP2_WAITL(rg);
+    if (g0) pp_sync<8 + stores_f32<TM>()>(rg); else pp_sync<kNoVm>(rg);
   } else if (prev_stores == stores_f32<2>()) {
-    if (g0) pp_sync<8 + stores_f32<2>()>(rg); else GG_PP2_WAITL(rg);
+    if (g0) pp_sync<8 + stores_f32<2>()>(rg); else pp_sync<kNoVm>(rg);
   } else {
-    if (g0) pp_sync<8>(rg); else GG_PP2_WAITL(rg);
+    if (g0) pp_sync<8>(rg); else pp_sync<kNoVm>(rg);
   }
 
 #define GG_RA(U) ((U) < 2 ? (ha ? a1 : a0) : (ha ? a3 : a2))
@@ -1077,7 +777,6 @@ __device__ __attribute__((always_inline)) inline void mainloop_pp_pair(
   }
 #define GG_PP_MFMA()                                                                              \
   {                                                                                               \
-    GG_PP_PRIO_UP                                                                                 \
     _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                        \
       const int i = q / TN, j = q % TN;                                                           \
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0.b[j], f0.a[i], acc[i][j], 0, 0, 0); \
@@ -1087,7 +786,6 @@ __device__ __attribute__((always_inline)) inline void mainloop_pp_pair(
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1.b[j], f1.a[i], acc[i][j], 0, 0, 0); \
     }                                                                                             \
     mfma_fence(acc);                                                                              \
-    GG_PP_PRIO_DOWN                                                                               \
   }
 // B of stage Q into slot U (one group's 4 waves)
 #define GG_PP_LOAD_B(U, Q)                                                                        \
@@ -1106,7 +804,7 @@ __device__ __attribute__((always_inline)) inline void mainloop_pp_pair(
     // step -1: read stage 0
     GG_PP_READ(0)
     __builtin_amdgcn_sched_barrier(0);
-    GG_PP2_WAITL(rg);
+    pp_sync<kNoVm>(rg);
     // stage KT = kt + U: compute it, then read stage KT + 1 and load (U even)
     // B of stage KT + 4 into slot U or (U odd) this group's half of the A
     // pair of stages KT + 3, KT + 4 into slot (U + 3) mod 4
@@ -1115,14 +813,13 @@ __device__ __attribute__((always_inline)) inline void mainloop_pp_pair(
     __builtin_amdgcn_sched_barrier(0);                                                            \
     GG_PP_MFMA()                                                                                  \
     __builtin_amdgcn_sched_barrier(0);                                                            \
-    if ((U) & 1) GG_PP2_WAIT4(rg); else GG_PP2_WAITL(rg);                                      \
+    if ((U) & 1) pp_sync<4>(rg); else pp_sync<kNoVm>(rg);                                      \
     __builtin_amdgcn_sched_barrier(0);                                                            \
-    if (!GG_PP_LOADFIRST && (KT) + 1 < nk) GG_PP_READ(((U) + 1) & 3)                              \
+    if ((KT) + 1 < nk) GG_PP_READ(((U) + 1) & 3)                                                  \
     if (((U) & 1) == 0) GG_PP_LOAD_B(U, (KT) + 4)                                                 \
     else GG_PP_LOAD_A((U) == 1 ? a0 : a2, (KT) + 3)                                               \
-    if (GG_PP_LOADFIRST && (KT) + 1 < nk) GG_PP_READ(((U) + 1) & 3)                               \
     __builtin_amdgcn_sched_barrier(0);                                                            \
-    GG_PP2_WAITL(rg);                                                                                \
+    pp_sync<kNoVm>(rg);                                                                                \
   }
     for (int kt = 0; kt < nk; kt += 4) {
       GG_PP_STAGE0(0, kt)
@@ -1137,23 +834,22 @@ __device__ __attribute__((always_inline)) inline void mainloop_pp_pair(
     __builtin_amdgcn_sched_barrier(0);
     if (prev_stores == stores_f32<TM>()) pp_sync<4 + stores_f32<TM>()>(rg);
     else if (prev_stores == stores_f32<2>()) pp_sync<4 + stores_f32<2>()>(rg);
-    else GG_PP2_WAIT4(rg);
+    else pp_sync<4>(rg);
     // stage KT = kt + U: read it and load (U even) this group's half of the A
     // pair of stages KT + 2, KT + 3 into slot (U + 3) mod 4 or (U odd) B of
     // stage KT + 2 into slot (U + 2) mod 4; then compute it
 #define GG_PP_STAGE1(U, KT)                                                                       \
   {                                                                                               \
     __builtin_amdgcn_sched_barrier(0);                                                            \
-    if (!GG_PP_LOADFIRST) GG_PP_READ(U)                                                           \
+    GG_PP_READ(U)                                                                                 \
     if (((U) & 1) == 0) GG_PP_LOAD_A((U) == 0 ? a3 : a1, (KT) + 2)                                \
     else GG_PP_LOAD_B(((U) + 2) & 3, (KT) + 2)                                                    \
-    if (GG_PP_LOADFIRST) GG_PP_READ(U)                                                            \
     __builtin_amdgcn_sched_barrier(0);                                                            \
-    if (((U) & 1) == 0) GG_PP2_WAIT4(rg); else GG_PP2_WAITL(rg);                               \
+    if (((U) & 1) == 0) pp_sync<4>(rg); else pp_sync<kNoVm>(rg);                               \
     __builtin_amdgcn_sched_barrier(0);                                                            \
     GG_PP_MFMA()                                                                                  \
     __builtin_amdgcn_sched_barrier(0);                                                            \
-    if ((U) & 1) GG_PP2_WAIT4(rg); else GG_PP2_WAITL(rg);                                      \
+    if ((U) & 1) pp_sync<4>(rg); else pp_sync<kNoVm>(rg);                                      \
   }
     for (int kt = 0; kt < nk; kt += 4) {
       GG_PP_STAGE1(0, kt)
@@ -1300,6 +996,11 @@ __device__ __attribute__((always_inline)) inline void prologue_loads8(
   }
 }
 
+// Loads per wave in flight after the first stage's when the fp8 loop starts:
+// W stage 1, X pair 1 and W stage 2 (waves 0 and 1 have one more, the
+// scales of k-block 1).
+constexpr int kPrologueLoads8 = 8;
+
 // The fp8 reduction loop: the bf16 row passes' schedule (W stage kt+3 loaded
 // in the first half-stage, wait and barrier, the X pair of stages kt+3, kt+4
 // in the second half of odd stages), with the MFMAs of a stage split by row
@@ -1332,8 +1033,8 @@ __device__ __attribute__((always_inline)) inline void mainloop8(
   const bool hi = wave >= 4;
   i32x8 fa[TMA], fb0[TN], fb1[TN];
   uint32_t sa0, sb0, sa1 = 0, sb1 = 0;
-  if (wave < 2) stage_barrier_vm<kPrologueLoadsPair + 1>();
-  else stage_barrier_vm<kPrologueLoadsPair>();
+  if (wave < 2) stage_barrier_vm<kPrologueLoads8 + 1>();
+  else stage_barrier_vm<kPrologueLoads8>();
   scale_read<TMA>(sc, wm, wn, lane, sa0, sb0);
 #pragma unroll
   for (int i = 0; i < TMA; ++i) fa[i] = read_frag8_pair(ha ? a1 : a0, faa, i, 0);
@@ -1822,21 +1523,15 @@ struct Tile {
 // host picks it for wgrad on short experts; see launch()).  WIDE (wgrad
 // only): an expert's rows may span 4 GB or more of X or dY, so the load
 // ranges are capped per stage (see dma_ctx); the host picks it from m.
-#ifndef GG_PINGPONG
-#define GG_PINGPONG 2
-#endif
-
 template <int MODE, bool OUT_F32, bool STAGED_F32 = false, bool WIDE = false>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   static_assert(!WIDE || is_wgrad(MODE), "only wgrad reads an operand down a data-dependent span");
   constexpr bool A_STRIDED = is_wgrad(MODE);
   constexpr bool B_STRIDED = !is_dgrad(MODE) && !is_fp8(MODE);
-  // bf16 passes on the ping-pong main loop (one stage per slot)
-  constexpr bool PP = GG_PINGPONG >= 1 && !is_fp8(MODE);
-  // ... the row passes with A in the pair layout
-  constexpr bool PP_PAIR = GG_PINGPONG >= 2 && PP && !is_wgrad(MODE);
-  // bf16 row passes: reduction-contiguous operands in the stage-pair layout
-  constexpr bool PAIRED = !PP && !is_wgrad(MODE) && !is_fp8(MODE);
+  // Main loops: the bf16 row passes ping-pong with A in the pair layout,
+  // wgrad ping-pongs with one stage per slot for both operands, the fp8
+  // forward interleaves (mainloop8).
+  constexpr bool PP_PAIR = !is_wgrad(MODE) && !is_fp8(MODE);
 
   // LDS: NSTAGE stage buffers of 32 KB (A tile, then B tile); fp8: two
   // k-blocks of scales.
@@ -1881,7 +1576,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   const uint8_t* pb = reinterpret_cast<const uint8_t*>(p.b);
   uint8_t* pc = reinterpret_cast<uint8_t*>(p.c);
   // A in the pair layout for the row passes (bf16 and fp8), one stage per slot for wgrad
-  constexpr bool A_PAIRED = !is_wgrad(MODE) && (!PP || PP_PAIR);
+  constexpr bool A_PAIRED = !is_wgrad(MODE);
   const FragAddr faa = A_PAIRED ? frag_addr_pair(128 * wm, lane) : frag_addr<A_STRIDED>(128 * wm, lane);
   // half-height tiles
   const FragAddr faa_half = A_PAIRED ? frag_addr_pair(64 * wm, lane) : frag_addr<A_STRIDED>(64 * wm, lane);
@@ -2031,17 +1726,10 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
       else if constexpr (PP_PAIR)
         prologue_loads_pp_pair<B_STRIDED>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
                                           T.A.origin, T.B.origin, T.A, T.B, tid, wave);
-      else if constexpr (PP)
+      else
         prologue_loads_pp<A_STRIDED, B_STRIDED, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
                                                       smem + 3 * STAGE_BYTES, T.A.origin, T.B.origin, T.A,
                                                       T.B, tid, wave);
-      else if constexpr (PAIRED)
-        prologue_loads_pair<B_STRIDED>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
-                                       sa3 + OP_BYTES, T.A.origin, T.B.origin, T.A, T.B, tid, wave);
-      else
-        prologue_loads<A_STRIDED, B_STRIDED, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
-                                                   smem + 3 * STAGE_BYTES, T.A.origin, T.B.origin, T.A,
-                                                   T.B, tid, wave);
     }
   };
 
@@ -2081,6 +1769,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
                       cur.A.origin, cur.B.origin, cur.sa, cur.sb, sc_bytes, cur.A, cur.B, tid, wave, wm, wn, wm,
                       faa, fab, acc);
     } else if constexpr (PP_PAIR) {
+      // the wave's A rows: 128 wm.. (full height, region wm) or 64 wm.. (half, region 0)
       if (half)
         mainloop_pp_pair<B_STRIDED, 2>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
                                        sa3 + OP_BYTES, cur.A.origin, cur.B.origin, cur.A, cur.B, tid, wave, 0,
@@ -2089,7 +1778,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
         mainloop_pp_pair<B_STRIDED, TM>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
                                         sa3 + OP_BYTES, cur.A.origin, cur.B.origin, cur.A, cur.B, tid, wave, wm,
                                         faa, fab, acc, prev_stores);
-    } else if constexpr (PP) {
+    } else {
       if (half)
         mainloop_pp<A_STRIDED, B_STRIDED, 2, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
                                                    smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
@@ -2098,25 +1787,6 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
         mainloop_pp<A_STRIDED, B_STRIDED, TM, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
                                                     smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
                                                     cur.B, tid, wave, faa, fab, acc, prev_stores);
-    } else if constexpr (PAIRED) {
-      // the wave's A rows: 128 wm.. (full height, region wm) or 64 wm.. (half, region 0)
-      if (half)
-        mainloop_pair<B_STRIDED, 2>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
-                                    sa3 + OP_BYTES, cur.A.origin, cur.B.origin, cur.A, cur.B, tid, wave, 0,
-                                    faa_half, fab, acc, prev_stores);
-      else
-        mainloop_pair<B_STRIDED, TM>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
-                                     sa3 + OP_BYTES, cur.A.origin, cur.B.origin, cur.A, cur.B, tid, wave, wm,
-                                     faa, fab, acc, prev_stores);
-    } else {
-      if (half)
-        mainloop<A_STRIDED, B_STRIDED, 2, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
-                                                smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
-                                                cur.B, tid, wave, faa_half, fab, acc, prev_stores);
-      else
-        mainloop<A_STRIDED, B_STRIDED, TM, WIDE>(smem, smem + STAGE_BYTES, smem + 2 * STAGE_BYTES,
-                                                 smem + 3 * STAGE_BYTES, cur.A.origin, cur.B.origin, cur.A,
-                                                 cur.B, tid, wave, faa, fab, acc, prev_stores);
     }
     const int64_t tn = t + gridDim.x;
     if (OUT_F32 && !STAGED_F32 && !scaled && !is_silu(MODE) && !is_fp8(MODE)) {
