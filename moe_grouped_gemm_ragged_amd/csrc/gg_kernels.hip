@@ -62,12 +62,12 @@
 // MFMA: v_mfma_f32_32x32x16_bf16, fp32 accumulation.  A workgroup is 8 waves
 // (2 x 4) over a 256 x 256 output tile; each wave owns 128 x 64, i.e. 4 x 2
 // MFMA blocks of 32 x 32 (128 accumulator registers per lane), so two waves
-// share each SIMD.  In the bf16 passes those two take turns (the ping-pong
-// loops): one issues a stage's 16 MFMAs back to back from fragments already
-// in its registers while the other reads its next fragments from LDS and
-// issues its share of the global->LDS loads, so a load that cannot issue yet
-// or an LDS read in flight holds up only the wave that is not computing.  The
-// fp8 forward interleaves loads with the MFMAs of both waves (mainloop8).
+// share each SIMD.  Those two take turns (the ping-pong loops): one issues a
+// stage's MFMAs back to back from fragments already in its registers while
+// the other reads its next fragments from LDS and issues its share of the
+// global->LDS loads, so a load that cannot issue yet or an LDS read in flight
+// holds up only the wave that is not computing.  The fp8 forward runs the
+// same schedule with v_mfma_scale_f32_32x32x64_f8f6f4 (mainloop8_pp).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -183,63 +183,15 @@ __device__ __forceinline__ void stage_barrier() {
 
 // ---- global -> LDS, one stage of one operand ------------------------------------
 
-// The 2 loads a thread issues for one operand stage.  Load j of wave w
-// fills LDS bytes [1024 (2 w + j), +1024) of the operand's stage tile; lane
-// i writes 16 bytes at 16 i.  Offsets beyond the record count read as zero.
+// A stage tile of one operand is 16 KB of LDS, written by the 4 waves of
+// one group with 4 direct-to-LDS loads each: load jj of the group's wave w
+// (0..3) fills bytes [4096 w + 1024 jj, +1024), lane i writing 16 bytes at
+// 16 i.  Offsets beyond the record count read as zero.
 struct DmaCtx {
   __amdgpu_buffer_rsrc_t rs;
   uint32_t voff;      // lane offset of load 0
   uint32_t step;      // extra byte offset per load (scalar offset)
 };
-
-template <bool STRIDED, int ESZ = 2, bool WIDE = false>
-__device__ __forceinline__ DmaCtx dma_ctx(const Operand& op, int q0, int tid) {
-  DmaCtx c;
-  // lane terms recomputed per stage (a few VALU ops) rather than hoisted and
-  // kept live across the unrolled main loop
-  const int lane = (int)opaque_v((uint32_t)(tid & 63));
-  const int w = tid >> 6;
-  if constexpr (STRIDED) {
-    // wave w fills half w mod 2 of block w / 2 (tile rows 64 (w / 2) ..):
-    // load j covers reduction rows 16 (w mod 2) + 8 j .. + 7; lane i: row
-    // 16 (w mod 2) + 8 j + i / 8, chunk position i mod 8, logical chunk
-    // (i mod 8) ^ 4 ((row / 2) mod 2) = (i mod 8) ^ 4 ((i / 16) mod 2).
-    // The range ends at the last reduction row.  WIDE: that row can lie
-    // 4 GB or more past this stage (a wgrad expert of 300k rows at k =
-    // 7168), which would wrap 32 bits.  A stage reads rows 0..31 of its
-    // origin only, so the range then stops at row 63 at most: every valid
-    // byte of those rows stays inside it, and it spans at most 2^27 bytes.
-    // Otherwise the host has bounded the whole span below 2^32.
-    const int left = op.red - q0;
-    int last = left - 1;
-    if constexpr (WIDE) last = last < 63 ? last : 63;
-    const uint32_t nrec = left > 0 ? (uint32_t)last * op.ld_bytes + op.row_tail : 0u;
-    c.rs = make_rsrc(op.origin + (int64_t)q0 * op.ld_bytes, nrec);
-    const int chunk = (lane & 7) ^ (4 * ((lane >> 4) & 1));
-    c.voff = (uint32_t)((lane >> 3) + 16 * (w & 1)) * op.ld_bytes + (uint32_t)(128 * (w >> 1) + 16 * chunk) +
-             (w >= 4 ? op.split : 0u);
-    c.step = 8u * op.ld_bytes;
-  } else {
-    // load j of wave w covers tile rows 32 w + 16 j .. + 15; lane i: row
-    // 32 w + 16 j + i / 4, chunk position i mod 4, logical chunk
-    // (i mod 4) ^ ((row / 4) mod 4) = (i mod 4) ^ ((i / 16) mod 4).  ESZ:
-    // bytes per element (2 bf16, 1 e4m3); a chunk is 16 bytes either way.
-    const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - (uint32_t)(ESZ * q0) : 0u;
-    c.rs = make_rsrc(op.origin + (int64_t)ESZ * q0, nrec);
-    const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
-    uint32_t v = (uint32_t)(32 * w + (lane >> 2)) * op.ld_bytes + 16u * (uint32_t)chunk;
-    if (q0 + (16 / ESZ) * chunk >= op.red) v = kOutOfRange;   // past the reduction end: zero
-    c.voff = v;
-    c.step = 16u * op.ld_bytes;
-  }
-  return c;
-}
-
-__device__ __forceinline__ void dma_load(const DmaCtx& c, uint8_t* lds_op, int wave, int j) {
-  // the wave's first 1 KB block of this tile, recomputed per use
-  const uint32_t wbase = opaque_s((uint32_t)uniform(2 * wave * 1024));
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, LDS_PTR(lds_op + wbase + 1024 * j), 16, c.voff, j * c.step, 0, 0);
-}
 
 // ---- LDS -> MFMA fragments ------------------------------------------------------
 
@@ -347,7 +299,7 @@ __device__ __forceinline__ void stage_barrier_vm() {
 }
 
 // Stores a wave issues for one fp32 output tile of TMA active row blocks
-// (store_tile<true, TMA> issues exactly this many, in or out of range).
+// (store_tile_f32<TMA> issues exactly this many, in or out of range).
 template <int TMA>
 constexpr int stores_f32() { return TMA * TN * 4; }
 
@@ -360,7 +312,7 @@ constexpr int stores_f32() { return TMA * TN * 4; }
 // in flight, then holds up only the wave that is not computing, and the
 // matrix core sees one uninterrupted MFMA stream after another.  Group g =
 // wm (waves 4 g .. 4 g + 3, one per SIMD) owns tile rows 128 g .. (64 g ..
-// for a half-height tile), as in the interleaved loop.
+// for a half-height tile).
 //
 // Steps alternate: in step 2s group 0 computes stage s while group 1 reads
 // stage s and loads B of stage s + 3; in step 2s + 1 group 1 computes stage
@@ -374,13 +326,29 @@ constexpr int stores_f32() { return TMA * TN * 4; }
 // each wave has at most the 8 loads of the two later stages in flight.
 //
 // A group's 4 loads per step fill its wave's 4 KB of the operand's 16 KB
-// stage tile (wave w of the group: LDS bytes [4096 w, +4096)), the same
-// placement the interleaved loop's 2 loads per wave of all 8 waves produce.
+// stage tile.
 
-// Lane offset of the group's load 0 for its wave w (0..3) of a group; load
-// jj (0..3) adds jj * step.  Equal to dma_ctx for virtual wave 2 w + jj / 2,
-// load jj mod 2.
-template <bool STRIDED, bool WIDE = false>
+// The load contexts of the group's wave w (0..3) for the stage whose first
+// reduction index is q0; load jj (0..3) adds jj * step.
+//   Reduction-contiguous (ESZ bytes per element: 2 bf16, 1 e4m3; a chunk is
+//   16 bytes either way): load jj covers tile rows 64 w + 16 jj .. + 15;
+//   lane i: row 64 w + 16 jj + i / 4, chunk position i mod 4, logical chunk
+//   (i mod 4) ^ ((row / 4) mod 4) = (i mod 4) ^ ((i / 16) mod 4).  Chunks
+//   past the reduction end read as zero.
+//   Reduction-strided: wave w covers tile rows 64 w .. + 63 (128 contiguous
+//   bytes of each reduction row; rows 128.. start op.split bytes further,
+//   the up half of a gate/up weight), load jj reduction rows 8 jj .. + 7;
+//   lane i: reduction row 8 jj + i / 8, chunk position i mod 8, logical
+//   chunk (i mod 8) ^ 4 ((i / 16) mod 2).  The range ends at the last
+//   reduction row.  WIDE: that row can lie 4 GB or more past this stage (a
+//   wgrad expert of 300k rows at k = 7168), which would wrap 32 bits.  A
+//   stage reads rows 0..31 of its origin only, so the range then stops at
+//   row 63 at most: every valid byte of those rows stays inside it, and it
+//   spans at most 2^27 bytes.  Otherwise the host has bounded the whole span
+//   below 2^32.
+// Lane terms are recomputed per stage (a few VALU ops) rather than hoisted
+// and kept live across the unrolled main loop.
+template <bool STRIDED, bool WIDE = false, int ESZ = 2>
 __device__ __forceinline__ DmaCtx dma_ctx_grp(const Operand& op, int q0, int lane_in, int w) {
   DmaCtx c;
   const int lane = (int)opaque_v((uint32_t)lane_in);
@@ -394,11 +362,11 @@ __device__ __forceinline__ DmaCtx dma_ctx_grp(const Operand& op, int q0, int lan
     c.voff = (uint32_t)(lane >> 3) * op.ld_bytes + (uint32_t)(128 * w + 16 * chunk) + (w >= 2 ? op.split : 0u);
     c.step = 8u * op.ld_bytes;
   } else {
-    const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - (uint32_t)(2 * q0) : 0u;
-    c.rs = make_rsrc(op.origin + (int64_t)2 * q0, nrec);
+    const uint32_t nrec = q0 < op.red ? (uint32_t)op.rows * op.ld_bytes - (uint32_t)(ESZ * q0) : 0u;
+    c.rs = make_rsrc(op.origin + (int64_t)ESZ * q0, nrec);
     const int chunk = (lane & 3) ^ ((lane >> 4) & 3);
     uint32_t v = (uint32_t)(64 * w + (lane >> 2)) * op.ld_bytes + 16u * (uint32_t)chunk;
-    if (q0 + 8 * chunk >= op.red) v = kOutOfRange;
+    if (q0 + (16 / ESZ) * chunk >= op.red) v = kOutOfRange;
     c.voff = v;
     c.step = 16u * op.ld_bytes;
   }
@@ -954,13 +922,25 @@ __device__ __forceinline__ i32x8 read_frag8_pair(const uint8_t* region, const Fr
   return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// The fp8 tile's loads in flight when its main loop starts, in this order:
-// the scales of k-block 0, X pair 0 (stages 0, 1), W stages 0 and 1, the
-// scales of k-block 1, X pair 1 (stages 2, 3), W stage 2.  X is staged in
-// the pair layout of the bf16 row passes, W one stage per slot; the scales
-// are loaded by waves 0 and 1 only.
-__device__ __attribute__((always_inline)) inline void prologue_loads8(
-    uint8_t* __restrict__ a0, uint8_t* __restrict__ a1, uint8_t* __restrict__ a2, uint8_t* __restrict__ a3,
+// ---- fp8 ping-pong main loop ---------------------------------------------------------
+//
+// The bf16 row passes' paired ping-pong schedule on e4m3 operands: X (A) in
+// the pair layout, W (B) one stage per slot, each group's waves taking turns
+// with a stage's 8 scaled MFMAs.  K is a multiple of 128, so A pair p (stages
+// 2p, 2p + 1) is exactly scale k-block p.  Waves 0 and 1 load the k-block's
+// X and W scale bytes into slot p mod 2 of the LDS scale ring as the first
+// load of the batch that brings group 0's half of the A pair, so the waits of
+// the bf16 schedule (vmcnt(4) where a group's next batch may still be in
+// flight) cover them unchanged; every wave reads its two scale dwords when it
+// reads the first stage of a k-block and keeps them for both stages.  The
+// prologue issues the first two k-blocks' scales ahead of everything else.
+
+// Loads in flight when the loop starts, in this order: group 0 (waves 0, 1
+// only) the scales of k-blocks 0 and 1, B of stage 0, its half of A pair 0,
+// B of stage 2, its half of A pair 1; group 1 its half of A pair 0, B of
+// stage 1.
+__device__ __attribute__((always_inline)) inline void prologue_loads8_pp(
+    uint8_t* __restrict__ a0, uint8_t* __restrict__ a1, uint8_t* __restrict__ a2,
     uint8_t* __restrict__ b0, uint8_t* __restrict__ b1, uint8_t* __restrict__ b2, uint8_t* __restrict__ sc,
     const uint8_t* __restrict__ a_origin, const uint8_t* __restrict__ b_origin,
     const uint8_t* __restrict__ sa_tile, const uint8_t* __restrict__ sb_tile, uint32_t sc_bytes, Operand A,
@@ -968,136 +948,167 @@ __device__ __attribute__((always_inline)) inline void prologue_loads8(
   A.origin = a_origin;
   B.origin = b_origin;
   const int lane = tid & 63;
-  const bool hi = wave >= 4;
-  scale_load(sa_tile, sb_tile, sc_bytes, 0, sc, wave, lane);
-  {
-    const DmaPair c = dma_pair<1>(A, 0, tid);
+  const int w = wave & 3;
+  if (wave < 4) {
+    scale_load(sa_tile, sb_tile, sc_bytes, 0, sc, wave, lane);
+    scale_load(sa_tile, sb_tile, sc_bytes, 1, sc + kScaleSlot, wave, lane);
+    {
+      const DmaCtx c = dma_ctx_grp<false, false, 1>(B, 0, lane, w);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) dma_load_pair(c, hi ? a1 : a0, wave, jj);
-  }
-  {
-    const DmaCtx c0 = dma_ctx<false, 1>(B, 0, tid);
-    dma_load(c0, b0, wave, 0);
-    dma_load(c0, b0, wave, 1);
-    const DmaCtx c1 = dma_ctx<false, 1>(B, BK8, tid);
-    dma_load(c1, b1, wave, 0);
-    dma_load(c1, b1, wave, 1);
-  }
-  scale_load(sa_tile, sb_tile, sc_bytes, 1, sc + kScaleSlot, wave, lane);
-  {
-    const DmaPair c = dma_pair<1>(A, 2 * BK8, tid);
+      for (int jj = 0; jj < 4; ++jj) dma_load_grp(c, b0, w, jj);
+    }
+    {
+      const DmaPair c = dma_pair<1>(A, 0, tid);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) dma_load_pair(c, hi ? a3 : a2, wave, jj);
-  }
-  {
-    const DmaCtx c2 = dma_ctx<false, 1>(B, 2 * BK8, tid);
-    dma_load(c2, b2, wave, 0);
-    dma_load(c2, b2, wave, 1);
+      for (int jj = 0; jj < 4; ++jj) dma_load_pair_s(c, a0, wave, jj);
+    }
+    {
+      const DmaCtx c = dma_ctx_grp<false, false, 1>(B, 2 * BK8, lane, w);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dma_load_grp(c, b2, w, jj);
+    }
+    {
+      const DmaPair c = dma_pair<1>(A, 2 * BK8, tid);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dma_load_pair_s(c, a2, wave, jj);
+    }
+  } else {
+    {
+      const DmaPair c = dma_pair<1>(A, 0, tid);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dma_load_pair_s(c, a1, wave, jj);
+    }
+    {
+      const DmaCtx c = dma_ctx_grp<false, false, 1>(B, BK8, lane, w);
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) dma_load_grp(c, b1, w, jj);
+    }
   }
 }
 
-// Loads per wave in flight after the first stage's when the fp8 loop starts:
-// W stage 1, X pair 1 and W stage 2 (waves 0 and 1 have one more, the
-// scales of k-block 1).
-constexpr int kPrologueLoads8 = 8;
-
-// The fp8 reduction loop: the bf16 row passes' schedule (W stage kt+3 loaded
-// in the first half-stage, wait and barrier, the X pair of stages kt+3, kt+4
-// in the second half of odd stages), with the MFMAs of a stage split by row
-// blocks instead of reduction halves (first half: blocks i < TMA/2).  The W
-// fragments of a stage serve both halves, so they are double-buffered across
-// stages (FB, NB); the X fragments of the first half of stage kt+1 are read
-// during the second half of stage kt, the rest after it.  Even stages also
-// issue (waves 0, 1) the scales of k-block kt/2 + 2, into the slot k-block
-// kt/2 used; odd stages read the next k-block's scales right after their
-// barrier.  Loads in flight at the waits: 8 in even stages and 4 in odd
-// ones, one more for waves 0 and 1 (a scale load).  ha: the pair-layout
-// region of the wave's X rows.
 template <int TMA>
-__device__ __attribute__((always_inline)) inline void mainloop8(
+__device__ __attribute__((always_inline)) inline void mainloop8_pp(
     uint8_t* __restrict__ a0, uint8_t* __restrict__ a1, uint8_t* __restrict__ a2, uint8_t* __restrict__ a3,
     uint8_t* __restrict__ b0, uint8_t* __restrict__ b1, uint8_t* __restrict__ b2, uint8_t* __restrict__ b3,
     uint8_t* __restrict__ sc, const uint8_t* __restrict__ a_origin, const uint8_t* __restrict__ b_origin,
     const uint8_t* __restrict__ sa_tile, const uint8_t* __restrict__ sb_tile, uint32_t sc_bytes, Operand A,
     Operand B, int tid, int wave, int wm, int wn, int ha, const FragAddr& faa, const FragAddr& fab,
     floatx16 (&acc)[TM][TN]) {
-  constexpr int kSub = TMA / 2 * TN;                 // MFMAs per half-stage
-  constexpr int kGap = kSub / 2 > 0 ? kSub / 2 : 1;
-  constexpr int kAt = 0;                            // W loads with MFMAs 0 and kGap (measured best)
-  constexpr int kItems = TMA / 2 + TN;              // fragments read during the second half
   A.origin = a_origin;
   B.origin = b_origin;
-  const int lane = tid & 63;
   const int nk = (A.red + BK8 - 1) / BK8;           // even: K is a multiple of 128
   if (nk <= 0) return;
-  const bool hi = wave >= 4;
-  i32x8 fa[TMA], fb0[TN], fb1[TN];
-  uint32_t sa0, sb0, sa1 = 0, sb1 = 0;
-  if (wave < 2) stage_barrier_vm<kPrologueLoads8 + 1>();
-  else stage_barrier_vm<kPrologueLoads8>();
-  scale_read<TMA>(sc, wm, wn, lane, sa0, sb0);
-#pragma unroll
-  for (int i = 0; i < TMA; ++i) fa[i] = read_frag8_pair(ha ? a1 : a0, faa, i, 0);
-#pragma unroll
-  for (int j = 0; j < TN; ++j) fb0[j] = read_frag8(b0, fab, j);
+  const int lane = tid & 63;
+  const int w = wave & 3;
+  const bool g0 = wave < 4;
+  const Regions rg = {{a0, a1, a2, a3, b0, b1, b2, b3}};
+  pp_regions_escape(rg);
+  const Regions rs = {{sc, sc, sc, sc, sc, sc, sc, sc}};
+  pp_regions_escape(rs);
+  i32x8 fa[TMA], fb[TN];
+  uint32_t sa = 0, sb = 0;
+  // group 0: the scales, B of stage 0 and its half of A pair 0 landed (the
+  // last 8 loads may be in flight); group 1 waits at the next barrier
+  if (g0) pp_sync<8>(rg); else pp_sync<kNoVm>(rg);
 
-// U = KT mod 4 (a literal): X of stage U in pair slots {0,1} or {2,3} (the
-// wave's half), parity U mod 2; W of stage U in slot U.
 #define GG8_RA(U) ((U) < 2 ? (ha ? a1 : a0) : (ha ? a3 : a2))
 #define GG8_RB(U) ((U) == 0 ? b0 : (U) == 1 ? b1 : (U) == 2 ? b2 : b3)
-#define GG8_STAGE(U, KT, FB, NB, SA, SB, SLOT, SA_N, SB_N)                                 \
-  {                                                                                       \
-    constexpr bool kOdd = ((U) & 1) == 1;                                                 \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    const DmaCtx cb = dma_ctx<false, 1>(B, ((KT) + 3) * BK8, tid);                        \
-    _Pragma("unroll") for (int q = 0; q < kSub; ++q) {                                    \
-      const int i = q / TN, j = q % TN;                                                   \
-      acc[i][j] = mfma8(i, j, FB[j], fa[i], acc[i][j], SA, SB);                           \
-      if (q % kGap == kAt && q / kGap < 2) dma_load(cb, GG8_RB(((U) + 3) & 3), wave, q / kGap); \
-      __builtin_amdgcn_sched_barrier(0);                                                  \
-    }                                                                                     \
-    mfma_fence(acc);                                                                      \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    if (!kOdd) { if (wave < 2) stage_barrier_vm<9>(); else stage_barrier_vm<8>(); }       \
-    else { if (wave < 2) stage_barrier_vm<5>(); else stage_barrier_vm<4>(); }             \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    if (!kOdd) scale_load(sa_tile, sb_tile, sc_bytes, (KT) / 2 + 2, sc + (SLOT) * kScaleSlot, wave, lane); \
-    if (kOdd) scale_read<TMA>(sc + (SLOT) * kScaleSlot, wm, wn, lane, SA_N, SB_N);        \
-    DmaPair cp;                                                                           \
-    if constexpr (kOdd) cp = dma_pair<1>(A, ((KT) + 3) * BK8, tid);                       \
-    _Pragma("unroll") for (int q = 0; q < kSub; ++q) {                                    \
-      const int i = TMA / 2 + q / TN, j = q % TN;                                         \
-      acc[i][j] = mfma8(i, j, FB[j], fa[i], acc[i][j], SA, SB);                           \
-      if constexpr (kOdd) {                                                               \
-        _Pragma("unroll") for (int jj = q * 4 / kSub; jj < (q + 1) * 4 / kSub; ++jj)      \
-          dma_load_pair(cp, (U) == 1 ? (hi ? a1 : a0) : (hi ? a3 : a2), wave, jj);        \
-      }                                                                                   \
-      if (q < TMA / 2) fa[q] = read_frag8_pair(GG8_RA(((U) + 1) & 3), faa, q, ((U) + 1) & 1); \
-      else if (q < kItems) NB[q - TMA / 2] = read_frag8(GG8_RB(((U) + 1) & 3), fab, q - TMA / 2); \
-      __builtin_amdgcn_sched_barrier(0);                                                  \
-    }                                                                                     \
-    mfma_fence(acc);                                                                      \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
-    _Pragma("unroll") for (int q = kSub; q < kItems; ++q) {                               \
-      if (q < TMA / 2) fa[q] = read_frag8_pair(GG8_RA(((U) + 1) & 3), faa, q, ((U) + 1) & 1); \
-      else NB[q - TMA / 2] = read_frag8(GG8_RB(((U) + 1) & 3), fab, q - TMA / 2);        \
-    }                                                                                     \
-    _Pragma("unroll") for (int i = TMA / 2; i < TMA; ++i)                                 \
-      fa[i] = read_frag8_pair(GG8_RA(((U) + 1) & 3), faa, i, ((U) + 1) & 1);              \
-    __builtin_amdgcn_sched_barrier(0);                                                    \
+// read stage U's fragments (and, for the first stage of a k-block, its
+// scales from slot (U / 2) mod 2 of the ring)
+#define GG8_PP_READ(U)                                                                            \
+  {                                                                                               \
+    if (((U) & 1) == 0) scale_read<TMA>(sc + (((U) >> 1) & 1) * kScaleSlot, wm, wn, lane, sa, sb); \
+    _Pragma("unroll") for (int i = 0; i < TMA; ++i) fa[i] = read_frag8_pair(GG8_RA(U), faa, i, (U) & 1); \
+    _Pragma("unroll") for (int j = 0; j < TN; ++j) fb[j] = read_frag8(GG8_RB(U), fab, j);        \
+  }
+#define GG8_PP_MFMA()                                                                             \
+  {                                                                                               \
+    _Pragma("unroll") for (int q = 0; q < TMA * TN; ++q) {                                        \
+      const int i = q / TN, j = q % TN;                                                           \
+      acc[i][j] = mfma8(i, j, fb[j], fa[i], acc[i][j], sa, sb);                                   \
+    }                                                                                             \
+    mfma_fence(acc);                                                                              \
+  }
+#define GG8_PP_LOAD_B(U, Q)                                                                       \
+  {                                                                                               \
+    const DmaCtx cb = dma_ctx_grp<false, false, 1>(B, (Q) * BK8, lane, w);                        \
+    _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) dma_load_grp(cb, GG8_RB(U), w, jj);           \
+  }
+#define GG8_PP_LOAD_A(R, Q)                                                                       \
+  {                                                                                               \
+    const DmaPair cp = dma_pair<1>(A, (Q) * BK8, tid);                                            \
+    _Pragma("unroll") for (int jj = 0; jj < 4; ++jj) dma_load_pair_s(cp, (R), wave, jj);          \
   }
 
-  for (int kt = 0; kt < nk; kt += 4) {
-    GG8_STAGE(0, kt, fb0, fb1, sa0, sb0, 0, sa1, sb1)
-    GG8_STAGE(1, kt + 1, fb1, fb0, sa0, sb0, 1, sa1, sb1)
-    if (kt + 2 < nk) {
-      GG8_STAGE(2, kt + 2, fb0, fb1, sa1, sb1, 1, sa0, sb0)
-      GG8_STAGE(3, kt + 3, fb1, fb0, sa1, sb1, 0, sa0, sb0)
-    }
+  if (g0) {
+    GG8_PP_READ(0)
+    __builtin_amdgcn_sched_barrier(0);
+    pp_sync<kNoVm>(rg);
+    // stage KT = kt + U: compute it, then read stage KT + 1 and load (U even)
+    // B of stage KT + 4 into slot U or (U odd) the scales of k-block
+    // (KT + 3) / 2 and this group's half of its A pair into slot (U + 3) mod 4
+#define GG8_PP_STAGE0(U, KT)                                                                      \
+  {                                                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    GG8_PP_MFMA()                                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    if ((U) & 1) pp_sync<4>(rg); else pp_sync<kNoVm>(rg);                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    GG8_PP_READ(((U) + 1) & 3)                                                                    \
+    if (((U) & 1) == 0) GG8_PP_LOAD_B(U, (KT) + 4)                                                \
+    else {                                                                                        \
+      scale_load(sa_tile, sb_tile, sc_bytes, ((KT) + 3) / 2, sc + ((((KT) + 3) / 2) & 1) * kScaleSlot, \
+                 wave, lane);                                                                     \
+      GG8_PP_LOAD_A((U) == 1 ? a0 : a2, (KT) + 3)                                                 \
+    }                                                                                             \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    pp_sync<kNoVm>(rg);                                                                           \
   }
-#undef GG8_STAGE
-#undef GG8_RA
+    for (int kt = 0; kt < nk; kt += 4) {
+      GG8_PP_STAGE0(0, kt)
+      GG8_PP_STAGE0(1, kt + 1)
+      if (kt + 2 < nk) {
+        GG8_PP_STAGE0(2, kt + 2)
+        GG8_PP_STAGE0(3, kt + 3)
+      }
+    }
+#undef GG8_PP_STAGE0
+  } else {
+    // this group's half of A pair 0 landed (B of stage 1 may be in flight)
+    __builtin_amdgcn_sched_barrier(0);
+    pp_sync<4>(rg);
+    // stage KT = kt + U: read it and load (U even) this group's half of the A
+    // pair of stages KT + 2, KT + 3 into slot (U + 3) mod 4 or (U odd) B of
+    // stage KT + 2 into slot (U + 2) mod 4; then compute it
+#define GG8_PP_STAGE1(U, KT)                                                                      \
+  {                                                                                               \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    GG8_PP_READ(U)                                                                                \
+    if (((U) & 1) == 0) GG8_PP_LOAD_A((U) == 0 ? a3 : a1, (KT) + 2)                               \
+    else GG8_PP_LOAD_B(((U) + 2) & 3, (KT) + 2)                                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    if (((U) & 1) == 0) pp_sync<4>(rg); else pp_sync<kNoVm>(rg);                                   \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    GG8_PP_MFMA()                                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                            \
+    if ((U) & 1) pp_sync<4>(rg); else pp_sync<kNoVm>(rg);                                          \
+  }
+    for (int kt = 0; kt < nk; kt += 4) {
+      GG8_PP_STAGE1(0, kt)
+      GG8_PP_STAGE1(1, kt + 1)
+      if (kt + 2 < nk) {
+        GG8_PP_STAGE1(2, kt + 2)
+        GG8_PP_STAGE1(3, kt + 3)
+      }
+    }
+#undef GG8_PP_STAGE1
+  }
+#undef GG8_PP_LOAD_A
+#undef GG8_PP_LOAD_B
+#undef GG8_PP_MFMA
+#undef GG8_PP_READ
 #undef GG8_RB
+#undef GG8_RA
 }
 
 // ---- epilogue --------------------------------------------------------------------
@@ -1522,7 +1533,7 @@ struct Tile {
 // STAGED_F32: fp32 output through the LDS epilogue even when unscaled (the
 // host picks it for wgrad on short experts; see launch()).  WIDE (wgrad
 // only): an expert's rows may span 4 GB or more of X or dY, so the load
-// ranges are capped per stage (see dma_ctx); the host picks it from m.
+// ranges are capped per stage (see dma_ctx_grp); the host picks it from m.
 template <int MODE, bool OUT_F32, bool STAGED_F32 = false, bool WIDE = false>
 __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   static_assert(!WIDE || is_wgrad(MODE), "only wgrad reads an operand down a data-dependent span");
@@ -1530,7 +1541,7 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   constexpr bool B_STRIDED = !is_dgrad(MODE) && !is_fp8(MODE);
   // Main loops: the bf16 row passes ping-pong with A in the pair layout,
   // wgrad ping-pongs with one stage per slot for both operands, the fp8
-  // forward interleaves (mainloop8).
+  // forward runs the row passes' schedule on bytes (mainloop8_pp).
   constexpr bool PP_PAIR = !is_wgrad(MODE) && !is_fp8(MODE);
 
   // LDS: NSTAGE stage buffers of 32 KB (A tile, then B tile); fp8: two
@@ -1721,8 +1732,8 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
   auto issue_prologue = [&](const Tile& T) __attribute__((always_inline)) {
     if (T.A.red > 0) {
       if constexpr (is_fp8(MODE))
-        prologue_loads8(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES, s_sc, T.A.origin,
-                        T.B.origin, T.sa, T.sb, (uint32_t)(p.k / 128 * 256), T.A, T.B, tid, wave);
+        prologue_loads8_pp(sa0, sa1, sa2, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES, s_sc, T.A.origin,
+                           T.B.origin, T.sa, T.sb, (uint32_t)(p.k / 128 * 256), T.A, T.B, tid, wave);
       else if constexpr (PP_PAIR)
         prologue_loads_pp_pair<B_STRIDED>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES,
                                           T.A.origin, T.B.origin, T.A, T.B, tid, wave);
@@ -1761,13 +1772,13 @@ __global__ __launch_bounds__(NT, 1) void grouped_gemm_kernel(Params p) {
     if constexpr (is_fp8(MODE)) {
       const uint32_t sc_bytes = (uint32_t)(p.k / 128 * 256);
       if (half)
-        mainloop8<2>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES, sa3 + OP_BYTES, s_sc,
-                     cur.A.origin, cur.B.origin, cur.sa, cur.sb, sc_bytes, cur.A, cur.B, tid, wave, wm, wn, 0,
-                     faa_half, fab, acc);
+        mainloop8_pp<2>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES, sa3 + OP_BYTES,
+                        s_sc, cur.A.origin, cur.B.origin, cur.sa, cur.sb, sc_bytes, cur.A, cur.B, tid, wave, wm,
+                        wn, 0, faa_half, fab, acc);
       else
-        mainloop8<TM>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES, sa3 + OP_BYTES, s_sc,
-                      cur.A.origin, cur.B.origin, cur.sa, cur.sb, sc_bytes, cur.A, cur.B, tid, wave, wm, wn, wm,
-                      faa, fab, acc);
+        mainloop8_pp<TM>(sa0, sa1, sa2, sa3, sa0 + OP_BYTES, sa1 + OP_BYTES, sa2 + OP_BYTES, sa3 + OP_BYTES,
+                         s_sc, cur.A.origin, cur.B.origin, cur.sa, cur.sb, sc_bytes, cur.A, cur.B, tid, wave, wm,
+                         wn, wm, faa, fab, acc);
     } else if constexpr (PP_PAIR) {
       // the wave's A rows: 128 wm.. (full height, region wm) or 64 wm.. (half, region 0)
       if (half)
