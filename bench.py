@@ -42,15 +42,41 @@ PEAK_FP8_TFLOPS = 5033.2       # the same with e4m3 operands (8192 FLOP/clk/CU, 
 PEAK_HBM_GBS = 8000.0
 KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_ragged_amd", "csrc", "gg_kernels.hip")
 
-# HBM bytes per launch of each pass of the workload, from rocprofv3 --pmc
-# FETCH_SIZE and WRITE_SIZE runs of `bench.py --profile-pass P`, each divided
-# by the factor the same counter reads for `bench.py --copy-calibration`.
-# Valid only for the kernel source they were taken on (sha256 below); for any
-# other source the roofline reports traffic as null.
-MEASURED_TRAFFIC = {
+# Counter readings of the kernel, from rocprofv3 --pmc runs of
+# `bench.py --profile-pass P --profile-workload W` (the summaries under
+# profiles/ give the commands and every reading):
+#   traffic: HBM-side bytes per launch, FETCH_SIZE and WRITE_SIZE each divided
+#     by the factor the same counter reads for `bench.py --copy-calibration`;
+#   clock_GHz: sustained shader clock, GRBM_GUI_ACTIVE / 8 XCDs / kernel time;
+#   mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles per XCD).
+# Last dispatch of each run.  Valid only for the kernel source they were
+# taken on (sha256 below); for any other source these fields are null.
+MEASURED = {
     "kernel_sha256": "fd91abfe4730992ba492957464a1800b0926314edad94b890b44730992a8f526",
-    "bytes": {"fwd": 23613423734, "dgrad": 25322833866, "wgrad": 23794400172},
+    "glm_up": {"fwd": {"traffic": 23613423734, "clock_GHz": 1.668, "mfma_busy": 0.695},
+               "dgrad": {"traffic": 25322833866, "clock_GHz": 1.666, "mfma_busy": 0.681},
+               "wgrad": {"traffic": 23794400172, "clock_GHz": 1.663, "mfma_busy": 0.681}},
 }
+NOMINAL_CLOCK_GHZ = 2.4
+
+
+def measured(workload, pass_, key):
+    """A counter reading of MEASURED for this kernel source, else None."""
+    if MEASURED["kernel_sha256"] != kernel_sha256():
+        return None
+    return MEASURED.get(workload, {}).get(pass_, {}).get(key)
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def kernel_sha256():
@@ -180,6 +206,7 @@ def cpu_baseline(wl, t, synth, budget_s=15.0):
         "value": flops / secs / 1e12,
         "unit": "TFLOP/s",
         "cores": oracle.num_threads(),
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{wl.name}, {'; '.join(parts)}; {flops / 1e9:.1f} GFLOP in {secs:.1f} s",
     }
@@ -259,6 +286,12 @@ def main():
         per_pass[name] = {"ms": round(avg, 4), "TFLOP/s": round(tf, 2),
                           "frac_of_mfma_peak": round(tf / PEAK_BF16_TFLOPS, 4),
                           "algorithmic_GB/s": round(algorithmic_bytes(wl, name) / (avg * 1e-3) / 1e9, 1)}
+        # frac_of_mfma_peak ~ (clock / 2.4 GHz) x MFMA busy, from the counters
+        clk, busy = measured(wl.name, name, "clock_GHz"), measured(wl.name, name, "mfma_busy")
+        per_pass[name]["sustained_clock_GHz"] = clk
+        per_pass[name]["mfma_busy"] = busy
+        per_pass[name]["clock_x_busy"] = (round(clk / NOMINAL_CLOCK_GHZ * busy, 4)
+                                          if clk is not None and busy is not None else None)
     dom = max(per_pass, key=lambda k: per_pass[k]["ms"])
     kernel_names = {"fwd": "grouped_gemm_kernel<0,false,false,false>", "dgrad": "grouped_gemm_kernel<1,false,false,false>",
                     "wgrad": "grouped_gemm_kernel<2,true,false,false>"}
@@ -270,9 +303,7 @@ def main():
                                     "TFLOP/s": round(flop_pass / (acc_ms * 1e-3) / 1e12, 2),
                                     "note": "dW += X^T dY into fp32 (gg_wgrad_ex, beta = 1); not in the step"}
 
-    traffic = None
-    if MEASURED_TRAFFIC["kernel_sha256"] == kernel_sha256():
-        traffic = MEASURED_TRAFFIC["bytes"].get(dom)
+    traffic = measured(wl.name, dom, "traffic")
     roofline = {
         "bound": "mfma",
         "kernel": f"{kernel_names[dom]} ({dom})",
@@ -300,9 +331,13 @@ def main():
             entry = {}
             for p, v in ms2.items():
                 avg = sorted(v)[len(v) // 2]
-                entry[p] = {"ms": round(avg, 4),
-                            "TFLOP/s": round(w2.flops() / (avg * 1e-3) / 1e12, 2),
-                            "algorithmic_GB/s": round(algorithmic_bytes(w2, p) / (avg * 1e-3) / 1e9, 1)}
+                gbs = algorithmic_bytes(w2, p) / (avg * 1e-3) / 1e9
+                tf2 = w2.flops() / (avg * 1e-3) / 1e12
+                entry[p] = {"ms": round(avg, 4), "TFLOP/s": round(tf2, 2),
+                            "frac_of_mfma_peak": round(tf2 / PEAK_BF16_TFLOPS, 4),
+                            "algorithmic_GB/s": round(gbs, 1),
+                            "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                            "traffic": measured(name, p, "traffic")}
             context[name] = entry
             del t2, y2, dx2, dw2
         # masked down-projection: forward and backward.  Its weights (201 MB)
@@ -331,8 +366,9 @@ def main():
         entry = {"weights": "rotated over 3 copies (HBM-resident per call)"}
         for name, v in msm.items():
             avg = sorted(v)[len(v) // 2]
+            gbs = mb[name] / (avg * 1e-3) / 1e9
             entry[name] = {"ms": round(avg, 4), "TFLOP/s": round(wm.flops() / (avg * 1e-3) / 1e12, 2),
-                           "algorithmic_GB/s": round(mb[name] / (avg * 1e-3) / 1e9, 1)}
+                           "algorithmic_GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4)}
         context["masked_down"] = entry
         del tm, wcopies, ym, dxm, dwm
         torch.cuda.empty_cache()
@@ -458,9 +494,11 @@ def main():
             live8 = int((w8.group_sizes() > 0).sum())
             ab8 = act * w8.k + live8 * w8.n * w8.k + 2 * act * w8.n
             tf8 = w8.flops() / (f8["fwd"] * 1e-3) / 1e12
+            gb8 = ab8 / (f8["fwd"] * 1e-3) / 1e9
             context[name] = {"fwd": {"ms": round(f8["fwd"], 4), "TFLOP/s": round(tf8, 2),
                                      "frac_of_fp8_mfma_peak": round(tf8 / PEAK_FP8_TFLOPS, 4),
-                                     "algorithmic_GB/s": round(ab8 / (f8["fwd"] * 1e-3) / 1e9, 1)},
+                                     "algorithmic_GB/s": round(gb8, 1),
+                                     "frac_of_hbm": round(gb8 / PEAK_HBM_GBS, 4)},
                              "pack_x_scales_ms": round(f8["pack"], 4)}
             if masked:
                 context[name]["weights"] = "rotated over 3 copies (HBM-resident per call)"
