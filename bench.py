@@ -52,10 +52,16 @@ KERNEL_SRC = os.path.join(ROOT, "moe_grouped_gemm_ragged_amd", "csrc", "gg_kerne
 # Last dispatch of each run.  Valid only for the kernel source they were
 # taken on (sha256 below); for any other source these fields are null.
 MEASURED = {
-    "kernel_sha256": "fd91abfe4730992ba492957464a1800b0926314edad94b890b44730992a8f526",
-    "glm_up": {"fwd": {"traffic": 23613423734, "clock_GHz": 1.668, "mfma_busy": 0.695},
-               "dgrad": {"traffic": 25322833866, "clock_GHz": 1.666, "mfma_busy": 0.681},
-               "wgrad": {"traffic": 23794400172, "clock_GHz": 1.663, "mfma_busy": 0.681}},
+    "kernel_sha256": "cc49d2c4205d349ab6865bd0f255484b1674667b43355bccf8eb15336978ba5d",
+    "glm_up": {"fwd": {"traffic": 23623406989, "clock_GHz": 1.564, "mfma_busy": 0.791},
+              "dgrad": {"traffic": 28929209119, "clock_GHz": 1.582, "mfma_busy": 0.757},
+              "wgrad": {"traffic": 23134283872, "clock_GHz": 1.576, "mfma_busy": 0.801}},
+    "qwen3_gateup": {"fwd": {"traffic": 1853467875, "clock_GHz": 1.954, "mfma_busy": 0.491},
+                    "dgrad": {"traffic": 1901057487, "clock_GHz": 1.772, "mfma_busy": 0.461},
+                    "wgrad": {"traffic": 2375981198, "clock_GHz": 1.915, "mfma_busy": 0.304}},
+    "dsv3": {"fwd": {"traffic": 8458537885},
+            "dgrad": {"traffic": 9091197942},
+            "wgrad": {"traffic": 16687648838}},
 }
 NOMINAL_CLOCK_GHZ = 2.4
 
@@ -337,7 +343,9 @@ def main():
                             "frac_of_mfma_peak": round(tf2 / PEAK_BF16_TFLOPS, 4),
                             "algorithmic_GB/s": round(gbs, 1),
                             "frac_of_hbm": round(gbs / PEAK_HBM_GBS, 4),
-                            "traffic": measured(name, p, "traffic")}
+                            "traffic": measured(name, p, "traffic"),
+                            "sustained_clock_GHz": measured(name, p, "clock_GHz"),
+                            "mfma_busy": measured(name, p, "mfma_busy")}
             context[name] = entry
             del t2, y2, dx2, dw2
         # masked down-projection: forward and backward.  Its weights (201 MB)
