@@ -25,12 +25,12 @@
 //
 // Data path (no register staging): every operand tile goes from global
 // memory straight into LDS with buffer loads in LDS mode (16 bytes per lane,
-// 1 KB per wave instruction), one 32-deep reduction stage at a time, through
-// a ring of 4 LDS stages, loads running 3 to 6 half-stages ahead of their
-// first reader.  In the bf16 row passes the A operand is staged two stages
-// at a time instead, so that its loads read whole cache lines (the pair
-// layout, stated with dma_pair).  Each operand keeps its memory layout in
-// LDS:
+// 1 KB per wave instruction), one 64-byte-deep reduction stage at a time
+// (32 bf16 or 64 e4m3 values), through a ring of 4 LDS slots, each load
+// issued 3 to 6 ping-pong steps before its first reader.  In the row passes the A
+// operand is staged two stages at a time instead, so that its loads read
+// whole cache lines (the pair layout, stated with dma_pair).  Each operand
+// keeps its memory layout in LDS:
 //   red-contig  : 256 tile rows x 64 bytes (32 reduction values), the
 //                 16-byte chunk c of row r at position c ^ ((r / 4) mod 4);
 //                 MFMA fragments come from ds_read_b128.
