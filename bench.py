@@ -23,6 +23,10 @@ Profiling helpers (each prints one JSON line of its own, not the bench line):
   --copy-calibration                run a plain device-to-device copy of known
                                     size, to scale the FETCH_SIZE / WRITE_SIZE
                                     counters into bytes
+  --tile-cost                       time the forward on uniform-expert shapes at
+                                    Qwen3's N: full- against half-height tiles,
+                                    and a reduction-length sweep that separates a
+                                    tile's fixed cost from its per-stage time
 """
 from __future__ import annotations
 
@@ -218,6 +222,45 @@ def cpu_baseline(wl, t, synth, budget_s=15.0):
     }
 
 
+def tile_cost(gg, synth, torch, dev, n=1536, experts=256, cus=256):
+    """Forward time per output tile on uniform experts (every expert the same
+    size, 256-column tiles at n = 1536): 256-row experts (one full-height tile
+    each), 192 rows (one full-height tile, partly empty), 128 rows (one
+    half-height tile), all at k = 2048; and 256-row experts at k = 512 ..
+    4096, whose least-squares line in the stage count (k / 32) gives a tile's
+    fixed cost (intercept) and its time per stage (slope).  Times are per
+    workgroup: launch time x CUs / tiles."""
+    import numpy as np
+    col_tiles = (n + 255) // 256
+    out = {"n": n, "experts": experts, "col_tiles": col_tiles, "shapes": []}
+
+    def run(rows, k):
+        wl = synth.custom_ragged(f"uniform_{rows}x{k}", [rows] * experts, k=k, n=n, seed=77)
+        t = synth.make_inputs(wl, dev, need=("x", "w"))
+        y = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device=dev)
+        _, ms = time_passes([("fwd", lambda: gg.forward(t["x"], t["w"], t["offs"], out=y))], 20, 3, torch)
+        med = sorted(ms["fwd"])[len(ms["fwd"]) // 2]
+        tiles = experts * col_tiles
+        e = {"rows": rows, "k": k, "stages": k // 32, "ms": round(med, 4), "tiles_per_cu": tiles / cus,
+             "us_per_tile": round(med * 1e3 * cus / tiles, 2),
+             "TFLOP/s": round(wl.flops() / (med * 1e-3) / 1e12, 1)}
+        out["shapes"].append(e)
+        del t, y
+        return e
+    full = run(256, 2048)
+    run(192, 2048)
+    half = run(128, 2048)
+    out["half_over_full_tile_time"] = round(half["us_per_tile"] / full["us_per_tile"], 3)
+    sweep = [full] + [run(256, k) for k in (512, 1024, 4096)]
+    st = np.array([e["stages"] for e in sweep], dtype=float)
+    us = np.array([e["us_per_tile"] for e in sweep])
+    slope, icpt = np.polyfit(st, us, 1)
+    out["fit_us_per_stage"] = round(float(slope), 4)
+    out["fit_fixed_us_per_tile"] = round(float(icpt), 2)
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -233,6 +276,8 @@ def main():
                     help="the workload --profile-pass runs (default glm_up, the bench workload)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain copy of known size (counter calibration) and exit")
+    ap.add_argument("--tile-cost", action="store_true",
+                    help="time full- against half-height tiles and a reduction sweep, then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -257,6 +302,10 @@ def main():
                                                "launches": args.warmup + args.steps,
                                                "ms": round(sum(msc["copy"]) / len(msc["copy"]), 4)}}),
               flush=True)
+        return
+
+    if args.tile_cost:
+        print(json.dumps({"tile_cost": tile_cost(gg, synth, torch, dev)}), flush=True)
         return
 
     wl = synth.by_name(args.profile_workload) if args.profile_pass else synth.glm_up()
