@@ -228,20 +228,23 @@ def tile_cost(gg, synth, torch, dev, n=1536, experts=256, cus=256):
     each), 192 rows (one full-height tile, partly empty), 128 rows (one
     half-height tile), all at k = 2048; and 256-row experts at k = 512 ..
     4096, whose least-squares line in the stage count (k / 32) gives a tile's
-    fixed cost (intercept) and its time per stage (slope).  Times are per
-    workgroup: launch time x CUs / tiles."""
+    fixed cost (intercept) and its time per stage (slope), for bf16 output
+    (stored through LDS) and fp32 output (stored straight from the
+    accumulators, overlapped with the next tile's first loads).  Times are
+    per workgroup: launch time x CUs / tiles."""
     import numpy as np
     col_tiles = (n + 255) // 256
     out = {"n": n, "experts": experts, "col_tiles": col_tiles, "shapes": []}
 
-    def run(rows, k):
+    def run(rows, k, out_dtype=torch.bfloat16):
         wl = synth.custom_ragged(f"uniform_{rows}x{k}", [rows] * experts, k=k, n=n, seed=77)
         t = synth.make_inputs(wl, dev, need=("x", "w"))
-        y = torch.empty((wl.m, wl.n), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((wl.m, wl.n), dtype=out_dtype, device=dev)
         _, ms = time_passes([("fwd", lambda: gg.forward(t["x"], t["w"], t["offs"], out=y))], 20, 3, torch)
         med = sorted(ms["fwd"])[len(ms["fwd"]) // 2]
         tiles = experts * col_tiles
-        e = {"rows": rows, "k": k, "stages": k // 32, "ms": round(med, 4), "tiles_per_cu": tiles / cus,
+        e = {"rows": rows, "k": k, "out": str(out_dtype).replace("torch.", ""), "stages": k // 32,
+             "ms": round(med, 4), "tiles_per_cu": tiles / cus,
              "us_per_tile": round(med * 1e3 * cus / tiles, 2),
              "TFLOP/s": round(wl.flops() / (med * 1e-3) / 1e12, 1)}
         out["shapes"].append(e)
@@ -251,12 +254,14 @@ def tile_cost(gg, synth, torch, dev, n=1536, experts=256, cus=256):
     run(192, 2048)
     half = run(128, 2048)
     out["half_over_full_tile_time"] = round(half["us_per_tile"] / full["us_per_tile"], 3)
-    sweep = [full] + [run(256, k) for k in (512, 1024, 4096)]
-    st = np.array([e["stages"] for e in sweep], dtype=float)
-    us = np.array([e["us_per_tile"] for e in sweep])
-    slope, icpt = np.polyfit(st, us, 1)
-    out["fit_us_per_stage"] = round(float(slope), 4)
-    out["fit_fixed_us_per_tile"] = round(float(icpt), 2)
+    for dt, sweep in ((torch.bfloat16, [full] + [run(256, k) for k in (512, 1024, 4096)]),
+                      (torch.float32, [run(256, k, torch.float32) for k in (512, 1024, 2048, 4096)])):
+        st = np.array([e["stages"] for e in sweep], dtype=float)
+        us = np.array([e["us_per_tile"] for e in sweep])
+        slope, icpt = np.polyfit(st, us, 1)
+        tag = str(dt).replace("torch.", "")
+        out[f"fit_{tag}_us_per_stage"] = round(float(slope), 4)
+        out[f"fit_{tag}_fixed_us_per_tile"] = round(float(icpt), 2)
     torch.cuda.empty_cache()
     return out
 
