@@ -12,8 +12,9 @@
 * edge cases: empty experts, one-row experts, a ragged row tail, k = 128
   (one scale block), a column tail, half-height last tiles;
 * the full-size masked down and gate/up projections of the page's operand
-  table and the fp8 GLM-up shape, on sampled rows, in the benchmark's
-  launch configuration.
+  table, every element, and the Qwen3 gate/up and GLM-up shapes on sampled
+  rows (every expert's first and last rows and its tile boundaries, plus
+  random rows), in the benchmark's launch configuration.
 Tolerance: parity.check_fp8.
 """
 import numpy as np
@@ -217,8 +218,7 @@ def _sample_rows(wl, rng, count):
     return np.unique(np.asarray(picks, dtype=np.int64))
 
 
-@pytest.mark.parametrize("name,count", [("fp8_masked_down", 120), ("fp8_masked_gateup", 120),
-                                        ("fp8_glm_up", 24)])
+@pytest.mark.parametrize("name,count", [("fp8_qwen3_gateup", 1024), ("fp8_glm_up", 24)])
 def test_fp8_forward_full_size_sampled(name, count):
     dev = device()
     import torch
@@ -239,6 +239,35 @@ def test_fp8_forward_full_size_sampled(name, count):
     rep = Report()
     check_fp8(yh, ref.value, ref.sabs, wl.k, f"fp8 {name} sampled", rep)
     print(name, len(rows), "rows", rep)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["fp8_masked_down", "fp8_masked_gateup"])
+def test_fp8_forward_full_size_every_element(name):
+    """The masked down and gate/up projections of the page's operand table at
+    full size, in the benchmark's launch configuration, compared element by
+    element with the oracle in row chunks; inactive rows keep the sentinel."""
+    dev = device()
+    import torch
+    wl = synth.by_name(name)
+    say("fp8 full-size every element", name, "drawing inputs")
+    t = synth.make_fp8_inputs(wl, dev)
+    y = sentinel_tensor(out_shape(wl), torch.bfloat16, dev)
+    say("fp8 full-size every element", name)
+    run_fp8(wl, t, y)
+    torch.cuda.synchronize()
+    yh = host(y).reshape(-1, wl.n)
+    total = yh.shape[0]
+    rep = Report()
+    for r0 in range(0, total, 8192):
+        rows = np.arange(r0, min(r0 + 8192, total))
+        ref = oracle_fp8(wl, t, rows=rows)
+        used = ref.status == 1
+        g = yh[rows]
+        check_fp8(g[used], ref.value[used], ref.sabs[used], wl.k, f"fp8 {name} rows {r0}..", rep)
+        assert np.all(raw_bits(g[~used]) == sentinel_bits(y.dtype)), f"{name}: a row outside the experts was written"
+    assert rep.n == int(wl.group_sizes().sum()) * wl.n
+    print(name, rep)
 
 
 @pytest.mark.parametrize("mm,max_m,k,n", [
