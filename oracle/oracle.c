@@ -372,18 +372,27 @@ static double e4m3_decode(uint8_t b) {
 
 double oracle_decode_e4m3(uint8_t b) { return e4m3_decode(b); }
 
+/* The 256 e4m3 values, e4m3_decode of each code (a lookup for the row
+ * loops below; the same values). */
+static double e4m3_table[256];
+static void e4m3_table_init(void) {
+    for (int c = 0; c < 256; ++c) e4m3_table[c] = e4m3_decode((uint8_t)c);
+}
+
 /* One output row of the fp8 forward: xr, sxr the row's values and scales,
- * wg, swg the expert's weight [n, k] and scales [n, kb]. */
+ * wg, swg the expert's weight [n, k] and scales [n, kb]; xs is room for k
+ * doubles.  The row's scaled values x(i, kk) sx[i, kk / 128] are formed
+ * once, then each output column sums its k products in order. */
 static void fp8_row(const uint8_t* xr, const float* sxr, const uint8_t* wg,
-                    const float* swg, int64_t k, int64_t n, double* yr, double* sr) {
+                    const float* swg, int64_t k, int64_t n, double* yr, double* sr, double* xs) {
     int64_t kb = (k + 127) / 128;
+    for (int64_t kk = 0; kk < k; ++kk) xs[kk] = e4m3_table[xr[kk]] * (double)sxr[kk / 128];
     for (int64_t j = 0; j < n; ++j) {
         double acc = 0.0, sabs = 0.0;
         const uint8_t* wr = wg + j * k;
         const float* swr = swg + j * kb;
         for (int64_t kk = 0; kk < k; ++kk) {
-            double a = e4m3_decode(xr[kk]) * (double)sxr[kk / 128];
-            double p = a * (e4m3_decode(wr[kk]) * (double)swr[kk / 128]);
+            double p = xs[kk] * (e4m3_table[wr[kk]] * (double)swr[kk / 128]);
             acc += p;
             sabs += fabs(p);
         }
@@ -402,19 +411,29 @@ int oracle_fp8_forward(const uint8_t* x, const float* sx, const uint8_t* w,
     int64_t* ends = (int64_t*)malloc(sizeof(int64_t) * (size_t)num_groups);
     if (!ends) return -2;
     group_ends(offs, num_groups, m, ends);
+    e4m3_table_init();
     int64_t kb = (k + 127) / 128;
     int64_t count = rows ? nrows : m;
+    int failed = 0;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < count; ++r) {
         int64_t i = rows ? rows[r] : r;
         int32_t g = (i >= 0 && i < m) ? group_of_row(ends, num_groups, i) : -1;
         status[r] = g >= 0;
         if (g < 0) continue;
+        double* xs = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+        if (!xs) {
+            status[r] = 0;
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
         fp8_row(x + i * k, sx + i * kb, w + (int64_t)g * n * k, sw + (int64_t)g * n * kb,
-                k, n, y + r * n, s + r * n);
+                k, n, y + r * n, s + r * n, xs);
+        free(xs);
     }
     free(ends);
-    return 0;
+    return failed ? -2 : 0;
 }
 
 /* Masked layout: x [E, max_m, k], sx [E, max_m, kb], w [E, n, k],
@@ -426,9 +445,11 @@ int oracle_fp8_masked_forward(const uint8_t* x, const float* sx, const uint8_t* 
                               const int64_t* rows, int64_t nrows, double* y, double* s,
                               int32_t* status) {
     if (num_groups < 1) return -1;
+    e4m3_table_init();
     int64_t kb = (k + 127) / 128;
     int64_t total = (int64_t)num_groups * max_m;
     int64_t count = rows ? nrows : total;
+    int failed = 0;
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < count; ++r) {
         int64_t flat = rows ? rows[r] : r;
@@ -437,10 +458,18 @@ int oracle_fp8_masked_forward(const uint8_t* x, const float* sx, const uint8_t* 
         if (ok) ok = row < masked_active(masked_m, e, max_m);
         status[r] = ok;
         if (!ok) continue;
+        double* xs = (double*)malloc(sizeof(double) * (size_t)(k > 0 ? k : 1));
+        if (!xs) {
+            status[r] = 0;
+#pragma omp atomic write
+            failed = 1;
+            continue;
+        }
         fp8_row(x + flat * k, sx + flat * kb, w + e * n * k, sw + e * n * kb, k, n,
-                y + r * n, s + r * n);
+                y + r * n, s + r * n, xs);
+        free(xs);
     }
-    return 0;
+    return failed ? -2 : 0;
 }
 
 /* Threads OpenMP will use for the calls above. */

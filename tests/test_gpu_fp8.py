@@ -11,10 +11,10 @@
   give bit-identical results to the same scales as fp32;
 * edge cases: empty experts, one-row experts, a ragged row tail, k = 128
   (one scale block), a column tail, half-height last tiles;
-* the full-size masked down and gate/up projections of the page's operand
-  table, every element, and the Qwen3 gate/up and GLM-up shapes on sampled
-  rows (every expert's first and last rows and its tile boundaries, plus
-  random rows), in the benchmark's launch configuration.
+* the full-size Qwen3 gate/up shape and the masked down and gate/up
+  projections of the page's operand table, every element, and the GLM-up
+  shape on sampled rows (every expert's first and last rows and its tile
+  boundaries, plus random rows), in the benchmark's launch configuration.
 Tolerance: parity.check_fp8.
 """
 import numpy as np
@@ -218,7 +218,7 @@ def _sample_rows(wl, rng, count):
     return np.unique(np.asarray(picks, dtype=np.int64))
 
 
-@pytest.mark.parametrize("name,count", [("fp8_qwen3_gateup", 1024), ("fp8_glm_up", 24)])
+@pytest.mark.parametrize("name,count", [("fp8_glm_up", 24)])
 def test_fp8_forward_full_size_sampled(name, count):
     dev = device()
     import torch
@@ -242,11 +242,12 @@ def test_fp8_forward_full_size_sampled(name, count):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["fp8_masked_down", "fp8_masked_gateup"])
+@pytest.mark.parametrize("name", ["fp8_qwen3_gateup", "fp8_masked_down", "fp8_masked_gateup"])
 def test_fp8_forward_full_size_every_element(name):
-    """The masked down and gate/up projections of the page's operand table at
-    full size, in the benchmark's launch configuration, compared element by
-    element with the oracle in row chunks; inactive rows keep the sentinel."""
+    """The full-size Qwen3 gate/up shape (ragged) and the masked down and
+    gate/up projections of the page's operand table, in the benchmark's
+    launch configuration, compared element by element with the oracle in
+    row chunks; rows outside the experts (inactive rows) keep the sentinel."""
     dev = device()
     import torch
     wl = synth.by_name(name)
