@@ -230,8 +230,9 @@ def tile_cost(gg, synth, torch, dev, n=1536, experts=256, cus=256):
     4096, whose least-squares line in the stage count (k / 32) gives a tile's
     fixed cost (intercept) and its time per stage (slope), for bf16 output
     (stored through LDS) and fp32 output (stored straight from the
-    accumulators, overlapped with the next tile's first loads).  Times are
-    per workgroup: launch time x CUs / tiles."""
+    accumulators, overlapped with the next tile's first loads); and the same
+    split for wgrad on 64 uniform experts of 128 .. 1024 rows (fp32 dW).
+    Times are per workgroup: launch time x CUs / tiles."""
     import numpy as np
     col_tiles = (n + 255) // 256
     out = {"n": n, "experts": experts, "col_tiles": col_tiles, "shapes": []}
@@ -262,6 +263,26 @@ def tile_cost(gg, synth, torch, dev, n=1536, experts=256, cus=256):
         tag = str(dt).replace("torch.", "")
         out[f"fit_{tag}_us_per_stage"] = round(float(slope), 4)
         out[f"fit_{tag}_fixed_us_per_tile"] = round(float(icpt), 2)
+    # wgrad on 64 uniform experts of 128 .. 1024 rows at k = 2048, n = 1536
+    # (48 dW tiles of 256 KB fp32 per expert; a stage is 32 of its rows)
+    wg, k_w, e_w = [], 2048, 64
+    tiles_w = e_w * (k_w // 256) * col_tiles
+    for rows in (128, 256, 512, 1024):
+        wl = synth.custom_ragged(f"uniform_wgrad_{rows}", [rows] * e_w, k=k_w, n=n, seed=78)
+        t = synth.make_inputs(wl, dev, need=("x", "dy"))
+        dw = torch.empty((e_w, k_w, n), dtype=torch.float32, device=dev)
+        _, ms = time_passes([("w", lambda: gg.wgrad(t["x"], t["dy"], t["offs"], out=dw))], 20, 3, torch)
+        med = sorted(ms["w"])[len(ms["w"]) // 2]
+        wg.append({"rows": rows, "stages": rows // 32, "ms": round(med, 4),
+                   "us_per_tile": round(med * 1e3 * cus / tiles_w, 2),
+                   "algorithmic_GB/s": round(algorithmic_bytes(wl, "wgrad") / (med * 1e-3) / 1e9, 1)})
+        del t, dw
+    st = np.array([e["stages"] for e in wg], dtype=float)
+    us = np.array([e["us_per_tile"] for e in wg])
+    slope, icpt = np.polyfit(st, us, 1)
+    out["wgrad_shapes"] = wg
+    out["fit_wgrad_us_per_stage"] = round(float(slope), 4)
+    out["fit_wgrad_fixed_us_per_tile"] = round(float(icpt), 2)
     torch.cuda.empty_cache()
     return out
 
