@@ -288,16 +288,6 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-// Wait until at most n global->LDS loads of this wave are in flight, then
-// barrier.  (The LDS operations of this wave are complete too.)
-template <int N>
-__device__ __forceinline__ void stage_barrier_vm() {
-  // s_waitcnt vmcnt(N) expcnt(7) lgkmcnt(0); vmcnt is 6 bits (low 4 at
-  // [3:0], high 2 at [15:14])
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-  asm volatile("s_barrier" ::: "memory");
-}
-
 // Stores a wave issues for one fp32 output tile of TMA active row blocks
 // (store_tile_f32<TMA> issues exactly this many, in or out of range).
 template <int TMA>
@@ -435,7 +425,8 @@ __device__ __forceinline__ void pp_regions_escape(const Regions& r) {
 }
 
 // s_waitcnt vmcnt(N) expcnt(7) lgkmcnt(0) (N < 64 a count of this wave's
-// loads, 64 no wait on loads), then barrier.
+// loads, 64 no wait on loads; vmcnt is 6 bits, the low 4 at [3:0] and the
+// high 2 at [15:14]), then barrier.
 template <int N>
 __device__ __forceinline__ void pp_sync(const Regions&) {
   if constexpr (N < 64) __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
