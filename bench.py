@@ -180,6 +180,7 @@ def cpu_baseline(wl, t, synth, budget_s=15.0):
     flops = 0.0
     secs = 0.0
     parts = []
+    per_pass = {}
 
     def timed(fn, *args, **kw):
         t0 = time.perf_counter()
@@ -198,6 +199,8 @@ def cpu_baseline(wl, t, synth, budget_s=15.0):
         flops += nrows * per_row
         secs += dt
         parts.append(f"{name}: {nrows} random rows")
+        per_pass[name] = {"GFLOP": round(nrows * per_row / 1e9, 2), "seconds": round(dt, 2),
+                          "GFLOP/s": round(nrows * per_row / dt / 1e9, 1)}
     # wgrad: (expert, k) rows of dW, expert chosen with probability ~ rows
     live = np.nonzero(sizes > 0)[0]
     p = sizes[live] / sizes[live].sum()
@@ -209,9 +212,11 @@ def cpu_baseline(wl, t, synth, budget_s=15.0):
     npairs = int(max(8, rate * budget_s / 3 / mean_cost))
     pairs = np.stack([rng.choice(live, npairs, p=p), rng.integers(0, wl.k, npairs)], axis=1)
     dt = timed(oracle.wgrad, hb["x"], hb["dy"], wl.offs, pairs=pairs)
-    flops += 2.0 * float(sizes[pairs[:, 0]].sum()) * wl.n
+    wf = 2.0 * float(sizes[pairs[:, 0]].sum()) * wl.n
+    flops += wf
     secs += dt
     parts.append(f"wgrad: {npairs} (expert, k) rows of dW")
+    per_pass["wgrad"] = {"GFLOP": round(wf / 1e9, 2), "seconds": round(dt, 2), "GFLOP/s": round(wf / dt / 1e9, 1)}
     return {
         "value": flops / secs / 1e12,
         "unit": "TFLOP/s",
@@ -219,6 +224,7 @@ def cpu_baseline(wl, t, synth, budget_s=15.0):
         "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": f"{wl.name}, {'; '.join(parts)}; {flops / 1e9:.1f} GFLOP in {secs:.1f} s",
+        "per_pass": per_pass,
     }
 
 

@@ -45,3 +45,17 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_reports_every_pass():
+    """The oracle timing on a small workload: a rate, the thread count, the
+    CPU model and per-pass GFLOP, seconds and GFLOP/s."""
+    from moe_grouped_gemm_ragged_amd import synth
+    wl = synth.by_name("glm_up_small")
+    t = synth.make_inputs(wl, "cpu")
+    cpu = bench.cpu_baseline(wl, t, synth, budget_s=0.3)
+    assert cpu["kind"] == "oracle" and cpu["unit"] == "TFLOP/s" and cpu["value"] > 0
+    assert cpu["cores"] >= 1 and "cpu_model" in cpu
+    assert set(cpu["per_pass"]) == {"forward", "dgrad", "wgrad"}
+    for v in cpu["per_pass"].values():
+        assert v["GFLOP"] > 0 and v["seconds"] >= 0
