@@ -1037,7 +1037,10 @@ __device__ __attribute__((always_inline)) inline void mainloop8_pp(
     pp_sync<kNoVm>(rg);
     // stage KT = kt + U: compute it, then read stage KT + 1 and load (U even)
     // B of stage KT + 4 into slot U or (U odd) the scales of k-block
-    // (KT + 3) / 2 and this group's half of its A pair into slot (U + 3) mod 4
+    // (KT + 3) / 2 and this group's half of its A pair into slot (U + 3) mod 4.
+    // The read is unconditional: after the last stage it reads LDS that
+    // nothing uses (under a condition the compiler kept the old and the new
+    // fragments live across it, copying them and spilling).
 #define GG8_PP_STAGE0(U, KT)                                                                      \
   {                                                                                               \
     __builtin_amdgcn_sched_barrier(0);                                                            \
